@@ -1,0 +1,185 @@
+"""Throughput of the selective scan (S6) forward pass on one MI355X.
+
+One step = one sscan_forward call over the whole workload (every row of the
+hot path: load/convert, ZOH discretisation, scan, readout + skip, final
+state), inputs already resident in HBM.  Default workload: batch 4 x 8192
+tokens x 4096 channels (Mamba-1.4B inner width), N = 16, A = -(n+1),
+bf16 x/delta/B/C/y, fp32 state and arithmetic, seeded synthetic inputs.
+
+Prints ONE JSON line: B*L*D elements/s, achieved algorithmic HBM bandwidth,
+a roofline object for the scan and the fp64 oracle's throughput on a bounded
+sample on the host cores.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
+                    [--no-cpu-baseline] [--calib-copy]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+# fp32 VALU without packed-FP32 forms: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz
+# lane-ops/s; an FMA counts 2 flops -> 78.6 TFLOP/s (the published 157.3
+# TFLOP/s fp32-vector figure needs the packed forms, which this build never emits).
+PEAK_VALU_TFLOPS = 78.6
+FLOPS_PER_UPDATE = 8           # per (b,t,d,n): 3 FMA + 2 MUL in the fused S4D-real update
+
+
+def algorithmic_bytes(wl, with_state: bool) -> int:
+    es = 2 if wl.io == "bf16" else 4
+    per_elem = 3 * es                                  # x, delta in; y out
+    bc = 2 * wl.batch * wl.seqlen * wl.dstate * es     # B, C
+    params = wl.dim * wl.dstate * 4 + wl.dim * 4       # A, Dskip
+    state = wl.batch * wl.dim * wl.dstate * 4 if with_state else 0
+    return wl.elements * per_elem + bc + params + state
+
+
+def cpu_baseline(wl, target_s: float = 10.0) -> dict:
+    """The fp64 oracle as it stands, on batch row 0, all channels, a token prefix sized so
+    the run takes about target_s seconds."""
+    import datagen
+    import oracle
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    T = min(wl.seqlen, 256)
+    while True:
+        inp = datagen.scan_inputs(datagen.Workload(wl.name, wl.key, 1, wl.seqlen, wl.dim, wl.dstate,
+                                                   wl.io, wl.a_init), t1=T)
+        t0 = time.perf_counter()
+        oracle.forward(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["Dskip"],
+                       nthreads=threads, want_state=True)
+        dt = time.perf_counter() - t0
+        if dt >= target_s * 0.5 or T >= wl.seqlen:
+            break
+        T = min(wl.seqlen, int(T * min(8.0, max(2.0, target_s / max(dt, 1e-3)))))
+    elems = T * wl.dim
+    return {"value": elems / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
+            "sample": f"batch row 0, tokens [0,{T}), all {wl.dim} channels, N={wl.dstate} "
+                      f"({elems} elements, {dt:.2f} s, fp64, {threads} threads)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mamba1p4b_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a 1 GiB device copy (HBM-counter calibration under rocprofv3)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the scan runs on a single MI355X and this build "
+              "has no multi-GPU path (see the sharding note in DESIGN.md).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import datagen
+    import selective_state_space_77_amd as sscan
+
+    wl = datagen.workload(args.workload)
+    if wl.mode != "scan":
+        print("bench.py times whole-sequence workloads", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- inputs resident in HBM (generated per token block, seeded)
+    def up(t):
+        a = datagen.gen_seq(wl, t)
+        if wl.io == "bf16":
+            return torch.from_numpy(datagen.bf16_bits(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    x, delta, B, C = (up(t) for t in ("x", "delta", "B", "C"))
+    A = torch.from_numpy(datagen.gen_A(wl)).to(dev)
+    D = torch.from_numpy(datagen.gen_Dskip(wl)).to(dev)
+    y = torch.empty_like(x)
+    hs = torch.empty(wl.batch, wl.dim, wl.dstate, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    print(f"[bench] workload {wl.name}: batch={wl.batch} L={wl.seqlen} dim={wl.dim} N={wl.dstate} "
+          f"io={wl.io}", file=sys.stderr, flush=True)
+
+    def step():
+        sscan.forward(x, delta, A, B, C, D, y=y, final_state=hs, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps, HIP events on the launch stream around each call
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = np.array([e0.elapsed_time(e1) for e0, e1 in ev]) * 1e-3  # seconds
+    per_step = wall / args.steps
+    ev_avg = float(durs.mean())
+
+    if args.calib_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    nbytes = algorithmic_bytes(wl, with_state=True)
+    updates = wl.elements * wl.dstate
+    hbm_gbs = nbytes / ev_avg / 1e9
+    tflops = updates * FLOPS_PER_UPDATE / ev_avg / 1e12
+    roof = {
+        "kernel": "sscan_forward (k_prep_bc + k_scan aggregate + k_scan main, one call)",
+        "bound": "alu",
+        "achieved": round(tflops, 3),
+        "peak": PEAK_VALU_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(tflops / PEAK_VALU_TFLOPS, 4),
+        "traffic": None,
+        "per_launch": {"updates": updates, "flops_per_update": FLOPS_PER_UPDATE,
+                       "algorithmic_bytes": nbytes, "event_avg_us": round(ev_avg * 1e6, 2),
+                       "event_min_us": round(float(durs.min()) * 1e6, 2)},
+        "hbm": {"achieved": round(hbm_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(hbm_gbs / PEAK_HBM_GBS, 4)},
+    }
+    out = {
+        "metric": "selective-scan B*L*D elements/s (+ achieved HBM GB/s vs MI355X peak)",
+        "value": wl.elements / per_step,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": per_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; x,B,C~N(0,1), delta=softplus(0.5N+bias), A=-(n+1))",
+        "config": {"workload": wl.name, "batch": wl.batch, "seqlen": wl.seqlen, "dim": wl.dim,
+                   "dstate": wl.dstate, "io_dtype": wl.io, "a_init": wl.a_init},
+        "hbm_gbs": round(nbytes / per_step / 1e9, 1),
+        "hbm_frac_of_peak": round(nbytes / per_step / 1e9 / PEAK_HBM_GBS, 4),
+        "roofline": roof,
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(wl),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

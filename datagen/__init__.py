@@ -89,12 +89,13 @@ def custom(name: str, batch: int, seqlen: int, dim: int, dstate: int, io: str = 
 def round_bf16(a: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bf16 (ties to even); result is float32."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    u = a.view(np.uint32)
+    # uint32 cannot overflow here for non-NaN inputs (largest: 0xFF7FFFFF + 0x8000)
     nan = np.isnan(a)
-    out = r.astype(np.uint32).view(np.float32)
+    r = u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
+    r &= np.uint32(0xFFFF0000)
+    out = r.view(np.float32)
     if nan.any():
-        out = out.copy()
         out[nan] = np.float32("nan")
     return out
 

@@ -1,0 +1,118 @@
+/*
+ * sscan.h -- C ABI of the MI355X (gfx950) selective scan (S6) library, libsscan.so.
+ *
+ * The operation (pages: "The loop that beats attention" eqs. (1)-(2) and
+ * "Selectivity" eq. (4); "Mamba and State Space Models", "Mamba: making the
+ * state selective"; "State space models and Mamba", continuous form with D;
+ * "Mamba matches the Transformer...", "Selection makes the recurrence read
+ * the token" and "The scan that pays for selection"):
+ *
+ *   for every batch row b, channel d and state n, with h = 0 before token 0:
+ *     Abar  = exp(delta[b,t,d] * A[d,n])                       zero-order hold
+ *     Bbar  = (exp(delta*A[d,n]) - 1) / A[d,n] * B[b,t,n]        (delta*B when A = 0)
+ *     h[n]  = Abar * h[n] + Bbar * x[b,t,d]                     linear recurrence
+ *     y[b,t,d] = sum_n C[b,t,n] * h[n] + Dskip[d] * x[b,t,d]    readout + skip
+ *
+ * delta, x are per (b, t, d); B, C per (b, t, n), shared by every channel;
+ * A is diagonal per channel, (dim, N).  The per-token Abar/Bbar tensor of
+ * shape (batch, L, dim, N) is never written to memory.
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers (hipMalloc / torch CUDA tensors) owned by the
+ *     caller.  The library keeps no reference after the call returns, except
+ *     that the enqueued work reads and writes them until it completes.
+ *   - All arrays are dense, row-major, contiguous, naturally aligned for their
+ *     element type.  io_dtype selects the element type of x, delta, B, C, y
+ *     (and of x_t, delta_t, B_t, C_t, y_t); A, Dskip and states are always fp32.
+ *     bf16 outputs are rounded to nearest, ties to even.  All arithmetic and the
+ *     state are fp32.
+ *   - Calls are asynchronous: work is enqueued on `stream` (a hipStream_t; NULL
+ *     is the default stream) and the call returns.  Errors found while the
+ *     kernels run surface at the caller's next synchronisation.
+ *   - Arguments are validated before anything is enqueued; on a validation error
+ *     nothing is touched and a negative status is returned.  There is no fallback
+ *     path of any kind: the kernels below run, or the call fails.
+ *   - Values are not checked: delta <= 0, A >= 0, NaN and Inf are computed by the
+ *     formula and propagate (A > 0 grows, as an eigenvalue above 1 would).
+ *   - Any tensor with zero elements may be passed as NULL.
+ *   - Calls on different streams may run concurrently; each call owns the
+ *     stream-ordered scratch memory it allocates (hipMallocAsync) and frees it on
+ *     the same stream.
+ */
+#ifndef SSCAN_H
+#define SSCAN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSCAN_ABI_VERSION 1
+#define SSCAN_MAX_DSTATE 16 /* N = 1 .. 16 */
+
+typedef enum { SSCAN_F32 = 0, SSCAN_BF16 = 1 } sscan_dtype;
+
+typedef enum {
+    SSCAN_OK = 0,
+    SSCAN_ERR_NULL = -1,        /* a required pointer is NULL (its tensor is non-empty) */
+    SSCAN_ERR_SHAPE = -2,       /* a size is negative, or a byte size overflows int64   */
+    SSCAN_ERR_UNSUPPORTED = -3, /* dstate outside 1..SSCAN_MAX_DSTATE, or bad io_dtype   */
+    SSCAN_ERR_ALIAS = -4,       /* an output overlaps an input or another output         */
+    SSCAN_ERR_HIP = -5          /* a HIP call (allocation, launch) failed; see last error */
+} sscan_status;
+
+/*
+ * Whole-sequence forward pass (prefill / training forward).
+ *
+ *   x, delta     [in]  (batch, seqlen, dim), io_dtype.  delta is the step size
+ *                      after its softplus (the pages' Delta_t), not the raw projection.
+ *   A            [in]  (dim, dstate) fp32, the diagonal continuous-time A.
+ *   B, C         [in]  (batch, seqlen, dstate), io_dtype.
+ *   Dskip        [in]  (dim) fp32, or NULL for no skip term.
+ *   y            [out] (batch, seqlen, dim), io_dtype.  Must not overlap any input.
+ *   final_state  [out] (batch, dim, dstate) fp32 state after the last token, or NULL.
+ *                      With seqlen == 0 it receives zeros.  Same layout as the
+ *                      `state` of sscan_step, so a prefill hands over directly.
+ *   batch, seqlen, dim >= 0; 1 <= dstate <= SSCAN_MAX_DSTATE.
+ *   stream       hipStream_t to enqueue on.
+ * Returns SSCAN_OK or a negative sscan_status.
+ */
+int sscan_forward(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                  const float *Dskip, void *y, float *final_state, int64_t batch, int64_t seqlen,
+                  int64_t dim, int64_t dstate, int io_dtype, void *stream);
+
+/*
+ * One recurrent decode step (generation: constant work and memory per token;
+ * "The loop that beats attention", section "Going back to the baton";
+ * "State space models and Mamba", cost table, generation per token O(1)).
+ *
+ *   state        [in/out] (batch, dim, dstate) fp32, h_{t-1} on entry, h_t on
+ *                      return; updated in place.  Must not overlap any other argument.
+ *   x_t, delta_t [in]  (batch, dim), io_dtype.
+ *   A            [in]  (dim, dstate) fp32.
+ *   B_t, C_t     [in]  (batch, dstate), io_dtype.
+ *   Dskip        [in]  (dim) fp32, or NULL.
+ *   y_t          [out] (batch, dim), io_dtype.
+ *   batch, dim >= 0; 1 <= dstate <= SSCAN_MAX_DSTATE.
+ * Returns SSCAN_OK or a negative sscan_status.
+ */
+int sscan_step(float *state, const void *x_t, const void *delta_t, const float *A,
+               const void *B_t, const void *C_t, const float *Dskip, void *y_t, int64_t batch,
+               int64_t dim, int64_t dstate, int io_dtype, void *stream);
+
+/* Static text for a status code (never NULL). */
+const char *sscan_status_string(int status);
+
+/* Detail of the last failure on the calling thread ("" if none). Valid until the
+ * next call on this thread. */
+const char *sscan_last_error(void);
+
+/* SSCAN_ABI_VERSION of the loaded library. */
+int sscan_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSCAN_H */

@@ -1,0 +1,135 @@
+"""MI355X (gfx950) selective scan (S6) -- Python binding of libsscan.so.
+
+Argument marshalling only: every step of the scan runs in the library's HIP
+kernels.  PyTorch supplies device memory and the stream.  There is no CPU or
+PyTorch fallback: if libsscan.so is missing or fails to load, importing this
+package raises.
+
+    forward(x, delta, A, B, C, Dskip=None, y=None, final_state=None, stream=None)
+    step(state, x_t, delta_t, A, B_t, C_t, Dskip=None, y_t=None, stream=None)
+
+Shapes and layouts follow include/sscan.h: x, delta, y (batch, L, dim); B, C
+(batch, L, N); A (dim, N) fp32; Dskip (dim,) fp32; states (batch, dim, N) fp32.
+x, delta, B, C (and y) are all float32 or all bfloat16.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsscan.so")
+
+F32, BF16 = 0, 1
+MAX_DSTATE = 16
+
+STATUS = {0: "SSCAN_OK", -1: "SSCAN_ERR_NULL", -2: "SSCAN_ERR_SHAPE", -3: "SSCAN_ERR_UNSUPPORTED",
+          -4: "SSCAN_ERR_ALIAS", -5: "SSCAN_ERR_HIP"}
+
+
+class SScanError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                          "(hipcc --offload-arch=gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, fp, i64 = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64
+    lib.sscan_forward.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i64, i64, i64, i64, ctypes.c_int, vp]
+    lib.sscan_forward.restype = ctypes.c_int
+    lib.sscan_step.argtypes = [fp, vp, vp, fp, vp, vp, fp, vp, i64, i64, i64, ctypes.c_int, vp]
+    lib.sscan_step.restype = ctypes.c_int
+    lib.sscan_status_string.argtypes = [ctypes.c_int]
+    lib.sscan_status_string.restype = ctypes.c_char_p
+    lib.sscan_last_error.argtypes = []
+    lib.sscan_last_error.restype = ctypes.c_char_p
+    lib.sscan_version.argtypes = []
+    lib.sscan_version.restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        detail = lib.sscan_last_error().decode() or lib.sscan_status_string(rc).decode()
+        raise SScanError(rc, detail)
+
+
+def _io_code(*ts: torch.Tensor) -> int:
+    dt = ts[0].dtype
+    if any(t.dtype != dt for t in ts):
+        raise TypeError("x, delta, B, C and y must share one dtype")
+    if dt == torch.float32:
+        return F32
+    if dt == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported I/O dtype {dt}; use float32 or bfloat16")
+
+
+def _dev(t: torch.Tensor | None, name: str, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream, device) -> int:
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return s.cuda_stream if isinstance(s, torch.cuda.Stream) else int(s)
+
+
+def forward(x, delta, A, B, C, Dskip=None, y=None, final_state=None, stream=None):
+    """Whole-sequence selective scan; returns y (written into `y` when given)."""
+    batch, L, dim = x.shape
+    N = A.shape[1]
+    if delta.shape != x.shape or tuple(A.shape) != (dim, N) or B.shape != (batch, L, N) or C.shape != B.shape:
+        raise ValueError("inconsistent shapes")
+    if y is None:
+        y = torch.empty_like(x)
+    io = _io_code(x, delta, B, C, y)
+    if Dskip is not None and tuple(Dskip.shape) != (dim,):
+        raise ValueError("Dskip must have shape (dim,)")
+    if final_state is not None and tuple(final_state.shape) != (batch, dim, N):
+        raise ValueError("final_state must have shape (batch, dim, N)")
+    rc = lib.sscan_forward(_dev(x, "x"), _dev(delta, "delta"), _dev(A, "A", torch.float32),
+                           _dev(B, "B"), _dev(C, "C"), _dev(Dskip, "Dskip", torch.float32),
+                           _dev(y, "y"), _dev(final_state, "final_state", torch.float32),
+                           batch, L, dim, N, io, _stream(stream, x.device))
+    _check(rc)
+    return y
+
+
+def step(state, x_t, delta_t, A, B_t, C_t, Dskip=None, y_t=None, stream=None):
+    """One decode step; updates `state` in place and returns y_t."""
+    batch, dim, N = state.shape
+    if x_t.shape != (batch, dim) or delta_t.shape != (batch, dim) or tuple(A.shape) != (dim, N) \
+            or B_t.shape != (batch, N) or C_t.shape != (batch, N):
+        raise ValueError("inconsistent shapes")
+    if y_t is None:
+        y_t = torch.empty_like(x_t)
+    io = _io_code(x_t, delta_t, B_t, C_t, y_t)
+    if Dskip is not None and tuple(Dskip.shape) != (dim,):
+        raise ValueError("Dskip must have shape (dim,)")
+    rc = lib.sscan_step(_dev(state, "state", torch.float32), _dev(x_t, "x_t"), _dev(delta_t, "delta_t"),
+                        _dev(A, "A", torch.float32), _dev(B_t, "B_t"), _dev(C_t, "C_t"),
+                        _dev(Dskip, "Dskip", torch.float32), _dev(y_t, "y_t"), batch, dim, N, io,
+                        _stream(stream, state.device))
+    _check(rc)
+    return y_t
+
+
+def version() -> int:
+    return lib.sscan_version()

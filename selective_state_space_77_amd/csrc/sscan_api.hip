@@ -1,0 +1,158 @@
+// C-ABI entry points of libsscan.so: argument validation, scratch memory and
+// dispatch to the gfx950 kernels.  Declarations and contracts: include/sscan.h.
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/sscan.h"
+#include "sscan_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512];
+
+int fail(int status, const char *fmt, const char *detail = nullptr) {
+    snprintf(g_last_error, sizeof g_last_error, fmt, detail ? detail : "");
+    return status;
+}
+
+int fail_hip(const char *what, hipError_t e) {
+    snprintf(g_last_error, sizeof g_last_error, "%s: %s (%d)", what, hipGetErrorString(e), int(e));
+    return SSCAN_ERR_HIP;
+}
+
+// bytes = product of sizes * elem; false on overflow or negative size
+bool nbytes(int64_t *out, int64_t elem, int64_t a, int64_t b = 1, int64_t c = 1) {
+    if (a < 0 || b < 0 || c < 0) return false;
+    int64_t v = elem;
+    if (__builtin_mul_overflow(v, a, &v) || __builtin_mul_overflow(v, b, &v) ||
+        __builtin_mul_overflow(v, c, &v))
+        return false;
+    *out = v;
+    return true;
+}
+
+struct Span {
+    const void *p;
+    int64_t bytes;
+    const char *name;
+};
+
+bool overlap(const Span &u, const Span &v) {
+    if (!u.p || !v.p || u.bytes == 0 || v.bytes == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(u.p), a1 = a0 + uintptr_t(u.bytes);
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(v.p), b1 = b0 + uintptr_t(v.bytes);
+    return a0 < b1 && b0 < a1;
+}
+
+// every output must be disjoint from every other span
+int check_alias(const Span *outs, int nout, const Span *ins, int nin) {
+    for (int i = 0; i < nout; ++i) {
+        for (int j = 0; j < nin; ++j)
+            if (overlap(outs[i], ins[j]))
+                return fail(SSCAN_ERR_ALIAS, "output overlaps an input (%s)", outs[i].name);
+        for (int j = i + 1; j < nout; ++j)
+            if (overlap(outs[i], outs[j]))
+                return fail(SSCAN_ERR_ALIAS, "outputs overlap (%s)", outs[i].name);
+    }
+    return SSCAN_OK;
+}
+
+int check_ptrs(const Span *s, int n) {
+    for (int i = 0; i < n; ++i)
+        if (!s[i].p && s[i].bytes > 0) return fail(SSCAN_ERR_NULL, "required pointer %s is NULL", s[i].name);
+    return SSCAN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sscan_version(void) { return SSCAN_ABI_VERSION; }
+
+const char *sscan_last_error(void) { return g_last_error; }
+
+const char *sscan_status_string(int status) {
+    switch (status) {
+        case SSCAN_OK: return "ok";
+        case SSCAN_ERR_NULL: return "required pointer is NULL";
+        case SSCAN_ERR_SHAPE: return "invalid shape (negative size or int64 overflow)";
+        case SSCAN_ERR_UNSUPPORTED: return "unsupported dstate or io_dtype";
+        case SSCAN_ERR_ALIAS: return "output overlaps another argument";
+        case SSCAN_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int sscan_forward(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                  const float *Dskip, void *y, float *final_state, int64_t batch, int64_t seqlen,
+                  int64_t dim, int64_t dstate, int io_dtype, void *stream) {
+    g_last_error[0] = '\0';
+    if (io_dtype != SSCAN_F32 && io_dtype != SSCAN_BF16)
+        return fail(SSCAN_ERR_UNSUPPORTED, "io_dtype must be SSCAN_F32 or SSCAN_BF16");
+    if (dstate < 1 || dstate > SSCAN_MAX_DSTATE)
+        return fail(SSCAN_ERR_UNSUPPORTED, "dstate must be in 1..16");
+    const int64_t es = io_dtype == SSCAN_BF16 ? 2 : 4;
+    int64_t bx, bbc, ba, bd, bs, ws_guard;
+    if (!nbytes(&bx, es, batch, seqlen, dim) || !nbytes(&bbc, es, batch, seqlen, dstate) ||
+        !nbytes(&ba, 4, dim, dstate) || !nbytes(&bd, 4, dim) || !nbytes(&bs, 4, batch, dim, dstate) ||
+        !nbytes(&ws_guard, 2 * 16 * 4, batch, seqlen))
+        return fail(SSCAN_ERR_SHAPE, "negative size or byte size overflows int64");
+    const Span ins[] = {{x, bx, "x"}, {delta, bx, "delta"}, {A, ba, "A"}, {B, bbc, "B"},
+                        {C, bbc, "C"}, {Dskip, Dskip ? bd : 0, "Dskip"}};
+    const Span outs[] = {{y, bx, "y"}, {final_state, final_state ? bs : 0, "final_state"}};
+    const Span req[] = {ins[0], ins[1], ins[2], ins[3], ins[4], outs[0]};
+    int rc = check_ptrs(req, 6);
+    if (rc) return rc;
+    rc = check_alias(outs, 2, ins, 6);
+    if (rc) return rc;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (batch == 0 || dim == 0) return SSCAN_OK;
+    if (seqlen == 0) {
+        if (!final_state) return SSCAN_OK;
+        hipError_t e = sscan::launch_zero(final_state, batch * dim * dstate, s);
+        return e == hipSuccess ? SSCAN_OK : fail_hip("zero-fill launch", e);
+    }
+
+    const sscan::FwdPlan plan = sscan::plan_forward(batch, seqlen, dim, dstate);
+    void *ws = nullptr;
+    hipError_t e = hipMallocAsync(&ws, plan.ws_bytes, s);
+    if (e != hipSuccess) return fail_hip("hipMallocAsync (scratch)", e);
+    sscan::FwdArgs a{x, delta, A, B, C, Dskip, y, final_state, batch, seqlen, dim, int(dstate),
+                     io_dtype};
+    e = sscan::launch_forward(a, plan, ws, s);
+    const hipError_t ef = hipFreeAsync(ws, s);
+    if (e != hipSuccess) return fail_hip("forward launch", e);
+    if (ef != hipSuccess) return fail_hip("hipFreeAsync (scratch)", ef);
+    return SSCAN_OK;
+}
+
+int sscan_step(float *state, const void *x_t, const void *delta_t, const float *A,
+               const void *B_t, const void *C_t, const float *Dskip, void *y_t, int64_t batch,
+               int64_t dim, int64_t dstate, int io_dtype, void *stream) {
+    g_last_error[0] = '\0';
+    if (io_dtype != SSCAN_F32 && io_dtype != SSCAN_BF16)
+        return fail(SSCAN_ERR_UNSUPPORTED, "io_dtype must be SSCAN_F32 or SSCAN_BF16");
+    if (dstate < 1 || dstate > SSCAN_MAX_DSTATE)
+        return fail(SSCAN_ERR_UNSUPPORTED, "dstate must be in 1..16");
+    const int64_t es = io_dtype == SSCAN_BF16 ? 2 : 4;
+    int64_t bx, bbc, ba, bd, bs;
+    if (!nbytes(&bx, es, batch, dim) || !nbytes(&bbc, es, batch, dstate) || !nbytes(&ba, 4, dim, dstate) ||
+        !nbytes(&bd, 4, dim) || !nbytes(&bs, 4, batch, dim, dstate))
+        return fail(SSCAN_ERR_SHAPE, "negative size or byte size overflows int64");
+    const Span ins[] = {{x_t, bx, "x_t"}, {delta_t, bx, "delta_t"}, {A, ba, "A"}, {B_t, bbc, "B_t"},
+                        {C_t, bbc, "C_t"}, {Dskip, Dskip ? bd : 0, "Dskip"}};
+    const Span outs[] = {{state, bs, "state"}, {y_t, bx, "y_t"}};
+    const Span req[] = {ins[0], ins[1], ins[2], ins[3], ins[4], outs[0], outs[1]};
+    int rc = check_ptrs(req, 7);
+    if (rc) return rc;
+    rc = check_alias(outs, 2, ins, 6);
+    if (rc) return rc;
+    if (batch == 0 || dim == 0) return SSCAN_OK;
+    sscan::StepArgs a{state, x_t, delta_t, A, B_t, C_t, Dskip, y_t, batch, dim, int(dstate), io_dtype};
+    const hipError_t e = sscan::launch_step(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SSCAN_OK : fail_hip("step launch", e);
+}
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// Private interface between the C-ABI layer (sscan_api.hip) and the kernels
+// (sscan_kernels.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sscan {
+
+constexpr int kWave = 64;  // CDNA wavefront width: one lane per channel
+
+// Work split of one forward pass: the sequence is cut into `segments` time
+// segments of `seg_len` tokens (the last may be shorter); each wave scans one
+// segment of 64 channels of one batch row.
+struct FwdPlan {
+    int64_t tiles_per_batch;  // ceil(dim / 64)
+    int64_t tiles;            // batch * tiles_per_batch
+    int64_t seg_len;
+    int segments;
+    int nt;                   // dstate rounded up to 1, 2, 4, 8 or 16
+    size_t ws_bytes;          // scratch: [B/(n+1), C] rows + segment aggregates
+};
+
+FwdPlan plan_forward(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+
+struct FwdArgs {
+    const void *x, *delta;
+    const float *A;
+    const void *B, *C;
+    const float *Dskip;
+    void *y;
+    float *final_state;
+    int64_t batch, L, dim;
+    int N;
+    int io;  // 0 fp32, 1 bf16
+};
+
+// Enqueue the forward pass; `ws` points at plan.ws_bytes of device scratch.
+hipError_t launch_forward(const FwdArgs &a, const FwdPlan &plan, void *ws, hipStream_t s);
+
+// Enqueue a fill of `count` floats with zero (used for final_state at seqlen 0).
+hipError_t launch_zero(float *p, int64_t count, hipStream_t s);
+
+struct StepArgs {
+    float *state;
+    const void *x, *delta;
+    const float *A;
+    const void *B, *C;
+    const float *Dskip;
+    void *y;
+    int64_t batch, dim;
+    int N;
+    int io;
+};
+
+hipError_t launch_step(const StepArgs &a, hipStream_t s);
+
+}  // namespace sscan

@@ -1,0 +1,455 @@
+// gfx950 kernels of the selective scan (S6): forward pass over a whole
+// sequence and the single-token decode step.
+//
+// Method (pages: "The loop that beats attention" eqs. (1)-(2); "Mamba and
+// State Space Models", selective pseudocode; "State space models and Mamba",
+// continuous form with D):  Abar = exp(delta*A), Bbar = (exp(delta*A)-1)/A*B,
+// h = Abar*h + Bbar*x, y = C.h + Dskip*x.  The fused-kernel idea (parameters
+// read from HBM once, discretisation and scan on chip, only y written, the
+// (batch, L, dim, N) tensor never materialised) follows "Mamba matches the
+// Transformer...", "The scan that pays for selection".
+//
+// Mapping on CDNA4.  One lane owns one channel d and keeps its N fp32 states
+// in VGPRs; the 64 lanes of a wave are 64 consecutive channels of one batch
+// row, so every lane of a wave works on the same token t:
+//   * x[b,t,d..d+63] and delta[...] are one contiguous 128 B (bf16) / 256 B
+//     (fp32) row per load instruction -- fully coalesced without LDS staging;
+//   * B[b,t,:] and C[b,t,:] are wave-uniform, so they come in through scalar
+//     loads into SGPRs and feed the VALU as scalar operands (no per-lane
+//     traffic, no LDS, no cross-lane exchange).
+// Time is split into segments so that the chip has >= 2 waves per SIMD:
+//   pass 1 (k_scan<.., false>): each wave scans its segment from a zero state
+//           and stores the segment aggregate (sum of delta, local final state);
+//   pass 2 (k_scan<.., true>):  each wave composes the aggregates of all
+//           earlier segments with the associative combine
+//           (a1,b1) o (a2,b2) = (a1*a2, a2*b1 + b2)  ("Mamba and State Space
+//           Models", the parallel scan), starting its own segment from the
+//           true carried state, and scans it again with the readout.
+// The decay of a whole segment needs no per-token product: the Abar of a
+// diagonal mode multiply to exp(A * sum(delta)).
+//
+// S4D-real fast path.  When every A row of a wave is A[d,n] = (n+1)*A[d,0]
+// with A[d,0] < 0 (the structured-real initialisation), Abar_n = r^(n+1) with
+// r = exp(delta*A[d,0]): one exp per (t,d) instead of N.  The state is kept
+// scaled, k_n = -A[d,0]*h_n, which turns the ZOH update into
+//     k_n <- w_n + Abar_n*(k_n - w_n),   w_n = (B[t,n]/(n+1)) * x
+// (two FMAs and one multiply; it never forms 1 - Abar) and the readout into
+// y = (sum_n C_n k_n) / (-A[d,0]) + Dskip*x.  B/(n+1) is staged once per
+// token by k_prep_bc.  Any other A takes the general path (exp and expm1 per
+// state), decided per wave from the data.
+
+#include <math.h>
+
+#include "sscan_internal.h"
+
+namespace sscan {
+namespace {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+__device__ __forceinline__ float exp2_hw(float v) { return __builtin_amdgcn_exp2f(v); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float v) {
+    // round to nearest even (the gfx950 conversion instruction)
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
+}
+
+struct IoF32 {
+    using T = float;
+    __device__ static float ld(const T *p, int64_t i) { return p[i]; }
+    __device__ static float cvt(T v) { return v; }
+    __device__ static T enc(float v) { return v; }
+};
+
+struct IoBF16 {
+    using T = uint16_t;
+    __device__ static float ld(const T *p, int64_t i) { return __uint_as_float(uint32_t(p[i]) << 16); }
+    __device__ static float cvt(T v) { return __uint_as_float(uint32_t(v) << 16); }
+    __device__ static T enc(float v) { return f32_to_bf16(v); }
+};
+
+// ----------------------------------------------------------------------------
+// Stage B/(n+1) and C of every token as fp32 rows of 2*NT floats, so the scan
+// reads one token's parameters with two scalar loads.  States n >= N (padding
+// up to NT) get B = C = 0 and therefore stay zero.
+template <class IO, int NT>
+__global__ __launch_bounds__(256) void k_prep_bc(const typename IO::T *__restrict__ B,
+                                                 const typename IO::T *__restrict__ C,
+                                                 float *__restrict__ bc, int64_t rows, int N) {
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= rows * NT) return;
+    const int64_t r = i / NT;
+    const int n = int(i - r * NT);
+    float bv = 0.f, cv = 0.f;
+    if (n < N) {
+        bv = IO::ld(B, r * N + n);
+        cv = IO::ld(C, r * N + n);
+    }
+    bc[r * (2 * NT) + n] = bv / float(n + 1);
+    bc[r * (2 * NT) + NT + n] = cv;
+}
+
+__global__ __launch_bounds__(256) void k_zero(float *__restrict__ p, int64_t count) {
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < count) p[i] = 0.f;
+}
+
+// ----------------------------------------------------------------------------
+// One wave = 64 channels x one time segment.  kMain = false: aggregate pass;
+// kMain = true: carried-state scan with readout.
+constexpr int kUnroll = 8;  // tokens of x/delta prefetched ahead
+
+template <class IO, int NT, bool kMain>
+__global__ __launch_bounds__(kWave) void k_scan(
+    const typename IO::T *__restrict__ x, const typename IO::T *__restrict__ delta,
+    const float *__restrict__ A, const float *__restrict__ bc, const float *__restrict__ Dskip,
+    typename IO::T *__restrict__ y, float *__restrict__ final_state,
+    float *__restrict__ agg_sum, float *__restrict__ agg_h, int64_t batch, int64_t L, int64_t dim,
+    int N, int64_t seg_len, int segments, int64_t tiles_per_batch, int64_t tiles) {
+    using T = typename IO::T;
+    const int lane = threadIdx.x;
+    const int64_t wid = blockIdx.x;
+    const int seg = int(wid / tiles);
+    const int64_t tile = wid - int64_t(seg) * tiles;
+    const int64_t b = tile / tiles_per_batch;
+    const int64_t dbase = (tile - b * tiles_per_batch) * kWave;  // first channel of the wave
+    const bool active = dbase + lane < dim;
+    const int lo = active ? lane : int(dim - 1 - dbase);         // clamped lane offset
+    const int64_t d = dbase + lo;
+    const int64_t t0 = int64_t(seg) * seg_len;
+    const int64_t t1 = min(L, t0 + seg_len);
+
+    float a[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) a[n] = (n < N) ? A[d * N + n] : 0.f;
+    bool s4d = (a[0] < 0.f) && (a[0] > -INFINITY);
+#pragma unroll
+    for (int n = 1; n < NT; ++n)
+        if (n < N) s4d = s4d && (a[n] == a[0] * float(n + 1));
+    const bool fast = __all(s4d);
+
+    // ---- carried state at the segment start (pass 2 only)
+    float h[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) h[n] = 0.f;
+    if (kMain) {
+        for (int j = 0; j < seg; ++j) {
+            const int64_t cj = int64_t(j) * batch + b;
+            const float s = agg_sum[cj * dim + d];
+            if (fast) {
+                const float rho = exp2_hw(a[0] * kLog2e * s);
+                float dec = rho;
+#pragma unroll
+                for (int n = 0; n < NT; ++n) {
+                    h[n] = fmaf(dec, h[n], agg_h[(cj * NT + n) * dim + d]);
+                    dec *= rho;
+                }
+            } else {
+#pragma unroll
+                for (int n = 0; n < NT; ++n)
+                    h[n] = fmaf(exp2_hw(a[n] * kLog2e * s), h[n], agg_h[(cj * NT + n) * dim + d]);
+            }
+        }
+    }
+
+    const T *xrow = x + (b * L) * dim + dbase;
+    const T *drow = delta + (b * L) * dim + dbase;
+    T *yrow = kMain ? y + (b * L) * dim + dbase : nullptr;
+    const float *bcrow = bc + (b * L) * (2 * NT);
+    const float dsk = (kMain && Dskip) ? Dskip[d] : 0.f;
+    float dsum = 0.f;
+
+    T xr[kUnroll], dr[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const int64_t t = min(t0 + u, t1 - 1);
+        xr[u] = xrow[t * dim + lo];
+        dr[u] = drow[t * dim + lo];
+    }
+    float brow[2 * NT];
+#pragma unroll
+    for (int i = 0; i < 2 * NT; ++i) brow[i] = bcrow[t0 * (2 * NT) + i];
+
+    if (fast) {
+        const float alpha = -a[0];
+        const float inv_alpha = 1.f / alpha;
+        const float a2 = a[0] * kLog2e;
+        float k[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) k[n] = h[n] * alpha;
+        for (int64_t tc = t0; tc < t1; tc += kUnroll) {
+            float xv[kUnroll], dv[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                xv[u] = IO::cvt(xr[u]);
+                dv[u] = IO::cvt(dr[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int64_t t = min(tc + kUnroll + u, t1 - 1);
+                xr[u] = xrow[t * dim + lo];
+                dr[u] = drow[t * dim + lo];
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int64_t t = tc + u;
+                if (t < t1) {
+                    float bnext[2 * NT];
+                    const int64_t tn = min(t + 1, t1 - 1);
+#pragma unroll
+                    for (int i = 0; i < 2 * NT; ++i) bnext[i] = bcrow[tn * (2 * NT) + i];
+                    const float r = exp2_hw(dv[u] * a2);
+                    float pw = r, yacc = 0.f;
+#pragma unroll
+                    for (int n = 0; n < NT; ++n) {
+                        const float e = fmaf(-brow[n], xv[u], k[n]);
+                        const float q = pw * e;
+                        k[n] = fmaf(brow[n], xv[u], q);
+                        if (kMain) yacc = fmaf(brow[NT + n], k[n], yacc);
+                        pw *= r;
+                    }
+                    if (kMain) {
+                        if (active) yrow[t * dim + lo] = IO::enc(fmaf(yacc, inv_alpha, dsk * xv[u]));
+                    } else {
+                        dsum += dv[u];
+                    }
+#pragma unroll
+                    for (int i = 0; i < 2 * NT; ++i) brow[i] = bnext[i];
+                }
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < NT; ++n) h[n] = k[n] * inv_alpha;
+    } else {
+        float a2n[NT], inva[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            a2n[n] = a[n] * kLog2e;
+            inva[n] = (a[n] != 0.f) ? 1.f / a[n] : 0.f;
+        }
+        for (int64_t tc = t0; tc < t1; tc += kUnroll) {
+            float xv[kUnroll], dv[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                xv[u] = IO::cvt(xr[u]);
+                dv[u] = IO::cvt(dr[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int64_t t = min(tc + kUnroll + u, t1 - 1);
+                xr[u] = xrow[t * dim + lo];
+                dr[u] = drow[t * dim + lo];
+            }
+            for (int u = 0; u < kUnroll; ++u) {
+                const int64_t t = tc + u;
+                if (t < t1) {
+                    const float *row = bcrow + t * (2 * NT);
+                    float yacc = 0.f;
+#pragma unroll
+                    for (int n = 0; n < NT; ++n) {
+                        const float dt = dv[u];
+                        const float abar = exp2_hw(dt * a2n[n]);
+                        // (exp(dt*A) - 1)/A without cancellation; dt when A == 0
+                        const float g = (a[n] != 0.f) ? expm1f(dt * a[n]) * inva[n] : dt;
+                        const float bn = row[n] * float(n + 1);
+                        h[n] = fmaf(abar, h[n], g * (bn * xv[u]));
+                        if (kMain) yacc = fmaf(row[NT + n], h[n], yacc);
+                    }
+                    if (kMain) {
+                        if (active) yrow[t * dim + lo] = IO::enc(fmaf(dsk, xv[u], yacc));
+                    } else {
+                        dsum += dv[u];
+                    }
+                }
+            }
+        }
+    }
+
+    if (!active) return;
+    if (!kMain) {
+        const int64_t cs = int64_t(seg) * batch + b;
+        agg_sum[cs * dim + d] = dsum;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) agg_h[(cs * NT + n) * dim + d] = h[n];
+    } else if (final_state && seg == segments - 1) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+            if (n < N) final_state[(b * dim + d) * N + n] = h[n];
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Decode step: LPC lanes share one channel, each owning SPL consecutive states
+// (16 B for N = 16), so a wave reads and writes one contiguous 1 KB span of
+// the (batch, dim, N) state.  The partial readouts are summed across the LPC
+// lanes.  Memory bound: exact expf/expm1f per state.
+template <class IO, int NT, bool kVec>
+__global__ __launch_bounds__(256) void k_step(float *__restrict__ state,
+                                              const typename IO::T *__restrict__ x,
+                                              const typename IO::T *__restrict__ delta,
+                                              const float *__restrict__ A,
+                                              const typename IO::T *__restrict__ B,
+                                              const typename IO::T *__restrict__ C,
+                                              const float *__restrict__ Dskip,
+                                              typename IO::T *__restrict__ y, int64_t batch,
+                                              int64_t dim, int N) {
+    constexpr int SPL = NT < 4 ? NT : 4;
+    constexpr int LPC = NT / SPL;
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t chans = batch * dim;
+    const int64_t c0 = i / LPC;
+    const int q = int(i - c0 * LPC);
+    const bool active = c0 < chans;
+    const int64_t c = active ? c0 : chans - 1;
+    const int64_t b = c / dim;
+    const int64_t d = c - b * dim;
+    const float xv = IO::ld(x, c);
+    const float dt = IO::ld(delta, c);
+
+    float h[SPL];
+    float *sp = state + c * N + q * SPL;
+    if constexpr (kVec) {
+        const float4 v = *reinterpret_cast<const float4 *>(sp);
+        h[0] = v.x; h[1] = v.y; h[2] = v.z; h[3] = v.w;
+    } else {
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) h[j] = (q * SPL + j < N) ? sp[j] : 0.f;
+    }
+    float yacc = 0.f;
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) {
+        const int n = q * SPL + j;
+        if (n < N) {
+            const float an = A[d * N + n];
+            const float z = dt * an;
+            const float abar = expf(z);
+            const float g = (an != 0.f) ? expm1f(z) / an : dt;
+            h[j] = fmaf(abar, h[j], g * (IO::ld(B, b * N + n) * xv));
+            yacc = fmaf(IO::ld(C, b * N + n), h[j], yacc);
+        }
+    }
+#pragma unroll
+    for (int off = LPC / 2; off >= 1; off /= 2) yacc += __shfl_xor(yacc, off, LPC);
+    if (!active) return;
+    if constexpr (kVec) {
+        *reinterpret_cast<float4 *>(sp) = make_float4(h[0], h[1], h[2], h[3]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < SPL; ++j)
+            if (q * SPL + j < N) sp[j] = h[j];
+    }
+    if (q == 0) {
+        const float dsk = Dskip ? Dskip[d] : 0.f;
+        y[c] = IO::enc(fmaf(dsk, xv, yacc));
+    }
+}
+
+int round_nt(int64_t N) { return N <= 1 ? 1 : N <= 2 ? 2 : N <= 4 ? 4 : N <= 8 ? 8 : 16; }
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+template <class IO, int NT>
+hipError_t forward_t(const FwdArgs &a, const FwdPlan &p, void *ws, hipStream_t s) {
+    using T = typename IO::T;
+    const int64_t rows = a.batch * a.L;
+    float *bc = static_cast<float *>(ws);
+    float *agg_sum = reinterpret_cast<float *>(static_cast<char *>(ws) +
+                                               align256(size_t(rows) * 2 * NT * sizeof(float)));
+    float *agg_h = agg_sum + align256(size_t(p.segments) * a.batch * a.dim * sizeof(float)) / sizeof(float);
+    const int64_t prep_threads = rows * NT;
+    hipLaunchKernelGGL((k_prep_bc<IO, NT>), dim3(unsigned((prep_threads + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const T *>(a.B), static_cast<const T *>(a.C), bc, rows, a.N);
+    if (p.segments > 1) {
+        hipLaunchKernelGGL((k_scan<IO, NT, false>), dim3(unsigned((p.segments - 1) * p.tiles)), dim3(kWave), 0, s,
+                           static_cast<const T *>(a.x), static_cast<const T *>(a.delta), a.A, bc, a.Dskip,
+                           static_cast<T *>(a.y), a.final_state, agg_sum, agg_h, a.batch, a.L, a.dim, a.N,
+                           p.seg_len, p.segments, p.tiles_per_batch, p.tiles);
+    }
+    hipLaunchKernelGGL((k_scan<IO, NT, true>), dim3(unsigned(p.segments * p.tiles)), dim3(kWave), 0, s,
+                       static_cast<const T *>(a.x), static_cast<const T *>(a.delta), a.A, bc, a.Dskip,
+                       static_cast<T *>(a.y), a.final_state, agg_sum, agg_h, a.batch, a.L, a.dim, a.N,
+                       p.seg_len, p.segments, p.tiles_per_batch, p.tiles);
+    return hipGetLastError();
+}
+
+template <class IO>
+hipError_t forward_io(const FwdArgs &a, const FwdPlan &p, void *ws, hipStream_t s) {
+    switch (p.nt) {
+        case 1: return forward_t<IO, 1>(a, p, ws, s);
+        case 2: return forward_t<IO, 2>(a, p, ws, s);
+        case 4: return forward_t<IO, 4>(a, p, ws, s);
+        case 8: return forward_t<IO, 8>(a, p, ws, s);
+        default: return forward_t<IO, 16>(a, p, ws, s);
+    }
+}
+
+template <class IO, int NT>
+hipError_t step_t(const StepArgs &a, hipStream_t s) {
+    using T = typename IO::T;
+    constexpr int SPL = NT < 4 ? NT : 4;
+    constexpr int LPC = NT / SPL;
+    const int64_t threads = a.batch * a.dim * LPC;
+    const dim3 grid(unsigned((threads + 255) / 256));
+    const bool vec = (SPL == 4) && (a.N == NT) && (reinterpret_cast<uintptr_t>(a.state) % 16 == 0);
+    if (vec) {
+        if constexpr (SPL == 4)
+            hipLaunchKernelGGL((k_step<IO, NT, true>), grid, dim3(256), 0, s, a.state,
+                               static_cast<const T *>(a.x), static_cast<const T *>(a.delta), a.A,
+                               static_cast<const T *>(a.B), static_cast<const T *>(a.C), a.Dskip,
+                               static_cast<T *>(a.y), a.batch, a.dim, a.N);
+    } else {
+        hipLaunchKernelGGL((k_step<IO, NT, false>), grid, dim3(256), 0, s, a.state,
+                           static_cast<const T *>(a.x), static_cast<const T *>(a.delta), a.A,
+                           static_cast<const T *>(a.B), static_cast<const T *>(a.C), a.Dskip,
+                           static_cast<T *>(a.y), a.batch, a.dim, a.N);
+    }
+    return hipGetLastError();
+}
+
+template <class IO>
+hipError_t step_io(const StepArgs &a, hipStream_t s) {
+    switch (round_nt(a.N)) {
+        case 1: return step_t<IO, 1>(a, s);
+        case 2: return step_t<IO, 2>(a, s);
+        case 4: return step_t<IO, 4>(a, s);
+        case 8: return step_t<IO, 8>(a, s);
+        default: return step_t<IO, 16>(a, s);
+    }
+}
+
+}  // namespace
+
+FwdPlan plan_forward(int64_t batch, int64_t L, int64_t dim, int64_t N) {
+    FwdPlan p{};
+    p.nt = round_nt(N);
+    p.tiles_per_batch = (dim + kWave - 1) / kWave;
+    p.tiles = batch * p.tiles_per_batch;
+    // enough segments for ~2 waves per SIMD (1024 SIMDs), segments of >= 64 tokens
+    const int64_t target_waves = 2048;
+    int64_t S = p.tiles > 0 ? (target_waves + p.tiles - 1) / p.tiles : 1;
+    S = std::min<int64_t>(S, std::max<int64_t>(1, L / 64));
+    S = std::max<int64_t>(1, std::min<int64_t>(S, 4096));
+    p.seg_len = L > 0 ? (L + S - 1) / S : 1;
+    p.segments = L > 0 ? int((L + p.seg_len - 1) / p.seg_len) : 1;
+    const size_t bc = align256(size_t(batch) * L * 2 * p.nt * sizeof(float));
+    const size_t sums = align256(size_t(p.segments) * batch * dim * sizeof(float));
+    const size_t hs = align256(size_t(p.segments) * batch * dim * p.nt * sizeof(float));
+    p.ws_bytes = bc + sums + hs;
+    return p;
+}
+
+hipError_t launch_forward(const FwdArgs &a, const FwdPlan &p, void *ws, hipStream_t s) {
+    return a.io == 1 ? forward_io<IoBF16>(a, p, ws, s) : forward_io<IoF32>(a, p, ws, s);
+}
+
+hipError_t launch_zero(float *ptr, int64_t count, hipStream_t s) {
+    if (count <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_zero, dim3(unsigned((count + 255) / 256)), dim3(256), 0, s, ptr, count);
+    return hipGetLastError();
+}
+
+hipError_t launch_step(const StepArgs &a, hipStream_t s) {
+    return a.io == 1 ? step_io<IoBF16>(a, s) : step_io<IoF32>(a, s);
+}
+
+}  // namespace sscan

@@ -1,0 +1,223 @@
+"""GPU parity of sscan_forward against the fp64 oracle, through the C ABI.
+
+Full-size workloads are compared element by element where the oracle finishes
+in seconds (tiny, Mamba-130M, Mamba-1.4B widths); the 2^20-token workload is
+compared on a full 4096-token prefix and on sampled channels over the whole
+sequence.  Edge shapes cover L=1, ragged L and dim, every N, both A paths,
+mixed A within a wave, A = 0 and A > 0, missing skip / final state, empty
+inputs, non-finite propagation and run-to-run determinism.
+"""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+from oracle.compare import TOL, rel_err
+from tests.gpuutil import announce, oracle_threads, to_dev, to_host, upload_scan
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import selective_state_space_77_amd as sscan  # noqa: E402
+
+
+def _run(t, wl, with_state=True, Dskip=True):
+    hs = torch.full((wl.batch, wl.dim, wl.dstate), float("nan"), device="cuda") if with_state else None
+    y = sscan.forward(t["x"], t["delta"], t["A"], t["B"], t["C"], t["Dskip"] if Dskip else None,
+                      final_state=hs)
+    torch.cuda.synchronize()
+    return to_host(y), (hs.cpu().numpy() if with_state else None)
+
+
+def _check_full(wl, seed=0, with_state=True, Dskip=True, inp=None):
+    announce(f"forward {wl.name} b={wl.batch} L={wl.seqlen} dim={wl.dim} N={wl.dstate} io={wl.io}")
+    inp = inp or datagen.scan_inputs(wl, seed)
+    t = upload_scan(inp, wl.io)
+    y, hs = _run(t, wl, with_state, Dskip)
+    yr, hr = oracle.forward(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"],
+                            inp["Dskip"] if Dskip else None, nthreads=oracle_threads(),
+                            want_state=with_state)
+    ey = rel_err(y, yr)
+    eh = rel_err(hs, hr) if with_state else 0.0
+    announce(f"  err(y)={ey:.3e} err(h)={eh:.3e}")
+    assert ey <= TOL[wl.io], ey
+    assert eh <= TOL[wl.io], eh
+    return ey, eh
+
+
+# ---------------------------------------------------------------- the named workloads
+
+def test_tiny_f32_random_A():
+    _check_full(datagen.workload("tiny_f32"))
+
+
+def test_mamba130m_width_f32_full():
+    _check_full(datagen.workload("mamba130m_f32"))
+
+
+def test_mamba1p4b_width_bf16_full():
+    """The benchmarked workload (4 x 8192 x 4096, N=16, bf16 I/O), every output checked."""
+    _check_full(datagen.workload("mamba1p4b_bf16"))
+
+
+def test_long_sequence_1m_tokens_bf16():
+    """2^20 tokens x 2048 channels: the full GPU output is produced in one call; the oracle
+    checks a full 4096-token prefix, and 12 sampled channels over the whole sequence
+    (every output of the last 4096 tokens and the final state)."""
+    wl = datagen.workload("long1m_bf16")
+    L, dim, N = wl.seqlen, wl.dim, wl.dstate
+    announce(f"forward {wl.name}: generating {2 * L * dim / 1e9:.1f} G bf16 inputs")
+    rng = np.random.default_rng(123)
+    chans = np.sort(rng.choice(dim, 12, replace=False))
+    x = torch.empty(1, L, dim, dtype=torch.bfloat16, device="cuda")
+    delta = torch.empty_like(x)
+    xs = np.empty((1, L, len(chans)), np.float32)
+    ds = np.empty_like(xs)
+    span = 64 * datagen.TBLK
+    for t0 in range(0, L, span):
+        t1 = min(L, t0 + span)
+        xb = datagen.gen_seq(wl, "x", t0, t1)
+        db = datagen.gen_seq(wl, "delta", t0, t1)
+        x[:, t0:t1] = to_dev(xb, "bf16")
+        delta[:, t0:t1] = to_dev(db, "bf16")
+        xs[:, t0:t1] = xb[:, :, chans]
+        ds[:, t0:t1] = db[:, :, chans]
+    B = datagen.gen_seq(wl, "B")
+    C = datagen.gen_seq(wl, "C")
+    A = datagen.gen_A(wl)
+    D = datagen.gen_Dskip(wl)
+    hs = torch.full((1, dim, N), float("nan"), device="cuda")
+    announce(f"forward {wl.name}: launching")
+    y = sscan.forward(x, delta, torch.from_numpy(A).cuda(), to_dev(B, "bf16"), to_dev(C, "bf16"),
+                      torch.from_numpy(D).cuda(), final_state=hs)
+    torch.cuda.synchronize()
+    # 1) prefix: every channel, first 4096 tokens
+    P = 4096
+    yr, _ = oracle.forward(to_host(x[:, :P]), to_host(delta[:, :P]), A, B[:, :P], C[:, :P], D,
+                           nthreads=oracle_threads(), want_state=False)
+    e1 = rel_err(to_host(y[:, :P]), yr)
+    # 2) sampled channels, whole sequence
+    ys, hr = oracle.forward(xs, ds, A[chans], B, C, D[chans], nthreads=oracle_threads())
+    idx = torch.from_numpy(chans).cuda()
+    yg = to_host(y[:, :, idx])
+    e2 = rel_err(yg[:, -P:], ys[:, -P:])
+    e3 = rel_err(hs[:, idx].cpu().numpy(), hr)
+    e4 = rel_err(yg, ys)
+    announce(f"  prefix err={e1:.3e} tail err={e2:.3e} final-state err={e3:.3e} sampled-all err={e4:.3e}")
+    for e in (e1, e2, e3, e4):
+        assert e <= TOL["bf16"], (e1, e2, e3, e4)
+
+
+# ---------------------------------------------------------------- edge shapes
+
+EDGE = [
+    # (batch, L, dim, N, io, a_init)
+    (1, 1, 64, 16, "f32", "s4d_real"),
+    (1, 1, 5, 3, "f32", "loguniform"),
+    (2, 777, 100, 16, "f32", "s4d_real"),
+    (2, 777, 100, 16, "bf16", "loguniform"),
+    (3, 129, 65, 1, "f32", "loguniform"),
+    (3, 129, 65, 1, "f32", "s4d_real"),
+    (1, 300, 33, 2, "bf16", "s4d_real"),
+    (1, 513, 70, 5, "f32", "s4d_real"),
+    (2, 400, 130, 8, "f32", "loguniform"),
+    (1, 20000, 64, 16, "f32", "s4d_real"),   # one tile: ~300 time segments
+    (1, 9000, 7, 4, "bf16", "loguniform"),
+]
+
+
+@pytest.mark.parametrize("shape", EDGE, ids=lambda s: "b{}_L{}_d{}_N{}_{}_{}".format(*s))
+def test_edge_shapes(shape):
+    batch, L, dim, N, io, a_init = shape
+    wl = datagen.custom(f"edge_{batch}_{L}_{dim}_{N}_{io}_{a_init}", batch, L, dim, N, io, a_init, key=7)
+    _check_full(wl)
+
+
+def test_without_skip_and_without_final_state():
+    wl = datagen.custom("noskip", 2, 300, 96, 16, "f32", "s4d_real", key=8)
+    _check_full(wl, with_state=False, Dskip=False)
+
+
+def test_mixed_A_within_a_wave_takes_the_general_path():
+    """Channels 0..31 of the wave S4D-real, 32..63 random: the whole wave must still match."""
+    wl = datagen.custom("mixed", 2, 500, 64, 16, "f32", "s4d_real", key=9)
+    inp = datagen.scan_inputs(wl)
+    rnd = datagen.gen_A(datagen.custom("mixedA", 1, 1, 64, 16, "f32", "loguniform", key=9))
+    inp["A"] = np.concatenate([inp["A"][:32], rnd[32:]]).astype(np.float32)
+    _check_full(wl, inp=inp)
+
+
+def test_zero_and_positive_A():
+    """A = 0 (Bbar -> delta*B limit) and small A > 0 (growing mode) per channel."""
+    wl = datagen.custom("zeroA", 1, 200, 70, 4, "f32", "loguniform", key=10)
+    inp = datagen.scan_inputs(wl)
+    A = inp["A"].copy()
+    A[3, :] = 0.0
+    A[5, 1] = 0.0
+    A[9, :] = 0.05
+    A[10, 2] = 0.2
+    inp["A"] = A
+    _check_full(wl, inp=inp)
+
+
+def test_s4d_scaled_rows_take_the_fast_path_correctly():
+    """A[d,n] = (n+1)*A[d,0] with a different A[d,0] per channel."""
+    wl = datagen.custom("s4dscaled", 2, 1000, 128, 16, "bf16", "s4d_real", key=11)
+    inp = datagen.scan_inputs(wl)
+    scale = np.linspace(0.1, 3.0, 128, dtype=np.float32)[:, None]
+    inp["A"] = (inp["A"] * scale).astype(np.float32)
+    _check_full(wl, inp=inp)
+
+
+def test_empty_inputs():
+    dev = "cuda"
+    x = torch.empty(1, 0, 8, device=dev)
+    hs = torch.full((1, 8, 4), 7.0, device=dev)
+    y = sscan.forward(x, x.clone(), torch.zeros(8, 4, device=dev), torch.empty(1, 0, 4, device=dev),
+                      torch.empty(1, 0, 4, device=dev), final_state=hs)
+    torch.cuda.synchronize()
+    assert y.shape == (1, 0, 8)
+    assert torch.all(hs == 0)
+    z = torch.empty(0, 5, 8, device=dev)
+    sscan.forward(z, z.clone(), torch.zeros(8, 4, device=dev), torch.empty(0, 5, 4, device=dev),
+                  torch.empty(0, 5, 4, device=dev))
+    torch.cuda.synchronize()
+
+
+def test_non_finite_inputs_propagate_like_the_oracle():
+    wl = datagen.custom("nan", 1, 200, 64, 16, "f32", "s4d_real", key=12)
+    inp = datagen.scan_inputs(wl)
+    inp["x"][0, 50, 3] = np.nan
+    inp["delta"][0, 120, 7] = np.inf
+    t = upload_scan(inp, "f32")
+    y, hs = _run(t, wl)
+    yr, hr = oracle.forward(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["Dskip"])
+    np.testing.assert_array_equal(np.isnan(y), np.isnan(yr))
+    np.testing.assert_array_equal(np.isnan(hs), np.isnan(hr))
+    ok = np.isfinite(yr)
+    assert rel_err(y[ok], yr[ok]) <= TOL["f32"]
+
+
+def test_run_to_run_bitwise_determinism():
+    wl = datagen.custom("det", 2, 3000, 256, 16, "bf16", "s4d_real", key=13)
+    t = upload_scan(datagen.scan_inputs(wl), "bf16")
+    y1, h1 = _run(t, wl)
+    y2, h2 = _run(t, wl)
+    np.testing.assert_array_equal(y1, y2)
+    np.testing.assert_array_equal(h1, h2)
+
+
+def test_runs_on_a_side_stream():
+    wl = datagen.custom("stream", 1, 1000, 128, 16, "f32", "s4d_real", key=14)
+    inp = datagen.scan_inputs(wl)
+    t = upload_scan(inp, "f32")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y = sscan.forward(t["x"], t["delta"], t["A"], t["B"], t["C"], t["Dskip"])
+    s.synchronize()
+    yr, _ = oracle.forward(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["Dskip"],
+                           want_state=False)
+    assert rel_err(to_host(y), yr) <= TOL["f32"]

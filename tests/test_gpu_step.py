@@ -1,0 +1,151 @@
+"""GPU parity of sscan_step (the single-token recurrent update) through the C ABI.
+
+The decode workload (batch 256 x 5120 channels x N=16, bf16 I/O, fp32 state in
+HBM updated in place, 1000 consecutive steps) is checked against the oracle's
+sequential loop on sampled channels at every step, and for every channel
+against the GPU forward pass over the same 1000 tokens (L steps == one
+forward, a property that holds at any size; the forward itself is
+oracle-checked in test_gpu_parity.py).
+"""
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+from oracle.compare import TOL, rel_err
+from tests.gpuutil import announce, oracle_threads, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import selective_state_space_77_amd as sscan  # noqa: E402
+
+
+def test_decode_1000_steps_bf16():
+    wl = datagen.workload("decode_bf16")
+    S, batch, dim, N = wl.seqlen, wl.batch, wl.dim, wl.dstate
+    announce(f"step {wl.name}: generating {S} steps of {batch}x{dim}")
+    bias = datagen.gen_dt_bias(wl)
+    X = torch.empty(S, batch, dim, dtype=torch.bfloat16, device="cuda")
+    Dl = torch.empty_like(X)
+    Bs = torch.empty(S, batch, N, dtype=torch.bfloat16, device="cuda")
+    Cs = torch.empty_like(Bs)
+    rng = np.random.default_rng(7)
+    cb = rng.choice(batch, 24)
+    cd = rng.choice(dim, 24)
+    xs = np.empty((S, 24), np.float32)
+    dsm = np.empty_like(xs)
+    Bh = np.empty((S, batch, N), np.float32)
+    Ch = np.empty_like(Bh)
+
+    def gen(k):
+        return k, datagen.step_inputs(wl, k, bias=bias)
+
+    with ThreadPoolExecutor(oracle_threads()) as ex:
+        for k, s in ex.map(gen, range(S)):
+            X[k] = to_dev(s["x"], "bf16")
+            Dl[k] = to_dev(s["delta"], "bf16")
+            Bs[k] = to_dev(s["B"], "bf16")
+            Cs[k] = to_dev(s["C"], "bf16")
+            xs[k] = s["x"][cb, cd]
+            dsm[k] = s["delta"][cb, cd]
+            Bh[k], Ch[k] = s["B"], s["C"]
+    A = datagen.gen_A(wl)
+    D = datagen.gen_Dskip(wl)
+    At, Dt = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
+    state = torch.zeros(batch, dim, N, device="cuda")
+    Y = torch.empty_like(X)
+    announce(f"step {wl.name}: {S} steps")
+    for k in range(S):
+        sscan.step(state, X[k], Dl[k], At, Bs[k], Cs[k], Dt, y_t=Y[k])
+    torch.cuda.synchronize()
+
+    # sampled channels against the oracle's sequential loop, every step
+    st = np.zeros((24, 1, N))
+    ys = np.empty((S, 24))
+    for j in range(24):
+        b, d = cb[j], cd[j]
+        yj, hj = oracle.forward(xs[None, :, j:j + 1], dsm[None, :, j:j + 1], A[d:d + 1],
+                                Bh[None, :, b], Ch[None, :, b], D[d:d + 1])
+        ys[:, j] = yj[0, :, 0]
+        st[j] = hj[0]
+    yg = to_host(Y[:, torch.from_numpy(cb).cuda(), torch.from_numpy(cd).cuda()])
+    e1 = max(rel_err(yg[k], ys[k]) for k in range(S))
+    e2 = rel_err(state[torch.from_numpy(cb).cuda(), torch.from_numpy(cd).cuda()].cpu().numpy(), st[:, 0])
+    announce(f"  per-step y err (max over steps)={e1:.3e} final-state err={e2:.3e}")
+    assert e1 <= TOL["bf16"] and e2 <= TOL["bf16"]
+
+    # every channel: 1000 steps == one forward pass over the same tokens
+    xf = X.permute(1, 0, 2).contiguous()
+    df = Dl.permute(1, 0, 2).contiguous()
+    hf = torch.empty(batch, dim, N, device="cuda")
+    yf = sscan.forward(xf, df, At, Bs.permute(1, 0, 2).contiguous(), Cs.permute(1, 0, 2).contiguous(),
+                       Dt, final_state=hf)
+    torch.cuda.synchronize()
+    e3 = rel_err(state.cpu().numpy(), hf.cpu().numpy().astype(np.float64))
+    e4 = rel_err(to_host(Y.permute(1, 0, 2)), to_host(yf))
+    announce(f"  steps vs forward: state err={e3:.3e} y err={e4:.3e}")
+    assert e3 <= 1e-4 and e4 <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("N,io", [(16, "f32"), (16, "bf16"), (8, "f32"), (5, "bf16"), (1, "f32"), (2, "f32")])
+def test_steps_match_the_oracle_small(N, io):
+    wl = datagen.custom(f"stepsmall{N}{io}", 3, 40, 70, N, io, "loguniform", key=20 + N, mode="step")
+    A = datagen.gen_A(wl)
+    D = datagen.gen_Dskip(wl)
+    bias = datagen.gen_dt_bias(wl)
+    At, Dt = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
+    state = torch.zeros(wl.batch, wl.dim, N, device="cuda")
+    ref = np.zeros((wl.batch, wl.dim, N))
+    for k in range(wl.seqlen):
+        s = datagen.step_inputs(wl, k, bias=bias)
+        yt = sscan.step(state, to_dev(s["x"], io), to_dev(s["delta"], io), At, to_dev(s["B"], io),
+                        to_dev(s["C"], io), Dt)
+        torch.cuda.synchronize()
+        yr, ref = oracle.step(ref, s["x"], s["delta"], A, s["B"], s["C"], D)
+        assert rel_err(to_host(yt), yr) <= TOL[io], k
+    assert rel_err(state.cpu().numpy(), ref) <= TOL[io]
+
+
+def test_misaligned_state_uses_the_scalar_path():
+    """A state view that is not 16-byte aligned still updates correctly."""
+    wl = datagen.custom("stepmis", 2, 5, 33, 16, "f32", "s4d_real", key=40, mode="step")
+    A, D = datagen.gen_A(wl), datagen.gen_Dskip(wl)
+    bias = datagen.gen_dt_bias(wl)
+    buf = torch.zeros(1 + wl.batch * wl.dim * 16, device="cuda")
+    state = buf[1:].view(wl.batch, wl.dim, 16)
+    ref = np.zeros((wl.batch, wl.dim, 16))
+    for k in range(wl.seqlen):
+        s = datagen.step_inputs(wl, k, bias=bias)
+        sscan.step(state, to_dev(s["x"], "f32"), to_dev(s["delta"], "f32"), torch.from_numpy(A).cuda(),
+                   to_dev(s["B"], "f32"), to_dev(s["C"], "f32"), torch.from_numpy(D).cuda())
+        _, ref = oracle.step(ref, s["x"], s["delta"], A, s["B"], s["C"], D)
+    torch.cuda.synchronize()
+    assert rel_err(state.cpu().numpy(), ref) <= TOL["f32"]
+    assert buf[0].item() == 0.0
+
+
+def test_prefill_then_decode_handover():
+    """forward() over a prompt, then step() from its final state, equals the oracle over
+    prompt + continuation (the state snapshot is the hand-over)."""
+    wl = datagen.custom("handover", 2, 300, 96, 16, "bf16", "s4d_real", key=41)
+    inp = datagen.scan_inputs(wl)
+    P = 250
+    t = {k: (to_dev(v[:, :P], "bf16") if k in ("x", "delta", "B", "C") else torch.from_numpy(v).cuda())
+         for k, v in inp.items()}
+    hs = torch.empty(wl.batch, wl.dim, 16, device="cuda")
+    sscan.forward(t["x"], t["delta"], t["A"], t["B"], t["C"], t["Dskip"], final_state=hs)
+    ys = []
+    for k in range(P, wl.seqlen):
+        ys.append(to_host(sscan.step(hs, to_dev(inp["x"][:, k], "bf16"), to_dev(inp["delta"][:, k], "bf16"),
+                                     t["A"], to_dev(inp["B"][:, k], "bf16"), to_dev(inp["C"][:, k], "bf16"),
+                                     t["Dskip"])))
+    torch.cuda.synchronize()
+    yr, hr = oracle.forward(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["Dskip"])
+    assert rel_err(np.stack(ys, 1), yr[:, P:]) <= TOL["bf16"]
+    assert rel_err(hs.cpu().numpy(), hr) <= TOL["bf16"]
