@@ -130,7 +130,7 @@ def gen_A(wl: Workload, seed: int = 0) -> np.ndarray:
     """A[d, n] (fp32, shape (dim, N))."""
     if wl.a_init == "s4d_real":
         row = -np.arange(1, wl.dstate + 1, dtype=np.float64)
-        return np.broadcast_to(row, (wl.dim, wl.dstate)).astype(np.float32)
+        return np.ascontiguousarray(np.broadcast_to(row, (wl.dim, wl.dstate)), dtype=np.float32)
     if wl.a_init == "loguniform":
         u = _rng(seed, wl, "A").uniform(np.log(0.5), np.log(4.0), size=(wl.dim, wl.dstate))
         return (-np.exp(u)).astype(np.float32)

@@ -9,16 +9,35 @@ namespace sscan {
 
 constexpr int kWave = 64;  // CDNA wavefront width: one lane per channel
 
-// Work split of one forward pass: the sequence is cut into `segments` time
-// segments of `seg_len` tokens (the last may be shorter); each wave scans one
-// segment of 64 channels of one batch row.
+// Launch shape of the lockstep kernel: kLockW waves per 64-channel tile, each
+// taking runs of kLockT tokens; used when tiles * kLockW >= kLockMinWaves.
+#ifndef SSCAN_LOCK_W
+#define SSCAN_LOCK_W 8
+#endif
+#ifndef SSCAN_LOCK_T
+#define SSCAN_LOCK_T 32
+#endif
+#ifndef SSCAN_TARGET_WAVES
+#define SSCAN_TARGET_WAVES 2048
+#endif
+constexpr int kLockW = SSCAN_LOCK_W;
+constexpr int kLockT = SSCAN_LOCK_T;
+constexpr int64_t kLockMinWaves = 1024;
+constexpr int64_t kTargetWaves = SSCAN_TARGET_WAVES;  // segment kernels: waves to aim for
+
+// Work split of one forward pass.  Segment kernels cut the sequence into
+// `segments` time segments of `seg_len` tokens (the last may be shorter); each
+// wave scans one segment of 64 channels of one batch row.  The lockstep kernel
+// gives each 64-channel tile one workgroup for the whole sequence.
 struct FwdPlan {
     int64_t tiles_per_batch;  // ceil(dim / 64)
     int64_t tiles;            // batch * tiles_per_batch
     int64_t seg_len;
     int segments;
     int nt;                   // dstate rounded up to 1, 2, 4, 8 or 16
-    size_t ws_bytes;          // scratch: [B/(n+1), C] rows + segment aggregates
+    bool lockstep;            // structured-real tiles use the lockstep kernel
+    size_t off_bc, off_flags, off_sum, off_h;  // scratch layout
+    size_t ws_bytes;          // scratch: [B/(n+1), C] rows, tile flags, segment aggregates
 };
 
 FwdPlan plan_forward(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);

@@ -69,24 +69,44 @@ struct IoBF16 {
 };
 
 // ----------------------------------------------------------------------------
-// Stage B/(n+1) and C of every token as fp32 rows of 2*NT floats, so the scan
-// reads one token's parameters with two scalar loads.  States n >= N (padding
-// up to NT) get B = C = 0 and therefore stay zero.
+// Prologue of every forward pass, one launch with two roles:
+//  * blocks [0, prep_blocks): stage B/(n+1) and C of every token as fp32 rows
+//    of 2*NT floats, so a scan wave reads one token's parameters with two
+//    scalar loads.  States n >= N (padding up to NT) get B = C = 0 and stay 0.
+//  * the remaining blocks: one wave per 64-channel tile decides whether every
+//    A row of the tile has the structured-real form A[d,n] = (n+1)*A[d,0],
+//    A[d,0] < 0 (tile_fast = 1) or not (0).  Later launches read the flag and
+//    take the matching path; A is never copied to the host.
 template <class IO, int NT>
-__global__ __launch_bounds__(256) void k_prep_bc(const typename IO::T *__restrict__ B,
-                                                 const typename IO::T *__restrict__ C,
-                                                 float *__restrict__ bc, int64_t rows, int N) {
-    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (i >= rows * NT) return;
-    const int64_t r = i / NT;
-    const int n = int(i - r * NT);
-    float bv = 0.f, cv = 0.f;
-    if (n < N) {
-        bv = IO::ld(B, r * N + n);
-        cv = IO::ld(C, r * N + n);
+__global__ __launch_bounds__(256) void k_prep(const typename IO::T *__restrict__ B,
+                                              const typename IO::T *__restrict__ C,
+                                              float *__restrict__ bc, int64_t rows, int N,
+                                              const float *__restrict__ A, int64_t dim,
+                                              int *__restrict__ tile_fast, int64_t tiles_per_batch,
+                                              int64_t prep_blocks) {
+    if (blockIdx.x < prep_blocks) {
+        const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+        if (i >= rows * NT) return;
+        const int64_t r = i / NT;
+        const int n = int(i - r * NT);
+        float bv = 0.f, cv = 0.f;
+        if (n < N) {
+            bv = IO::ld(B, r * N + n);
+            cv = IO::ld(C, r * N + n);
+        }
+        bc[r * (2 * NT) + n] = bv / float(n + 1);
+        bc[r * (2 * NT) + NT + n] = cv;
+        return;
     }
-    bc[r * (2 * NT) + n] = bv / float(n + 1);
-    bc[r * (2 * NT) + NT + n] = cv;
+    const int64_t dt = (int64_t(blockIdx.x) - prep_blocks) * 4 + threadIdx.x / kWave;
+    if (dt >= tiles_per_batch) return;  // whole wave
+    const int lane = threadIdx.x % kWave;
+    const int64_t d = min(dt * kWave + lane, dim - 1);
+    const float a0 = A[d * N];
+    bool ok = (a0 < 0.f) && (a0 > -INFINITY);
+    for (int n = 1; n < N; ++n) ok = ok && (A[d * N + n] == a0 * float(n + 1));
+    const bool all_ok = __all(ok);
+    if (lane == 0) tile_fast[dt] = all_ok ? 1 : 0;
 }
 
 __global__ __launch_bounds__(256) void k_zero(float *__restrict__ p, int64_t count) {
@@ -95,26 +115,31 @@ __global__ __launch_bounds__(256) void k_zero(float *__restrict__ p, int64_t cou
 }
 
 // ----------------------------------------------------------------------------
-// One wave = 64 channels x one time segment.  kMain = false: aggregate pass;
-// kMain = true: carried-state scan with readout.
+// Segment scan: one wave = 64 channels x one time segment.  kMain = false:
+// aggregate pass; kMain = true: carried-state scan with readout.  kFast picks
+// the structured-real (one exp per token) or general (exp and expm1 per state)
+// update; a wave whose tile flag says otherwise exits at once.
 constexpr int kUnroll = 8;  // tokens of x/delta prefetched ahead
 
-template <class IO, int NT, bool kMain>
-__global__ __launch_bounds__(kWave) void k_scan(
+template <class IO, int NT, bool kMain, bool kFast>
+__global__ __launch_bounds__(kWave) void k_seg(
     const typename IO::T *__restrict__ x, const typename IO::T *__restrict__ delta,
     const float *__restrict__ A, const float *__restrict__ bc, const float *__restrict__ Dskip,
     typename IO::T *__restrict__ y, float *__restrict__ final_state,
-    float *__restrict__ agg_sum, float *__restrict__ agg_h, int64_t batch, int64_t L, int64_t dim,
-    int N, int64_t seg_len, int segments, int64_t tiles_per_batch, int64_t tiles) {
+    float *__restrict__ agg_sum, float *__restrict__ agg_h, const int *__restrict__ tile_fast,
+    int64_t batch, int64_t L, int64_t dim, int N, int64_t seg_len, int segments,
+    int64_t tiles_per_batch, int64_t tiles) {
     using T = typename IO::T;
     const int lane = threadIdx.x;
     const int64_t wid = blockIdx.x;
     const int seg = int(wid / tiles);
     const int64_t tile = wid - int64_t(seg) * tiles;
     const int64_t b = tile / tiles_per_batch;
-    const int64_t dbase = (tile - b * tiles_per_batch) * kWave;  // first channel of the wave
+    const int64_t dt = tile - b * tiles_per_batch;
+    if ((tile_fast[dt] != 0) != kFast) return;
+    const int64_t dbase = dt * kWave;  // first channel of the wave
     const bool active = dbase + lane < dim;
-    const int lo = active ? lane : int(dim - 1 - dbase);         // clamped lane offset
+    const int lo = active ? lane : int(dim - 1 - dbase);  // clamped lane offset
     const int64_t d = dbase + lo;
     const int64_t t0 = int64_t(seg) * seg_len;
     const int64_t t1 = min(L, t0 + seg_len);
@@ -122,13 +147,9 @@ __global__ __launch_bounds__(kWave) void k_scan(
     float a[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) a[n] = (n < N) ? A[d * N + n] : 0.f;
-    bool s4d = (a[0] < 0.f) && (a[0] > -INFINITY);
-#pragma unroll
-    for (int n = 1; n < NT; ++n)
-        if (n < N) s4d = s4d && (a[n] == a[0] * float(n + 1));
-    const bool fast = __all(s4d);
 
-    // ---- carried state at the segment start (pass 2 only)
+    // ---- carried state at the segment start (pass 2 only): fold the aggregates
+    // of all earlier segments with (a1,b1) o (a2,b2) = (a1*a2, a2*b1 + b2)
     float h[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) h[n] = 0.f;
@@ -136,7 +157,7 @@ __global__ __launch_bounds__(kWave) void k_scan(
         for (int j = 0; j < seg; ++j) {
             const int64_t cj = int64_t(j) * batch + b;
             const float s = agg_sum[cj * dim + d];
-            if (fast) {
+            if (kFast) {
                 const float rho = exp2_hw(a[0] * kLog2e * s);
                 float dec = rho;
 #pragma unroll
@@ -166,11 +187,11 @@ __global__ __launch_bounds__(kWave) void k_scan(
         xr[u] = xrow[t * dim + lo];
         dr[u] = drow[t * dim + lo];
     }
-    float brow[2 * NT];
-#pragma unroll
-    for (int i = 0; i < 2 * NT; ++i) brow[i] = bcrow[t0 * (2 * NT) + i];
 
-    if (fast) {
+    if constexpr (kFast) {
+        float brow[2 * NT];
+#pragma unroll
+        for (int i = 0; i < 2 * NT; ++i) brow[i] = bcrow[t0 * (2 * NT) + i];
         const float alpha = -a[0];
         const float inv_alpha = 1.f / alpha;
         const float a2 = a[0] * kLog2e;
@@ -221,12 +242,6 @@ __global__ __launch_bounds__(kWave) void k_scan(
 #pragma unroll
         for (int n = 0; n < NT; ++n) h[n] = k[n] * inv_alpha;
     } else {
-        float a2n[NT], inva[NT];
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-            a2n[n] = a[n] * kLog2e;
-            inva[n] = (a[n] != 0.f) ? 1.f / a[n] : 0.f;
-        }
         for (int64_t tc = t0; tc < t1; tc += kUnroll) {
             float xv[kUnroll], dv[kUnroll];
 #pragma unroll
@@ -240,17 +255,18 @@ __global__ __launch_bounds__(kWave) void k_scan(
                 xr[u] = xrow[t * dim + lo];
                 dr[u] = drow[t * dim + lo];
             }
+#pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 const int64_t t = tc + u;
                 if (t < t1) {
                     const float *row = bcrow + t * (2 * NT);
+                    const float dtv = dv[u];
                     float yacc = 0.f;
-#pragma unroll
                     for (int n = 0; n < NT; ++n) {
-                        const float dt = dv[u];
-                        const float abar = exp2_hw(dt * a2n[n]);
+                        const float an = a[n];
+                        const float abar = exp2_hw(dtv * (an * kLog2e));
                         // (exp(dt*A) - 1)/A without cancellation; dt when A == 0
-                        const float g = (a[n] != 0.f) ? expm1f(dt * a[n]) * inva[n] : dt;
+                        const float g = (an != 0.f) ? expm1f(dtv * an) / an : dtv;
                         const float bn = row[n] * float(n + 1);
                         h[n] = fmaf(abar, h[n], g * (bn * xv[u]));
                         if (kMain) yacc = fmaf(row[NT + n], h[n], yacc);
@@ -258,7 +274,7 @@ __global__ __launch_bounds__(kWave) void k_scan(
                     if (kMain) {
                         if (active) yrow[t * dim + lo] = IO::enc(fmaf(dsk, xv[u], yacc));
                     } else {
-                        dsum += dv[u];
+                        dsum += dtv;
                     }
                 }
             }
@@ -275,6 +291,189 @@ __global__ __launch_bounds__(kWave) void k_scan(
 #pragma unroll
         for (int n = 0; n < NT; ++n)
             if (n < N) final_state[(b * dim + d) * N + n] = h[n];
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Lockstep chunked scan for structured-real tiles (one launch, no aggregate
+// pass).  A workgroup of W waves owns one 64-channel tile for the whole
+// sequence, processed in chunks of W*TS tokens; wave w takes the w-th run of
+// TS tokens of every chunk:
+//   1. local pass: wave 0 starts from the chunk's carried state, the others
+//      from zero; each keeps its TS finished outputs and the running decay
+//      rho_tau = prod r (r = exp(delta*A[d,0])) in VGPRs;
+//   2. every wave publishes (sum of delta, local final state) in LDS; after a
+//      barrier the states are split across the waves (NT/W each) and every
+//      wave folds the W aggregates of its states in order with the
+//      associative combine, writing the state entering each wave's run and
+//      the chunk's carry-out back to LDS;
+//   3. after a second barrier waves 1..W-1 add the contribution of the state
+//      they entered with, sum_n C_n rho_tau^(n+1) k_in[n], evaluated as a
+//      Horner polynomial in rho_tau, and store y.
+template <class IO, int NT, int W, int TS>
+__global__ __launch_bounds__(W *kWave) void k_lockstep(
+    const typename IO::T *__restrict__ x, const typename IO::T *__restrict__ delta,
+    const float *__restrict__ A, const float *__restrict__ bc, const float *__restrict__ Dskip,
+    typename IO::T *__restrict__ y, float *__restrict__ final_state,
+    const int *__restrict__ tile_fast, int64_t L, int64_t dim, int N, int64_t tiles_per_batch) {
+    using T = typename IO::T;
+    constexpr int U = kUnroll;
+    static_assert(TS % U == 0, "TS must be a multiple of the prefetch group");
+    constexpr int NPW = (NT + W - 1) / W;  // states each wave folds
+    constexpr int64_t CH = int64_t(W) * TS;
+    __shared__ float s_sum[W][kWave];
+    __shared__ float s_k[W][NT][kWave];
+    __shared__ float s_pre[W][NT][kWave];  // [0]: chunk carry-out; [j]: state entering run j
+
+    const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
+    const int lane = int(threadIdx.x) % kWave;
+    const int64_t tile = blockIdx.x;
+    const int64_t b = tile / tiles_per_batch;
+    const int64_t dt = tile - b * tiles_per_batch;
+    if (!tile_fast[dt]) return;  // whole workgroup
+    const int64_t dbase = dt * kWave;
+    const bool active = dbase + lane < dim;
+    const int lo = active ? lane : int(dim - 1 - dbase);
+    const int64_t d = dbase + lo;
+    const float a0 = A[d * N];
+    const float alpha = -a0, inv_alpha = 1.f / alpha, a2 = a0 * kLog2e;
+    const float dsk = Dskip ? Dskip[d] : 0.f;
+    const T *xrow = x + (b * L) * dim + dbase;
+    const T *drow = delta + (b * L) * dim + dbase;
+    T *yrow = y + (b * L) * dim + dbase;
+    const float *bcrow = bc + (b * L) * (2 * NT);
+    const int64_t nchunks = (L + CH - 1) / CH;
+
+    // token of the j-th element of this wave's stream (its run in every chunk)
+    auto tok = [&](int64_t j) -> int64_t { return (j / TS) * CH + int64_t(w) * TS + (j % TS); };
+
+    T xr[U], dr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t t = min(tok(u), L - 1);
+        xr[u] = xrow[t * dim + lo];
+        dr[u] = drow[t * dim + lo];
+    }
+    float k[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) k[n] = 0.f;
+
+    for (int64_t c = 0; c < nchunks; ++c) {
+        const int64_t t0 = c * CH + int64_t(w) * TS;
+        const int nv = int(max<int64_t>(0, min<int64_t>(TS, L - t0)));
+        if (w == 0) {
+            if (c > 0) {
+#pragma unroll
+                for (int n = 0; n < NT; ++n) k[n] = s_pre[0][n][lane];
+            }
+        } else {
+#pragma unroll
+            for (int n = 0; n < NT; ++n) k[n] = 0.f;
+        }
+        float yl[TS], rho[TS];
+        float cum = 1.f, dsum = 0.f;
+        float brow[2 * NT];
+        const int64_t tlast = min(t0 + TS, L) - 1;  // last valid token of the run (< t0 if empty)
+#pragma unroll
+        for (int i = 0; i < 2 * NT; ++i) brow[i] = bcrow[min(t0, L - 1) * (2 * NT) + i];
+#pragma unroll
+        for (int g = 0; g < TS / U; ++g) {
+            float xv[U], dv[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                xv[u] = IO::cvt(xr[u]);
+                dv[u] = IO::cvt(dr[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t t = min(tok(c * TS + (g + 1) * U + u), L - 1);
+                xr[u] = xrow[t * dim + lo];
+                dr[u] = drow[t * dim + lo];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int tau = g * U + u;
+                if (tau < nv) {
+                    const int64_t t = t0 + tau;
+                    float bnext[2 * NT];
+                    const int64_t tn = min(t + 1, tlast);
+#pragma unroll
+                    for (int i = 0; i < 2 * NT; ++i) bnext[i] = bcrow[tn * (2 * NT) + i];
+                    const float r = exp2_hw(dv[u] * a2);
+                    cum *= r;
+                    rho[tau] = cum;
+                    dsum += dv[u];
+                    float pw = r, yacc = 0.f;
+#pragma unroll
+                    for (int n = 0; n < NT; ++n) {
+                        const float e = fmaf(-brow[n], xv[u], k[n]);
+                        const float q = pw * e;
+                        k[n] = fmaf(brow[n], xv[u], q);
+                        yacc = fmaf(brow[NT + n], k[n], yacc);
+                        pw *= r;
+                    }
+                    const float yv = fmaf(yacc, inv_alpha, dsk * xv[u]);
+                    if (w == 0) {
+                        if (active) yrow[t * dim + lo] = IO::enc(yv);
+                    } else {
+                        yl[tau] = yv;
+                    }
+#pragma unroll
+                    for (int i = 0; i < 2 * NT; ++i) brow[i] = bnext[i];
+                }
+            }
+        }
+        s_sum[w][lane] = dsum;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) s_k[w][n][lane] = k[n];
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < NPW; ++i) {
+            const int n = w * NPW + i;
+            if (n < NT) {
+                const float an2 = a2 * float(n + 1);
+                float P = s_k[0][n][lane];  // run 0 started from the carry: its end state is exact
+                for (int j = 1; j < W; ++j) {
+                    s_pre[j][n][lane] = P;
+                    P = fmaf(exp2_hw(an2 * s_sum[j][lane]), P, s_k[j][n][lane]);
+                }
+                s_pre[0][n][lane] = P;
+            }
+        }
+        __syncthreads();
+        if (w != 0 && nv > 0) {
+            float kin[NT];
+#pragma unroll
+            for (int n = 0; n < NT; ++n) kin[n] = s_pre[w][n][lane];
+            float crow[NT];
+#pragma unroll
+            for (int n = 0; n < NT; ++n) crow[n] = bcrow[t0 * (2 * NT) + NT + n];
+#pragma unroll
+            for (int tau = 0; tau < TS; ++tau) {
+                if (tau < nv) {
+                    const int64_t t = t0 + tau;
+                    float cnext[NT];
+                    const int64_t tn = min(t + 1, tlast);
+#pragma unroll
+                    for (int n = 0; n < NT; ++n) cnext[n] = bcrow[tn * (2 * NT) + NT + n];
+                    const float rr = rho[tau];
+                    float acc = crow[NT - 1] * kin[NT - 1];
+#pragma unroll
+                    for (int n = NT - 2; n >= 0; --n) acc = fmaf(acc, rr, crow[n] * kin[n]);
+                    acc *= rr;
+                    if (active) yrow[t * dim + lo] = IO::enc(fmaf(acc, inv_alpha, yl[tau]));
+#pragma unroll
+                    for (int n = 0; n < NT; ++n) crow[n] = cnext[n];
+                }
+            }
+        }
+    }
+    if (final_state && active) {
+#pragma unroll
+        for (int i = 0; i < NPW; ++i) {
+            const int n = w * NPW + i;
+            if (n < N) final_state[(b * dim + d) * N + n] = s_pre[0][n][lane] * inv_alpha;
+        }
     }
 }
 
@@ -351,24 +550,37 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 template <class IO, int NT>
 hipError_t forward_t(const FwdArgs &a, const FwdPlan &p, void *ws, hipStream_t s) {
     using T = typename IO::T;
+    char *base = static_cast<char *>(ws);
+    float *bc = reinterpret_cast<float *>(base + p.off_bc);
+    int *flags = reinterpret_cast<int *>(base + p.off_flags);
+    float *agg_sum = reinterpret_cast<float *>(base + p.off_sum);
+    float *agg_h = reinterpret_cast<float *>(base + p.off_h);
+    const T *x = static_cast<const T *>(a.x), *dl = static_cast<const T *>(a.delta);
+    T *y = static_cast<T *>(a.y);
     const int64_t rows = a.batch * a.L;
-    float *bc = static_cast<float *>(ws);
-    float *agg_sum = reinterpret_cast<float *>(static_cast<char *>(ws) +
-                                               align256(size_t(rows) * 2 * NT * sizeof(float)));
-    float *agg_h = agg_sum + align256(size_t(p.segments) * a.batch * a.dim * sizeof(float)) / sizeof(float);
-    const int64_t prep_threads = rows * NT;
-    hipLaunchKernelGGL((k_prep_bc<IO, NT>), dim3(unsigned((prep_threads + 255) / 256)), dim3(256), 0, s,
-                       static_cast<const T *>(a.B), static_cast<const T *>(a.C), bc, rows, a.N);
-    if (p.segments > 1) {
-        hipLaunchKernelGGL((k_scan<IO, NT, false>), dim3(unsigned((p.segments - 1) * p.tiles)), dim3(kWave), 0, s,
-                           static_cast<const T *>(a.x), static_cast<const T *>(a.delta), a.A, bc, a.Dskip,
-                           static_cast<T *>(a.y), a.final_state, agg_sum, agg_h, a.batch, a.L, a.dim, a.N,
-                           p.seg_len, p.segments, p.tiles_per_batch, p.tiles);
+    const int64_t prep_blocks = (rows * NT + 255) / 256;
+    const int64_t cls_blocks = (p.tiles_per_batch + 3) / 4;
+    hipLaunchKernelGGL((k_prep<IO, NT>), dim3(unsigned(prep_blocks + cls_blocks)), dim3(256), 0, s,
+                       static_cast<const T *>(a.B), static_cast<const T *>(a.C), bc, rows, a.N, a.A,
+                       a.dim, flags, p.tiles_per_batch, prep_blocks);
+    const dim3 seg_agg(unsigned((p.segments - 1) * p.tiles)), seg_main(unsigned(p.segments * p.tiles));
+#define SSCAN_SEG(MAIN, FAST, GRID)                                                                 \
+    hipLaunchKernelGGL((k_seg<IO, NT, MAIN, FAST>), GRID, dim3(kWave), 0, s, x, dl, a.A, bc, a.Dskip, y, \
+                       a.final_state, agg_sum, agg_h, flags, a.batch, a.L, a.dim, a.N, p.seg_len,      \
+                       p.segments, p.tiles_per_batch, p.tiles)
+    // general-A tiles (waves of structured-real tiles exit at once)
+    if (p.segments > 1) SSCAN_SEG(false, false, seg_agg);
+    SSCAN_SEG(true, false, seg_main);
+    // structured-real tiles
+    if (p.lockstep) {
+        hipLaunchKernelGGL((k_lockstep<IO, NT, kLockW, kLockT>), dim3(unsigned(p.tiles)),
+                           dim3(kLockW * kWave), 0, s, x, dl, a.A, bc, a.Dskip, y, a.final_state, flags,
+                           a.L, a.dim, a.N, p.tiles_per_batch);
+    } else {
+        if (p.segments > 1) SSCAN_SEG(false, true, seg_agg);
+        SSCAN_SEG(true, true, seg_main);
     }
-    hipLaunchKernelGGL((k_scan<IO, NT, true>), dim3(unsigned(p.segments * p.tiles)), dim3(kWave), 0, s,
-                       static_cast<const T *>(a.x), static_cast<const T *>(a.delta), a.A, bc, a.Dskip,
-                       static_cast<T *>(a.y), a.final_state, agg_sum, agg_h, a.batch, a.L, a.dim, a.N,
-                       p.seg_len, p.segments, p.tiles_per_batch, p.tiles);
+#undef SSCAN_SEG
     return hipGetLastError();
 }
 
@@ -424,17 +636,26 @@ FwdPlan plan_forward(int64_t batch, int64_t L, int64_t dim, int64_t N) {
     p.nt = round_nt(N);
     p.tiles_per_batch = (dim + kWave - 1) / kWave;
     p.tiles = batch * p.tiles_per_batch;
-    // enough segments for ~2 waves per SIMD (1024 SIMDs), segments of >= 64 tokens
-    const int64_t target_waves = 2048;
+    // Segment kernels: enough segments for ~2 waves per SIMD (1024 SIMDs) with
+    // segments of >= 64 tokens.
+    const int64_t target_waves = kTargetWaves;
     int64_t S = p.tiles > 0 ? (target_waves + p.tiles - 1) / p.tiles : 1;
     S = std::min<int64_t>(S, std::max<int64_t>(1, L / 64));
     S = std::max<int64_t>(1, std::min<int64_t>(S, 4096));
     p.seg_len = L > 0 ? (L + S - 1) / S : 1;
     p.segments = L > 0 ? int((L + p.seg_len - 1) / p.seg_len) : 1;
-    const size_t bc = align256(size_t(batch) * L * 2 * p.nt * sizeof(float));
-    const size_t sums = align256(size_t(p.segments) * batch * dim * sizeof(float));
-    const size_t hs = align256(size_t(p.segments) * batch * dim * p.nt * sizeof(float));
-    p.ws_bytes = bc + sums + hs;
+    // Lockstep kernel when the tiles alone give at least one wave per SIMD.
+    p.lockstep = p.tiles * kLockW >= kLockMinWaves;
+    size_t off = 0;
+    p.off_bc = off;
+    off += align256(size_t(batch) * L * 2 * p.nt * sizeof(float));
+    p.off_flags = off;
+    off += align256(size_t(p.tiles_per_batch) * sizeof(int));
+    p.off_sum = off;
+    off += align256(size_t(p.segments) * batch * dim * sizeof(float));
+    p.off_h = off;
+    off += align256(size_t(p.segments) * batch * dim * p.nt * sizeof(float));
+    p.ws_bytes = off;
     return p;
 }
 

@@ -90,3 +90,10 @@ def test_step_streams():
         np.testing.assert_array_equal(a[k], b[k])
         assert a[k].shape[0] == 4
     assert not np.array_equal(a["x"], c["x"])
+
+
+def test_parameter_arrays_are_contiguous():
+    for name in ("tiny_f32", "mamba130m_f32"):
+        wl = datagen.workload(name)
+        for a in (datagen.gen_A(wl), datagen.gen_Dskip(wl)):
+            assert a.flags["C_CONTIGUOUS"] and torch.from_numpy(a).is_contiguous()

@@ -126,6 +126,13 @@ EDGE = [
     (2, 400, 130, 8, "f32", "loguniform"),
     (1, 20000, 64, 16, "f32", "s4d_real"),   # one tile: ~300 time segments
     (1, 9000, 7, 4, "bf16", "loguniform"),
+    # >= 128 tiles of 64 channels: the lockstep kernel
+    (128, 300, 65, 16, "bf16", "s4d_real"),
+    (160, 517, 64, 5, "f32", "s4d_real"),
+    (130, 1, 64, 16, "f32", "s4d_real"),
+    (64, 2100, 130, 8, "f32", "s4d_real"),
+    (129, 700, 64, 1, "bf16", "s4d_real"),
+    (128, 256, 64, 16, "f32", "s4d_real"),
 ]
 
 
@@ -147,6 +154,18 @@ def test_mixed_A_within_a_wave_takes_the_general_path():
     inp = datagen.scan_inputs(wl)
     rnd = datagen.gen_A(datagen.custom("mixedA", 1, 1, 64, 16, "f32", "loguniform", key=9))
     inp["A"] = np.concatenate([inp["A"][:32], rnd[32:]]).astype(np.float32)
+    _check_full(wl, inp=inp)
+
+
+def test_lockstep_with_some_general_tiles():
+    """128 tiles: tiles 1 and 70 have random A (segment kernels), the rest S4D-real (lockstep)."""
+    wl = datagen.custom("mixedlock", 2, 1000, 4096, 16, "bf16", "s4d_real", key=15)
+    inp = datagen.scan_inputs(wl)
+    rnd = datagen.gen_A(datagen.custom("mixedlockA", 1, 1, 4096, 16, "f32", "loguniform", key=15))
+    A = inp["A"].copy()
+    A[64:128] = rnd[64:128]
+    A[70 * 64 - 4096 + 5] = rnd[70 * 64 - 4096 + 5]
+    inp["A"] = A
     _check_full(wl, inp=inp)
 
 
