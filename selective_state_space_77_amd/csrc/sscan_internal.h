@@ -10,19 +10,24 @@ namespace sscan {
 constexpr int kWave = 64;  // CDNA wavefront width: one lane per channel
 
 // Launch shape of the lockstep kernel: kLockW waves per 64-channel tile, each
-// taking runs of kLockT tokens; used when tiles * kLockW >= kLockMinWaves.
+// taking runs of kLockT tokens.  A tile's workgroup fills one CU, so the kernel
+// is used when there are at least kLockMinTiles tiles (MI355X has 256 CUs);
+// fewer tiles go to the segment kernels, which spread over every CU.
 #ifndef SSCAN_LOCK_W
-#define SSCAN_LOCK_W 8
+#define SSCAN_LOCK_W 16
 #endif
 #ifndef SSCAN_LOCK_T
-#define SSCAN_LOCK_T 32
+#define SSCAN_LOCK_T 16
 #endif
 #ifndef SSCAN_TARGET_WAVES
 #define SSCAN_TARGET_WAVES 2048
 #endif
 constexpr int kLockW = SSCAN_LOCK_W;
 constexpr int kLockT = SSCAN_LOCK_T;
-constexpr int64_t kLockMinWaves = 1024;
+#ifndef SSCAN_LOCK_MIN_TILES
+#define SSCAN_LOCK_MIN_TILES 192
+#endif
+constexpr int64_t kLockMinTiles = SSCAN_LOCK_MIN_TILES;
 constexpr int64_t kTargetWaves = SSCAN_TARGET_WAVES;  // segment kernels: waves to aim for
 
 // Work split of one forward pass.  Segment kernels cut the sequence into

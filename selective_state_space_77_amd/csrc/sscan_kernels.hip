@@ -49,23 +49,53 @@ constexpr float kLog2e = 1.44269504088896340736f;
 
 __device__ __forceinline__ float exp2_hw(float v) { return __builtin_amdgcn_exp2f(v); }
 
+// s_waitcnt lgkmcnt(0) alone (gfx9 encoding: vmcnt and expcnt fields left at
+// their "no wait" maxima).  Scalar loads return out of order, so the only wait
+// for one is lgkmcnt(0); issuing it before the next token's loads makes that
+// wait cover only the loads issued one token earlier.
+__device__ __forceinline__ void wait_scalar_loads() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
     // round to nearest even (the gfx950 conversion instruction)
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
 }
 
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+
+// Raw buffer descriptor over `bytes` bytes from `base` (stride 0).  Accesses at
+// or past `bytes` read 0 and drop stores; the hardware range check is what
+// keeps loads of tokens past the end of the sequence in bounds.
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    const int64_t n = bytes < 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), short(0), int(n), 0x00020000);
+}
+
 struct IoF32 {
     using T = float;
+    static constexpr int kBytes = 4;
     __device__ static float ld(const T *p, int64_t i) { return p[i]; }
     __device__ static float cvt(T v) { return v; }
     __device__ static T enc(float v) { return v; }
+    __device__ static T bld(rsrc_t r, uint32_t voff, uint32_t soff) {
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+    }
+    __device__ static void bst(T v, rsrc_t r, uint32_t voff, uint32_t soff) {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+    }
 };
 
 struct IoBF16 {
     using T = uint16_t;
+    static constexpr int kBytes = 2;
     __device__ static float ld(const T *p, int64_t i) { return __uint_as_float(uint32_t(p[i]) << 16); }
     __device__ static float cvt(T v) { return __uint_as_float(uint32_t(v) << 16); }
     __device__ static T enc(float v) { return f32_to_bf16(v); }
+    __device__ static T bld(rsrc_t r, uint32_t voff, uint32_t soff) {
+        return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+    }
+    __device__ static void bst(T v, rsrc_t r, uint32_t voff, uint32_t soff) {
+        __builtin_amdgcn_raw_buffer_store_b16(v, r, voff, soff, 0);
+    }
 };
 
 // ----------------------------------------------------------------------------
@@ -318,9 +348,10 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
     const int *__restrict__ tile_fast, int64_t L, int64_t dim, int N, int64_t tiles_per_batch) {
     using T = typename IO::T;
     constexpr int U = kUnroll;
-    static_assert(TS % U == 0, "TS must be a multiple of the prefetch group");
+    static_assert(TS % U == 0 && U % 2 == 0, "TS must be a multiple of the prefetch group");
     constexpr int NPW = (NT + W - 1) / W;  // states each wave folds
-    constexpr int64_t CH = int64_t(W) * TS;
+    constexpr int CH = W * TS;             // tokens per chunk
+    constexpr int ES = IO::kBytes;
     __shared__ float s_sum[W][kWave];
     __shared__ float s_k[W][NT][kWave];
     __shared__ float s_pre[W][NT][kWave];  // [0]: chunk carry-out; [j]: state entering run j
@@ -333,26 +364,30 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
     if (!tile_fast[dt]) return;  // whole workgroup
     const int64_t dbase = dt * kWave;
     const bool active = dbase + lane < dim;
-    const int lo = active ? lane : int(dim - 1 - dbase);
-    const int64_t d = dbase + lo;
+    const int64_t d = active ? dbase + lane : dim - 1;
     const float a0 = A[d * N];
     const float alpha = -a0, inv_alpha = 1.f / alpha, a2 = a0 * kLog2e;
     const float dsk = Dskip ? Dskip[d] : 0.f;
-    const T *xrow = x + (b * L) * dim + dbase;
-    const T *drow = delta + (b * L) * dim + dbase;
-    T *yrow = y + (b * L) * dim + dbase;
     const float *bcrow = bc + (b * L) * (2 * NT);
     const int64_t nchunks = (L + CH - 1) / CH;
+    // per-lane byte offset inside a token row; per-token row stride (uniform)
+    const uint32_t voff = uint32_t((dbase + lane) * ES);
+    const uint32_t rowb = uint32_t(dim * ES);
 
-    // token of the j-th element of this wave's stream (its run in every chunk)
-    auto tok = [&](int64_t j) -> int64_t { return (j / TS) * CH + int64_t(w) * TS + (j % TS); };
+    // descriptors over [token t0 of chunk c, end of the sequence) of this batch row
+    auto rsrc_at = [&](const T *base, int64_t t0) {
+        return make_rsrc(base + (b * L + t0) * dim, (L - t0) * dim * ES);
+    };
 
     T xr[U], dr[U];
+    {
+        const int64_t t0 = int64_t(w) * TS;
+        const rsrc_t rx = rsrc_at(x, t0), rd = rsrc_at(delta, t0);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t t = min(tok(u), L - 1);
-        xr[u] = xrow[t * dim + lo];
-        dr[u] = drow[t * dim + lo];
+        for (int u = 0; u < U; ++u) {
+            xr[u] = IO::bld(rx, voff, uint32_t(u) * rowb);
+            dr[u] = IO::bld(rd, voff, uint32_t(u) * rowb);
+        }
     }
     float k[NT];
 #pragma unroll
@@ -361,6 +396,8 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
     for (int64_t c = 0; c < nchunks; ++c) {
         const int64_t t0 = c * CH + int64_t(w) * TS;
         const int nv = int(max<int64_t>(0, min<int64_t>(TS, L - t0)));
+        const rsrc_t rx = rsrc_at(x, t0), rd = rsrc_at(delta, t0), ry = rsrc_at(y, t0);
+        const float *bc0 = bcrow + min(t0, L - 1) * (2 * NT);
         if (w == 0) {
             if (c > 0) {
 #pragma unroll
@@ -372,10 +409,33 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
         }
         float yl[TS], rho[TS];
         float cum = 1.f, dsum = 0.f;
-        float brow[2 * NT];
-        const int64_t tlast = min(t0 + TS, L) - 1;  // last valid token of the run (< t0 if empty)
+        // B/(n+1) and C rows of two consecutive tokens (ping-pong): the scalar
+        // loads of token tau+1 are issued, after waiting for those of tau,
+        // before tau computes, so they have a whole token to arrive.
+        float rowA[2 * NT], rowB[2 * NT];
 #pragma unroll
-        for (int i = 0; i < 2 * NT; ++i) brow[i] = bcrow[min(t0, L - 1) * (2 * NT) + i];
+        for (int i = 0; i < 2 * NT; ++i) rowA[i] = bc0[i];
+        auto token = [&](int tau, float xv, float dv, const float *row) {
+            const float r = exp2_hw(dv * a2);
+            cum *= r;
+            rho[tau] = cum;
+            dsum += dv;
+            float pw = r, yacc = 0.f;
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+                const float e = fmaf(-row[n], xv, k[n]);
+                const float q = pw * e;
+                k[n] = fmaf(row[n], xv, q);
+                yacc = fmaf(row[NT + n], k[n], yacc);
+                pw *= r;
+            }
+            const float yv = fmaf(yacc, inv_alpha, dsk * xv);
+            if (w == 0) {
+                if (active) IO::bst(IO::enc(yv), ry, voff, uint32_t(tau) * rowb);
+            } else {
+                yl[tau] = yv;
+            }
+        };
 #pragma unroll
         for (int g = 0; g < TS / U; ++g) {
             float xv[U], dv[U];
@@ -384,42 +444,34 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
                 xv[u] = IO::cvt(xr[u]);
                 dv[u] = IO::cvt(dr[u]);
             }
+            // prefetch the next group of this wave's stream: the rest of this run,
+            // then the start of its run in the next chunk (out-of-range reads give 0)
+            const uint32_t nxt = (g + 1 < TS / U) ? uint32_t((g + 1) * U) : uint32_t(CH);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int64_t t = min(tok(c * TS + (g + 1) * U + u), L - 1);
-                xr[u] = xrow[t * dim + lo];
-                dr[u] = drow[t * dim + lo];
+                xr[u] = IO::bld(rx, voff, (nxt + u) * rowb);
+                dr[u] = IO::bld(rd, voff, (nxt + u) * rowb);
             }
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
+            for (int u = 0; u < U; u += 2) {
                 const int tau = g * U + u;
                 if (tau < nv) {
-                    const int64_t t = t0 + tau;
-                    float bnext[2 * NT];
-                    const int64_t tn = min(t + 1, tlast);
+                    __builtin_amdgcn_sched_barrier(0);
+                    wait_scalar_loads();
+                    const float *rn = bc0 + min(tau + 1, nv - 1) * (2 * NT);
 #pragma unroll
-                    for (int i = 0; i < 2 * NT; ++i) bnext[i] = bcrow[tn * (2 * NT) + i];
-                    const float r = exp2_hw(dv[u] * a2);
-                    cum *= r;
-                    rho[tau] = cum;
-                    dsum += dv[u];
-                    float pw = r, yacc = 0.f;
+                    for (int i = 0; i < 2 * NT; ++i) rowB[i] = rn[i];
+                    __builtin_amdgcn_sched_barrier(0);
+                    token(tau, xv[u], dv[u], rowA);
+                }
+                if (tau + 1 < nv) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    wait_scalar_loads();
+                    const float *rn = bc0 + min(tau + 2, nv - 1) * (2 * NT);
 #pragma unroll
-                    for (int n = 0; n < NT; ++n) {
-                        const float e = fmaf(-brow[n], xv[u], k[n]);
-                        const float q = pw * e;
-                        k[n] = fmaf(brow[n], xv[u], q);
-                        yacc = fmaf(brow[NT + n], k[n], yacc);
-                        pw *= r;
-                    }
-                    const float yv = fmaf(yacc, inv_alpha, dsk * xv[u]);
-                    if (w == 0) {
-                        if (active) yrow[t * dim + lo] = IO::enc(yv);
-                    } else {
-                        yl[tau] = yv;
-                    }
-#pragma unroll
-                    for (int i = 0; i < 2 * NT; ++i) brow[i] = bnext[i];
+                    for (int i = 0; i < 2 * NT; ++i) rowA[i] = rn[i];
+                    __builtin_amdgcn_sched_barrier(0);
+                    token(tau + 1, xv[u + 1], dv[u + 1], rowB);
                 }
             }
         }
@@ -445,25 +497,36 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
             float kin[NT];
 #pragma unroll
             for (int n = 0; n < NT; ++n) kin[n] = s_pre[w][n][lane];
-            float crow[NT];
+            float cA[NT], cB[NT];
 #pragma unroll
-            for (int n = 0; n < NT; ++n) crow[n] = bcrow[t0 * (2 * NT) + NT + n];
+            for (int n = 0; n < NT; ++n) cA[n] = bc0[NT + n];
+            auto fix = [&](int tau, const float *crow) {
+                const float rr = rho[tau];
+                float acc = crow[NT - 1] * kin[NT - 1];
 #pragma unroll
-            for (int tau = 0; tau < TS; ++tau) {
+                for (int n = NT - 2; n >= 0; --n) acc = fmaf(acc, rr, crow[n] * kin[n]);
+                acc *= rr;
+                if (active) IO::bst(IO::enc(fmaf(acc, inv_alpha, yl[tau])), ry, voff, uint32_t(tau) * rowb);
+            };
+#pragma unroll
+            for (int tau = 0; tau < TS; tau += 2) {
                 if (tau < nv) {
-                    const int64_t t = t0 + tau;
-                    float cnext[NT];
-                    const int64_t tn = min(t + 1, tlast);
+                    __builtin_amdgcn_sched_barrier(0);
+                    wait_scalar_loads();
+                    const float *rn = bc0 + min(tau + 1, nv - 1) * (2 * NT) + NT;
 #pragma unroll
-                    for (int n = 0; n < NT; ++n) cnext[n] = bcrow[tn * (2 * NT) + NT + n];
-                    const float rr = rho[tau];
-                    float acc = crow[NT - 1] * kin[NT - 1];
+                    for (int n = 0; n < NT; ++n) cB[n] = rn[n];
+                    __builtin_amdgcn_sched_barrier(0);
+                    fix(tau, cA);
+                }
+                if (tau + 1 < nv) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    wait_scalar_loads();
+                    const float *rn = bc0 + min(tau + 2, nv - 1) * (2 * NT) + NT;
 #pragma unroll
-                    for (int n = NT - 2; n >= 0; --n) acc = fmaf(acc, rr, crow[n] * kin[n]);
-                    acc *= rr;
-                    if (active) yrow[t * dim + lo] = IO::enc(fmaf(acc, inv_alpha, yl[tau]));
-#pragma unroll
-                    for (int n = 0; n < NT; ++n) crow[n] = cnext[n];
+                    for (int n = 0; n < NT; ++n) cA[n] = rn[n];
+                    __builtin_amdgcn_sched_barrier(0);
+                    fix(tau + 1, cB);
                 }
             }
         }
@@ -645,7 +708,9 @@ FwdPlan plan_forward(int64_t batch, int64_t L, int64_t dim, int64_t N) {
     p.seg_len = L > 0 ? (L + S - 1) / S : 1;
     p.segments = L > 0 ? int((L + p.seg_len - 1) / p.seg_len) : 1;
     // Lockstep kernel when the tiles alone give at least one wave per SIMD.
-    p.lockstep = p.tiles * kLockW >= kLockMinWaves;
+    // (its buffer offsets reach (W*TS + 8) rows past a run start: keep them 32-bit)
+    p.lockstep = p.tiles >= kLockMinTiles &&
+                 (int64_t(kLockW) * kLockT + kUnroll) * dim * 4 < (int64_t(1) << 31);
     size_t off = 0;
     p.off_bc = off;
     off += align256(size_t(batch) * L * 2 * p.nt * sizeof(float));

@@ -126,13 +126,18 @@ EDGE = [
     (2, 400, 130, 8, "f32", "loguniform"),
     (1, 20000, 64, 16, "f32", "s4d_real"),   # one tile: ~300 time segments
     (1, 9000, 7, 4, "bf16", "loguniform"),
-    # >= 128 tiles of 64 channels: the lockstep kernel
+    # >= 192 tiles of 64 channels: the lockstep kernel (ragged dim, N < 16, L = 1,
+    # partial last chunk, exactly one chunk)
     (128, 300, 65, 16, "bf16", "s4d_real"),
-    (160, 517, 64, 5, "f32", "s4d_real"),
-    (130, 1, 64, 16, "f32", "s4d_real"),
+    (200, 517, 64, 5, "f32", "s4d_real"),
+    (200, 1, 64, 16, "f32", "s4d_real"),
     (64, 2100, 130, 8, "f32", "s4d_real"),
+    (193, 700, 64, 1, "bf16", "s4d_real"),
+    (256, 256, 64, 16, "f32", "s4d_real"),
+    (192, 1000, 64, 2, "bf16", "s4d_real"),
+    # 64..191 tiles: segment kernels
+    (160, 517, 64, 5, "f32", "s4d_real"),
     (129, 700, 64, 1, "bf16", "s4d_real"),
-    (128, 256, 64, 16, "f32", "s4d_real"),
 ]
 
 
@@ -158,8 +163,9 @@ def test_mixed_A_within_a_wave_takes_the_general_path():
 
 
 def test_lockstep_with_some_general_tiles():
-    """128 tiles: tiles 1 and 70 have random A (segment kernels), the rest S4D-real (lockstep)."""
-    wl = datagen.custom("mixedlock", 2, 1000, 4096, 16, "bf16", "s4d_real", key=15)
+    """256 tiles: d-tile 1 and one channel of d-tile 6 have random A (segment kernels), the rest
+    are S4D-real (lockstep kernel)."""
+    wl = datagen.custom("mixedlock", 4, 1000, 4096, 16, "bf16", "s4d_real", key=15)
     inp = datagen.scan_inputs(wl)
     rnd = datagen.gen_A(datagen.custom("mixedlockA", 1, 1, 4096, 16, "f32", "loguniform", key=15))
     A = inp["A"].copy()
