@@ -409,6 +409,12 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
         }
         float yl[TS], rho[TS];
         float cum = 1.f, dsum = 0.f;
+        // The run is processed branch-free even when it is ragged: tokens past
+        // the end of the sequence read x = delta = 0 through the descriptor's
+        // range check, which leaves the state exactly unchanged (r = 1, w = 0),
+        // and their stores fall outside the range and are dropped.  Only the
+        // B/C row index is clamped.
+        const int last = max(nv - 1, 0);
         // B/(n+1) and C rows of two consecutive tokens (ping-pong): the scalar
         // loads of token tau+1 are issued, after waiting for those of tau,
         // before tau computes, so they have a whole token to arrive.
@@ -429,12 +435,7 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
                 yacc = fmaf(row[NT + n], k[n], yacc);
                 pw *= r;
             }
-            const float yv = fmaf(yacc, inv_alpha, dsk * xv);
-            if (w == 0) {
-                if (active) IO::bst(IO::enc(yv), ry, voff, uint32_t(tau) * rowb);
-            } else {
-                yl[tau] = yv;
-            }
+            yl[tau] = fmaf(yacc, inv_alpha, dsk * xv);
         };
 #pragma unroll
         for (int g = 0; g < TS / U; ++g) {
@@ -445,7 +446,7 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
                 dv[u] = IO::cvt(dr[u]);
             }
             // prefetch the next group of this wave's stream: the rest of this run,
-            // then the start of its run in the next chunk (out-of-range reads give 0)
+            // then the start of its run in the next chunk
             const uint32_t nxt = (g + 1 < TS / U) ? uint32_t((g + 1) * U) : uint32_t(CH);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -455,25 +456,30 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
 #pragma unroll
             for (int u = 0; u < U; u += 2) {
                 const int tau = g * U + u;
-                if (tau < nv) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    wait_scalar_loads();
-                    const float *rn = bc0 + min(tau + 1, nv - 1) * (2 * NT);
+                __builtin_amdgcn_sched_barrier(0);
+                wait_scalar_loads();
+                {
+                    const float *rn = bc0 + min(tau + 1, last) * (2 * NT);
 #pragma unroll
                     for (int i = 0; i < 2 * NT; ++i) rowB[i] = rn[i];
-                    __builtin_amdgcn_sched_barrier(0);
-                    token(tau, xv[u], dv[u], rowA);
                 }
-                if (tau + 1 < nv) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    wait_scalar_loads();
-                    const float *rn = bc0 + min(tau + 2, nv - 1) * (2 * NT);
+                __builtin_amdgcn_sched_barrier(0);
+                token(tau, xv[u], dv[u], rowA);
+                __builtin_amdgcn_sched_barrier(0);
+                wait_scalar_loads();
+                {
+                    const float *rn = bc0 + min(tau + 2, last) * (2 * NT);
 #pragma unroll
                     for (int i = 0; i < 2 * NT; ++i) rowA[i] = rn[i];
-                    __builtin_amdgcn_sched_barrier(0);
-                    token(tau + 1, xv[u + 1], dv[u + 1], rowB);
                 }
+                __builtin_amdgcn_sched_barrier(0);
+                token(tau + 1, xv[u + 1], dv[u + 1], rowB);
             }
+        }
+        if (w == 0 && active) {
+            // run 0 started from the carried state: its outputs are final
+#pragma unroll
+            for (int tau = 0; tau < TS; ++tau) IO::bst(IO::enc(yl[tau]), ry, voff, uint32_t(tau) * rowb);
         }
         s_sum[w][lane] = dsum;
 #pragma unroll
@@ -510,24 +516,24 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
             };
 #pragma unroll
             for (int tau = 0; tau < TS; tau += 2) {
-                if (tau < nv) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    wait_scalar_loads();
-                    const float *rn = bc0 + min(tau + 1, nv - 1) * (2 * NT) + NT;
+                __builtin_amdgcn_sched_barrier(0);
+                wait_scalar_loads();
+                {
+                    const float *rn = bc0 + min(tau + 1, last) * (2 * NT) + NT;
 #pragma unroll
                     for (int n = 0; n < NT; ++n) cB[n] = rn[n];
-                    __builtin_amdgcn_sched_barrier(0);
-                    fix(tau, cA);
                 }
-                if (tau + 1 < nv) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    wait_scalar_loads();
-                    const float *rn = bc0 + min(tau + 2, nv - 1) * (2 * NT) + NT;
+                __builtin_amdgcn_sched_barrier(0);
+                fix(tau, cA);
+                __builtin_amdgcn_sched_barrier(0);
+                wait_scalar_loads();
+                {
+                    const float *rn = bc0 + min(tau + 2, last) * (2 * NT) + NT;
 #pragma unroll
                     for (int n = 0; n < NT; ++n) cA[n] = rn[n];
-                    __builtin_amdgcn_sched_barrier(0);
-                    fix(tau + 1, cB);
                 }
+                __builtin_amdgcn_sched_barrier(0);
+                fix(tau + 1, cB);
             }
         }
     }
