@@ -16,27 +16,25 @@
 //     (fp32) row per load instruction -- fully coalesced without LDS staging;
 //   * B[b,t,:] and C[b,t,:] are wave-uniform, so they come in through scalar
 //     loads into SGPRs and feed the VALU as scalar operands (no per-lane
-//     traffic, no LDS, no cross-lane exchange).
-// Time is split into segments so that the chip has >= 2 waves per SIMD:
-//   pass 1 (k_scan<.., false>): each wave scans its segment from a zero state
-//           and stores the segment aggregate (sum of delta, local final state);
-//   pass 2 (k_scan<.., true>):  each wave composes the aggregates of all
-//           earlier segments with the associative combine
-//           (a1,b1) o (a2,b2) = (a1*a2, a2*b1 + b2)  ("Mamba and State Space
-//           Models", the parallel scan), starting its own segment from the
-//           true carried state, and scans it again with the readout.
-// The decay of a whole segment needs no per-token product: the Abar of a
-// diagonal mode multiply to exp(A * sum(delta)).
+//     traffic, no cross-lane exchange).
+// Time is split so the chip has enough waves, and the pieces are composed with
+// the associative combine (a1,b1) o (a2,b2) = (a1*a2, a2*b1 + b2) ("Mamba and
+// State Space Models", the parallel scan).  The decay of a run of tokens needs
+// no per-token product: the Abar of a diagonal mode multiply to exp(A*sum(delta)).
+//   k_lockstep: one workgroup of W waves per 64-channel tile; runs of a chunk
+//               are scanned locally, composed through LDS, and corrected.
+//   k_seg:      one wave per (tile, time segment); an aggregate pass and a
+//               main pass that folds the aggregates of earlier segments.
 //
-// S4D-real fast path.  When every A row of a wave is A[d,n] = (n+1)*A[d,0]
-// with A[d,0] < 0 (the structured-real initialisation), Abar_n = r^(n+1) with
+// Structured-real fast path.  When every A row of a tile is
+// A[d,n] = (n+1)*A[d,0] with A[d,0] < 0, Abar_n = r^(n+1) with
 // r = exp(delta*A[d,0]): one exp per (t,d) instead of N.  The state is kept
 // scaled, k_n = -A[d,0]*h_n, which turns the ZOH update into
 //     k_n <- w_n + Abar_n*(k_n - w_n),   w_n = (B[t,n]/(n+1)) * x
 // (two FMAs and one multiply; it never forms 1 - Abar) and the readout into
 // y = (sum_n C_n k_n) / (-A[d,0]) + Dskip*x.  B/(n+1) is staged once per
-// token by k_prep_bc.  Any other A takes the general path (exp and expm1 per
-// state), decided per wave from the data.
+// token by k_prep, which also classifies each tile; any other A takes the
+// general path (exp2 and the ZOH gain per state).
 
 #include <math.h>
 
@@ -54,6 +52,26 @@ __device__ __forceinline__ float exp2_hw(float v) { return __builtin_amdgcn_exp2
 // for one is lgkmcnt(0); issuing it before the next token's loads makes that
 // wait cover only the loads issued one token earlier.
 __device__ __forceinline__ void wait_scalar_loads() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// ZOH input gain g = (exp(z) - 1)/A with z = dt*A (dt when A == 0), given
+// abar = exp(z).  For |z| < 1/4 it uses dt * expm1(z)/z as the Taylor
+// polynomial 1 + z/2 + ... + z^6/7! (truncation below 2e-9 relative), which
+// avoids the cancellation in abar - 1 and needs no division; otherwise
+// (abar - 1)/A has no cancellation.
+__device__ __forceinline__ float zoh_gain(float dt, float a, float z, float abar) {
+    if (fabsf(z) < 0.25f) {
+        float p = 1.f / 5040.f;
+        p = fmaf(p, z, 1.f / 720.f);
+        p = fmaf(p, z, 1.f / 120.f);
+        p = fmaf(p, z, 1.f / 24.f);
+        p = fmaf(p, z, 1.f / 6.f);
+        p = fmaf(p, z, 0.5f);
+        p = fmaf(p, z, 1.f);
+        return dt * p;
+    }
+    return (abar - 1.f) / a;
+}
+
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
     // round to nearest even (the gfx950 conversion instruction)
@@ -295,8 +313,7 @@ __global__ __launch_bounds__(kWave) void k_seg(
                     for (int n = 0; n < NT; ++n) {
                         const float an = a[n];
                         const float abar = exp2_hw(dtv * (an * kLog2e));
-                        // (exp(dt*A) - 1)/A without cancellation; dt when A == 0
-                        const float g = (an != 0.f) ? expm1f(dtv * an) / an : dtv;
+                        const float g = zoh_gain(dtv, an, dtv * an, abar);
                         const float bn = row[n] * float(n + 1);
                         h[n] = fmaf(abar, h[n], g * (bn * xv[u]));
                         if (kMain) yacc = fmaf(row[NT + n], h[n], yacc);
@@ -550,7 +567,7 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
 // Decode step: LPC lanes share one channel, each owning SPL consecutive states
 // (16 B for N = 16), so a wave reads and writes one contiguous 1 KB span of
 // the (batch, dim, N) state.  The partial readouts are summed across the LPC
-// lanes.  Memory bound: exact expf/expm1f per state.
+// lanes.  Memory bound; per state one hardware exp2 and the gain above.
 template <class IO, int NT, bool kVec>
 __global__ __launch_bounds__(256) void k_step(float *__restrict__ state,
                                               const typename IO::T *__restrict__ x,
@@ -574,27 +591,38 @@ __global__ __launch_bounds__(256) void k_step(float *__restrict__ state,
     const float xv = IO::ld(x, c);
     const float dt = IO::ld(delta, c);
 
-    float h[SPL];
+    float h[SPL], av[SPL], bv[SPL], cv[SPL];
     float *sp = state + c * N + q * SPL;
     if constexpr (kVec) {
+        // N == NT (a multiple of 4) and 16-byte aligned state: vector accesses
         const float4 v = *reinterpret_cast<const float4 *>(sp);
         h[0] = v.x; h[1] = v.y; h[2] = v.z; h[3] = v.w;
+        const float4 va = *reinterpret_cast<const float4 *>(A + d * N + q * SPL);
+        av[0] = va.x; av[1] = va.y; av[2] = va.z; av[3] = va.w;
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) {
+            bv[j] = IO::ld(B, b * N + q * SPL + j);
+            cv[j] = IO::ld(C, b * N + q * SPL + j);
+        }
     } else {
 #pragma unroll
-        for (int j = 0; j < SPL; ++j) h[j] = (q * SPL + j < N) ? sp[j] : 0.f;
+        for (int j = 0; j < SPL; ++j) {
+            const int n = q * SPL + j;
+            const bool ok = n < N;
+            h[j] = ok ? sp[j] : 0.f;
+            av[j] = ok ? A[d * N + n] : 0.f;
+            bv[j] = ok ? IO::ld(B, b * N + n) : 0.f;
+            cv[j] = ok ? IO::ld(C, b * N + n) : 0.f;
+        }
     }
     float yacc = 0.f;
 #pragma unroll
     for (int j = 0; j < SPL; ++j) {
-        const int n = q * SPL + j;
-        if (n < N) {
-            const float an = A[d * N + n];
-            const float z = dt * an;
-            const float abar = expf(z);
-            const float g = (an != 0.f) ? expm1f(z) / an : dt;
-            h[j] = fmaf(abar, h[j], g * (IO::ld(B, b * N + n) * xv));
-            yacc = fmaf(IO::ld(C, b * N + n), h[j], yacc);
-        }
+        const float z = dt * av[j];
+        const float abar = exp2_hw(dt * (av[j] * kLog2e));
+        const float g = zoh_gain(dt, av[j], z, abar);
+        h[j] = fmaf(abar, h[j], g * (bv[j] * xv));
+        yacc = fmaf(cv[j], h[j], yacc);
     }
 #pragma unroll
     for (int off = LPC / 2; off >= 1; off /= 2) yacc += __shfl_xor(yacc, off, LPC);
@@ -671,7 +699,8 @@ hipError_t step_t(const StepArgs &a, hipStream_t s) {
     constexpr int LPC = NT / SPL;
     const int64_t threads = a.batch * a.dim * LPC;
     const dim3 grid(unsigned((threads + 255) / 256));
-    const bool vec = (SPL == 4) && (a.N == NT) && (reinterpret_cast<uintptr_t>(a.state) % 16 == 0);
+    const bool vec = (SPL == 4) && (a.N == NT) && (reinterpret_cast<uintptr_t>(a.state) % 16 == 0) &&
+                     (reinterpret_cast<uintptr_t>(a.A) % 16 == 0);
     if (vec) {
         if constexpr (SPL == 4)
             hipLaunchKernelGGL((k_step<IO, NT, true>), grid, dim3(256), 0, s, a.state,
