@@ -83,6 +83,25 @@ int sscan_forward(const void *x, const void *delta, const float *A, const void *
                   int64_t dim, int64_t dstate, int io_dtype, void *stream);
 
 /*
+ * Whole-sequence forward pass that starts from a given state instead of zero:
+ * resuming a sequence from a snapshot, or prefilling it in pieces ("Mamba and
+ * State Space Models", failure mode 2: an SSM resumes a shared prefix by
+ * snapshotting and restoring its state).  Running [0, L1) with sscan_forward and
+ * then [L1, L) with this call from the first call's final_state gives the same
+ * result as one call over [0, L), up to rounding.
+ *
+ *   initial_state [in] (batch, dim, dstate) fp32 state h before the first token, or
+ *                      NULL for zero (then identical to sscan_forward).  It may not
+ *                      overlap final_state or any other argument (use two buffers).
+ *   All other arguments as for sscan_forward.  With seqlen == 0 final_state
+ *   receives a copy of initial_state.
+ */
+int sscan_forward_from_state(const void *x, const void *delta, const float *A, const void *B,
+                             const void *C, const float *Dskip, const float *initial_state,
+                             void *y, float *final_state, int64_t batch, int64_t seqlen,
+                             int64_t dim, int64_t dstate, int io_dtype, void *stream);
+
+/*
  * One recurrent decode step (generation: constant work and memory per token;
  * "The loop that beats attention", section "Going back to the baton";
  * "State space models and Mamba", cost table, generation per token O(1)).

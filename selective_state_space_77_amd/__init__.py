@@ -5,7 +5,8 @@ kernels.  PyTorch supplies device memory and the stream.  There is no CPU or
 PyTorch fallback: if libsscan.so is missing or fails to load, importing this
 package raises.
 
-    forward(x, delta, A, B, C, Dskip=None, y=None, final_state=None, stream=None)
+    forward(x, delta, A, B, C, Dskip=None, y=None, final_state=None, stream=None,
+            initial_state=None)
     step(state, x_t, delta_t, A, B_t, C_t, Dskip=None, y_t=None, stream=None)
 
 Shapes and layouts follow include/sscan.h: x, delta, y (batch, L, dim); B, C
@@ -43,6 +44,9 @@ def _load() -> ctypes.CDLL:
     vp, fp, i64 = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64
     lib.sscan_forward.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i64, i64, i64, i64, ctypes.c_int, vp]
     lib.sscan_forward.restype = ctypes.c_int
+    lib.sscan_forward_from_state.argtypes = [vp, vp, fp, vp, vp, fp, fp, vp, fp, i64, i64, i64, i64,
+                                             ctypes.c_int, vp]
+    lib.sscan_forward_from_state.restype = ctypes.c_int
     lib.sscan_step.argtypes = [fp, vp, vp, fp, vp, vp, fp, vp, i64, i64, i64, ctypes.c_int, vp]
     lib.sscan_step.restype = ctypes.c_int
     lib.sscan_status_string.argtypes = [ctypes.c_int]
@@ -91,8 +95,11 @@ def _stream(stream, device) -> int:
     return s.cuda_stream if isinstance(s, torch.cuda.Stream) else int(s)
 
 
-def forward(x, delta, A, B, C, Dskip=None, y=None, final_state=None, stream=None):
-    """Whole-sequence selective scan; returns y (written into `y` when given)."""
+def forward(x, delta, A, B, C, Dskip=None, y=None, final_state=None, stream=None,
+            initial_state=None):
+    """Whole-sequence selective scan; returns y (written into `y` when given).
+
+    initial_state: (batch, dim, N) fp32 state before the first token (default zero)."""
     batch, L, dim = x.shape
     N = A.shape[1]
     if delta.shape != x.shape or tuple(A.shape) != (dim, N) or B.shape != (batch, L, N) or C.shape != B.shape:
@@ -104,10 +111,13 @@ def forward(x, delta, A, B, C, Dskip=None, y=None, final_state=None, stream=None
         raise ValueError("Dskip must have shape (dim,)")
     if final_state is not None and tuple(final_state.shape) != (batch, dim, N):
         raise ValueError("final_state must have shape (batch, dim, N)")
-    rc = lib.sscan_forward(_dev(x, "x"), _dev(delta, "delta"), _dev(A, "A", torch.float32),
-                           _dev(B, "B"), _dev(C, "C"), _dev(Dskip, "Dskip", torch.float32),
-                           _dev(y, "y"), _dev(final_state, "final_state", torch.float32),
-                           batch, L, dim, N, io, _stream(stream, x.device))
+    if initial_state is not None and tuple(initial_state.shape) != (batch, dim, N):
+        raise ValueError("initial_state must have shape (batch, dim, N)")
+    rc = lib.sscan_forward_from_state(_dev(x, "x"), _dev(delta, "delta"), _dev(A, "A", torch.float32),
+                                      _dev(B, "B"), _dev(C, "C"), _dev(Dskip, "Dskip", torch.float32),
+                                      _dev(initial_state, "initial_state", torch.float32),
+                                      _dev(y, "y"), _dev(final_state, "final_state", torch.float32),
+                                      batch, L, dim, N, io, _stream(stream, x.device))
     _check(rc)
     return y
 

@@ -11,8 +11,8 @@ namespace {
 
 thread_local char g_last_error[512];
 
-int fail(int status, const char *fmt, const char *detail = nullptr) {
-    snprintf(g_last_error, sizeof g_last_error, fmt, detail ? detail : "");
+int fail(int status, const char *fmt, const char *a = "", const char *b = "") {
+    snprintf(g_last_error, sizeof g_last_error, fmt, a, b);
     return status;
 }
 
@@ -50,10 +50,10 @@ int check_alias(const Span *outs, int nout, const Span *ins, int nin) {
     for (int i = 0; i < nout; ++i) {
         for (int j = 0; j < nin; ++j)
             if (overlap(outs[i], ins[j]))
-                return fail(SSCAN_ERR_ALIAS, "output overlaps an input (%s)", outs[i].name);
+                return fail(SSCAN_ERR_ALIAS, "output %s overlaps input %s", outs[i].name, ins[j].name);
         for (int j = i + 1; j < nout; ++j)
             if (overlap(outs[i], outs[j]))
-                return fail(SSCAN_ERR_ALIAS, "outputs overlap (%s)", outs[i].name);
+                return fail(SSCAN_ERR_ALIAS, "outputs %s and %s overlap", outs[i].name, outs[j].name);
     }
     return SSCAN_OK;
 }
@@ -84,9 +84,10 @@ const char *sscan_status_string(int status) {
     }
 }
 
-int sscan_forward(const void *x, const void *delta, const float *A, const void *B, const void *C,
-                  const float *Dskip, void *y, float *final_state, int64_t batch, int64_t seqlen,
-                  int64_t dim, int64_t dstate, int io_dtype, void *stream) {
+static int forward_impl(const void *x, const void *delta, const float *A, const void *B,
+                        const void *C, const float *Dskip, const float *initial_state, void *y,
+                        float *final_state, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                        int io_dtype, void *stream) {
     g_last_error[0] = '\0';
     if (io_dtype != SSCAN_F32 && io_dtype != SSCAN_BF16)
         return fail(SSCAN_ERR_UNSUPPORTED, "io_dtype must be SSCAN_F32 or SSCAN_BF16");
@@ -99,33 +100,49 @@ int sscan_forward(const void *x, const void *delta, const float *A, const void *
         !nbytes(&ws_guard, 2 * 16 * 4, batch, seqlen))
         return fail(SSCAN_ERR_SHAPE, "negative size or byte size overflows int64");
     const Span ins[] = {{x, bx, "x"}, {delta, bx, "delta"}, {A, ba, "A"}, {B, bbc, "B"},
-                        {C, bbc, "C"}, {Dskip, Dskip ? bd : 0, "Dskip"}};
+                        {C, bbc, "C"}, {Dskip, Dskip ? bd : 0, "Dskip"},
+                        {initial_state, initial_state ? bs : 0, "initial_state"}};
     const Span outs[] = {{y, bx, "y"}, {final_state, final_state ? bs : 0, "final_state"}};
     const Span req[] = {ins[0], ins[1], ins[2], ins[3], ins[4], outs[0]};
     int rc = check_ptrs(req, 6);
     if (rc) return rc;
-    rc = check_alias(outs, 2, ins, 6);
+    rc = check_alias(outs, 2, ins, 7);
     if (rc) return rc;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (batch == 0 || dim == 0) return SSCAN_OK;
     if (seqlen == 0) {
         if (!final_state) return SSCAN_OK;
-        hipError_t e = sscan::launch_zero(final_state, batch * dim * dstate, s);
-        return e == hipSuccess ? SSCAN_OK : fail_hip("zero-fill launch", e);
+        hipError_t e = sscan::launch_copy_or_zero(final_state, initial_state, batch * dim * dstate, s);
+        return e == hipSuccess ? SSCAN_OK : fail_hip("state copy launch", e);
     }
 
     const sscan::FwdPlan plan = sscan::plan_forward(batch, seqlen, dim, dstate);
     void *ws = nullptr;
     hipError_t e = hipMallocAsync(&ws, plan.ws_bytes, s);
     if (e != hipSuccess) return fail_hip("hipMallocAsync (scratch)", e);
-    sscan::FwdArgs a{x, delta, A, B, C, Dskip, y, final_state, batch, seqlen, dim, int(dstate),
-                     io_dtype};
+    sscan::FwdArgs a{x, delta, A, B, C, Dskip, initial_state, y, final_state, batch, seqlen, dim,
+                     int(dstate), io_dtype};
     e = sscan::launch_forward(a, plan, ws, s);
     const hipError_t ef = hipFreeAsync(ws, s);
     if (e != hipSuccess) return fail_hip("forward launch", e);
     if (ef != hipSuccess) return fail_hip("hipFreeAsync (scratch)", ef);
     return SSCAN_OK;
+}
+
+int sscan_forward(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                  const float *Dskip, void *y, float *final_state, int64_t batch, int64_t seqlen,
+                  int64_t dim, int64_t dstate, int io_dtype, void *stream) {
+    return forward_impl(x, delta, A, B, C, Dskip, nullptr, y, final_state, batch, seqlen, dim, dstate,
+                        io_dtype, stream);
+}
+
+int sscan_forward_from_state(const void *x, const void *delta, const float *A, const void *B,
+                             const void *C, const float *Dskip, const float *initial_state, void *y,
+                             float *final_state, int64_t batch, int64_t seqlen, int64_t dim,
+                             int64_t dstate, int io_dtype, void *stream) {
+    return forward_impl(x, delta, A, B, C, Dskip, initial_state, y, final_state, batch, seqlen, dim,
+                        dstate, io_dtype, stream);
 }
 
 int sscan_step(float *state, const void *x_t, const void *delta_t, const float *A,

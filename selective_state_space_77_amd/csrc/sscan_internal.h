@@ -52,6 +52,7 @@ struct FwdArgs {
     const float *A;
     const void *B, *C;
     const float *Dskip;
+    const float *h0;  // state before token 0, (batch, dim, N); NULL = zero
     void *y;
     float *final_state;
     int64_t batch, L, dim;
@@ -62,8 +63,8 @@ struct FwdArgs {
 // Enqueue the forward pass; `ws` points at plan.ws_bytes of device scratch.
 hipError_t launch_forward(const FwdArgs &a, const FwdPlan &plan, void *ws, hipStream_t s);
 
-// Enqueue a fill of `count` floats with zero (used for final_state at seqlen 0).
-hipError_t launch_zero(float *p, int64_t count, hipStream_t s);
+// Enqueue dst[i] = src ? src[i] : 0 for `count` floats (final_state at seqlen 0).
+hipError_t launch_copy_or_zero(float *dst, const float *src, int64_t count, hipStream_t s);
 
 struct StepArgs {
     float *state;

@@ -157,9 +157,10 @@ __global__ __launch_bounds__(256) void k_prep(const typename IO::T *__restrict__
     if (lane == 0) tile_fast[dt] = all_ok ? 1 : 0;
 }
 
-__global__ __launch_bounds__(256) void k_zero(float *__restrict__ p, int64_t count) {
+__global__ __launch_bounds__(256) void k_copy_or_zero(float *__restrict__ dst,
+                                                      const float *__restrict__ src, int64_t count) {
     const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (i < count) p[i] = 0.f;
+    if (i < count) dst[i] = src ? src[i] : 0.f;
 }
 
 // ----------------------------------------------------------------------------
@@ -173,7 +174,7 @@ template <class IO, int NT, bool kMain, bool kFast>
 __global__ __launch_bounds__(kWave) void k_seg(
     const typename IO::T *__restrict__ x, const typename IO::T *__restrict__ delta,
     const float *__restrict__ A, const float *__restrict__ bc, const float *__restrict__ Dskip,
-    typename IO::T *__restrict__ y, float *__restrict__ final_state,
+    const float *__restrict__ h0, typename IO::T *__restrict__ y, float *__restrict__ final_state,
     float *__restrict__ agg_sum, float *__restrict__ agg_h, const int *__restrict__ tile_fast,
     int64_t batch, int64_t L, int64_t dim, int N, int64_t seg_len, int segments,
     int64_t tiles_per_batch, int64_t tiles) {
@@ -196,11 +197,12 @@ __global__ __launch_bounds__(kWave) void k_seg(
 #pragma unroll
     for (int n = 0; n < NT; ++n) a[n] = (n < N) ? A[d * N + n] : 0.f;
 
-    // ---- carried state at the segment start (pass 2 only): fold the aggregates
-    // of all earlier segments with (a1,b1) o (a2,b2) = (a1*a2, a2*b1 + b2)
+    // ---- carried state at the segment start (pass 2 only): the state before
+    // token 0, then the aggregates of all earlier segments folded in with
+    // (a1,b1) o (a2,b2) = (a1*a2, a2*b1 + b2)
     float h[NT];
 #pragma unroll
-    for (int n = 0; n < NT; ++n) h[n] = 0.f;
+    for (int n = 0; n < NT; ++n) h[n] = (kMain && h0 && n < N) ? h0[(b * dim + d) * N + n] : 0.f;
     if (kMain) {
         for (int j = 0; j < seg; ++j) {
             const int64_t cj = int64_t(j) * batch + b;
@@ -361,7 +363,7 @@ template <class IO, int NT, int W, int TS>
 __global__ __launch_bounds__(W *kWave) void k_lockstep(
     const typename IO::T *__restrict__ x, const typename IO::T *__restrict__ delta,
     const float *__restrict__ A, const float *__restrict__ bc, const float *__restrict__ Dskip,
-    typename IO::T *__restrict__ y, float *__restrict__ final_state,
+    const float *__restrict__ h0, typename IO::T *__restrict__ y, float *__restrict__ final_state,
     const int *__restrict__ tile_fast, int64_t L, int64_t dim, int N, int64_t tiles_per_batch) {
     using T = typename IO::T;
     constexpr int U = kUnroll;
@@ -406,9 +408,9 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
             dr[u] = IO::bld(rd, voff, uint32_t(u) * rowb);
         }
     }
-    float k[NT];
+    float k[NT];  // wave 0 enters chunk 0 with the state before token 0 (scaled)
 #pragma unroll
-    for (int n = 0; n < NT; ++n) k[n] = 0.f;
+    for (int n = 0; n < NT; ++n) k[n] = (w == 0 && h0 && n < N) ? h0[(b * dim + d) * N + n] * alpha : 0.f;
 
     for (int64_t c = 0; c < nchunks; ++c) {
         const int64_t t0 = c * CH + int64_t(w) * TS;
@@ -662,8 +664,9 @@ hipError_t forward_t(const FwdArgs &a, const FwdPlan &p, void *ws, hipStream_t s
                        a.dim, flags, p.tiles_per_batch, prep_blocks);
     const dim3 seg_agg(unsigned((p.segments - 1) * p.tiles)), seg_main(unsigned(p.segments * p.tiles));
 #define SSCAN_SEG(MAIN, FAST, GRID)                                                                 \
-    hipLaunchKernelGGL((k_seg<IO, NT, MAIN, FAST>), GRID, dim3(kWave), 0, s, x, dl, a.A, bc, a.Dskip, y, \
-                       a.final_state, agg_sum, agg_h, flags, a.batch, a.L, a.dim, a.N, p.seg_len,      \
+    hipLaunchKernelGGL((k_seg<IO, NT, MAIN, FAST>), GRID, dim3(kWave), 0, s, x, dl, a.A, bc, a.Dskip,  \
+                       a.h0, y, a.final_state, agg_sum, agg_h, flags, a.batch, a.L, a.dim, a.N,        \
+                       p.seg_len,                                                                     \
                        p.segments, p.tiles_per_batch, p.tiles)
     // general-A tiles (waves of structured-real tiles exit at once)
     if (p.segments > 1) SSCAN_SEG(false, false, seg_agg);
@@ -671,7 +674,8 @@ hipError_t forward_t(const FwdArgs &a, const FwdPlan &p, void *ws, hipStream_t s
     // structured-real tiles
     if (p.lockstep) {
         hipLaunchKernelGGL((k_lockstep<IO, NT, kLockW, kLockT>), dim3(unsigned(p.tiles)),
-                           dim3(kLockW * kWave), 0, s, x, dl, a.A, bc, a.Dskip, y, a.final_state, flags,
+                           dim3(kLockW * kWave), 0, s, x, dl, a.A, bc, a.Dskip, a.h0, y, a.final_state,
+                           flags,
                            a.L, a.dim, a.N, p.tiles_per_batch);
     } else {
         if (p.segments > 1) SSCAN_SEG(false, true, seg_agg);
@@ -763,9 +767,10 @@ hipError_t launch_forward(const FwdArgs &a, const FwdPlan &p, void *ws, hipStrea
     return a.io == 1 ? forward_io<IoBF16>(a, p, ws, s) : forward_io<IoF32>(a, p, ws, s);
 }
 
-hipError_t launch_zero(float *ptr, int64_t count, hipStream_t s) {
+hipError_t launch_copy_or_zero(float *dst, const float *src, int64_t count, hipStream_t s) {
     if (count <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_zero, dim3(unsigned((count + 255) / 256)), dim3(256), 0, s, ptr, count);
+    hipLaunchKernelGGL(k_copy_or_zero, dim3(unsigned((count + 255) / 256)), dim3(256), 0, s, dst, src,
+                       count);
     return hipGetLastError();
 }
 

@@ -27,7 +27,8 @@ def _declared():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared() == ["sscan_forward", "sscan_last_error", "sscan_status_string", "sscan_step",
+    assert _declared() == ["sscan_forward", "sscan_forward_from_state", "sscan_last_error",
+                           "sscan_status_string", "sscan_step",
                            "sscan_version"]
 
 
@@ -77,6 +78,20 @@ def test_empty_inputs_need_no_pointers_and_launch_nothing(lib):
     assert _fwd(lib, x=None, delta=None, B=None, C=None, y=None, batch=0) == 0
     assert _fwd(lib, x=None, delta=None, y=None, dim=0, A=None) == 0
     assert _fwd(lib, x=None, delta=None, y=None, dim=0, A=None, B=None) == -1  # B still non-empty
+
+
+def test_initial_state_validation(lib):
+    f = lib.sscan_forward_from_state
+    args = lambda h0, hs, **kw: (kw.get("x", 0x1000), 0x2000, 0x3000, 0x4000, 0x5000, None, h0, 0x6000,
+                                 hs, 1, 4, 2, 3, 0, None)
+    assert f(*args(0x20000, 0x20000)) == -4          # initial_state == final_state
+    assert f(*args(0x20004, 0x20000)) == -4          # initial_state overlaps final_state
+    assert f(*args(0x6004, None)) == -4              # initial_state overlaps y
+    assert b"initial_state" in lib.sscan_last_error()
+    assert f(*args(0x20000, None, x=None)) == -1     # required pointers still checked
+    # empty batch: nothing to do, initial_state may be NULL (A still required: dim > 0)
+    assert lib.sscan_forward_from_state(None, None, 0x3000, None, None, None, None, None, None,
+                                        0, 4, 2, 3, 0, None) == 0
 
 
 def _step(lib, **kw):

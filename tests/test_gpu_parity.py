@@ -246,3 +246,66 @@ def test_runs_on_a_side_stream():
     yr, _ = oracle.forward(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["Dskip"],
                            want_state=False)
     assert rel_err(to_host(y), yr) <= TOL["f32"]
+
+
+# ---------------------------------------------------------------- starting from a state
+
+STATE_SHAPES = [
+    (2, 700, 100, 16, "f32", "s4d_real"),     # segment kernels, structured-real A
+    (2, 700, 100, 8, "bf16", "loguniform"),   # segment kernels, general A
+    (256, 300, 64, 16, "bf16", "s4d_real"),   # lockstep kernel
+    (1, 20000, 64, 16, "f32", "s4d_real"),    # ~300 segments
+]
+
+
+@pytest.mark.parametrize("shape", STATE_SHAPES, ids=lambda s: "b{}_L{}_d{}_N{}_{}_{}".format(*s))
+def test_initial_state_matches_oracle(shape):
+    batch, L, dim, N, io, a_init = shape
+    wl = datagen.custom(f"h0_{batch}_{L}_{dim}_{N}_{io}", batch, L, dim, N, io, a_init, key=30)
+    inp = datagen.scan_inputs(wl)
+    h0 = (np.random.default_rng(5).standard_normal((batch, dim, N)) * 0.5).astype(np.float32)
+    announce(f"forward_from_state {wl.name}")
+    t = upload_scan(inp, io)
+    hs = torch.full((batch, dim, N), float("nan"), device="cuda")
+    y = sscan.forward(t["x"], t["delta"], t["A"], t["B"], t["C"], t["Dskip"], final_state=hs,
+                      initial_state=torch.from_numpy(h0).cuda())
+    torch.cuda.synchronize()
+    yr, hr = oracle.forward(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["Dskip"], h0=h0,
+                            nthreads=oracle_threads())
+    ey, eh = rel_err(to_host(y), yr), rel_err(hs.cpu().numpy(), hr)
+    announce(f"  err(y)={ey:.3e} err(h)={eh:.3e}")
+    assert ey <= TOL[io] and eh <= TOL[io]
+
+
+@pytest.mark.parametrize("shape", STATE_SHAPES[:3], ids=lambda s: "b{}_L{}_d{}_N{}_{}_{}".format(*s))
+def test_prefill_in_two_pieces_equals_one_pass(shape):
+    """forward over [0, L1), then forward_from_state over [L1, L) from its final state, against the
+    oracle over [0, L) in one pass."""
+    batch, L, dim, N, io, a_init = shape
+    wl = datagen.custom(f"split_{batch}_{L}_{dim}_{N}_{io}", batch, L, dim, N, io, a_init, key=31)
+    inp = datagen.scan_inputs(wl)
+    L1 = 257
+    dev = lambda a: to_dev(np.ascontiguousarray(a), io)
+    A, D = torch.from_numpy(inp["A"]).cuda(), torch.from_numpy(inp["Dskip"]).cuda()
+    h1 = torch.empty(batch, dim, N, device="cuda")
+    h2 = torch.empty(batch, dim, N, device="cuda")
+    ya = sscan.forward(dev(inp["x"][:, :L1]), dev(inp["delta"][:, :L1]), A, dev(inp["B"][:, :L1]),
+                       dev(inp["C"][:, :L1]), D, final_state=h1)
+    yb = sscan.forward(dev(inp["x"][:, L1:]), dev(inp["delta"][:, L1:]), A, dev(inp["B"][:, L1:]),
+                       dev(inp["C"][:, L1:]), D, final_state=h2, initial_state=h1)
+    torch.cuda.synchronize()
+    yr, hr = oracle.forward(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["Dskip"],
+                            nthreads=oracle_threads())
+    y = np.concatenate([to_host(ya), to_host(yb)], axis=1)
+    assert rel_err(y, yr) <= TOL[io]
+    assert rel_err(h2.cpu().numpy(), hr) <= TOL[io]
+
+
+def test_empty_sequence_copies_the_initial_state():
+    h0 = torch.randn(2, 8, 4, device="cuda")
+    hs = torch.zeros(2, 8, 4, device="cuda")
+    x = torch.empty(2, 0, 8, device="cuda")
+    sscan.forward(x, x.clone(), torch.zeros(8, 4, device="cuda"), torch.empty(2, 0, 4, device="cuda"),
+                  torch.empty(2, 0, 4, device="cuda"), final_state=hs, initial_state=h0)
+    torch.cuda.synchronize()
+    assert torch.equal(hs, h0)
