@@ -35,6 +35,26 @@ PEAK_VALU_TFLOPS = 78.6
 FLOPS_PER_UPDATE = 8           # per (b,t,d,n): 3 FMA + 2 MUL in the fused S4D-real update
 
 
+def recorded_traffic(wl):
+    """HBM bytes per launch of the dominant kernel from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated with a plain copy), or None when there is no summary
+    for this workload or the kernel source has changed since the counters were taken."""
+    import hashlib
+    import re
+    prof = os.path.join(ROOT, "profiles", f"k_lockstep_{wl.name}_hbm_counters.md")
+    src = os.path.join(ROOT, "selective_state_space_77_amd", "csrc", "sscan_kernels.hip")
+    if not os.path.exists(prof):
+        return None
+    text = open(prof).read()
+    m_t = re.search(r"^traffic_bytes: (\d+)$", text, re.M)
+    m_h = re.search(r"^kernel_src_sha256_16: ([0-9a-f]+)$", text, re.M)
+    if not (m_t and m_h):
+        return None
+    if hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != m_h.group(1):
+        return None
+    return int(m_t.group(1))
+
+
 def algorithmic_bytes(wl, with_state: bool) -> int:
     es = 2 if wl.io == "bf16" else 4
     per_elem = 3 * es                                  # x, delta in; y out
@@ -209,7 +229,7 @@ def main() -> int:
         "peak": PEAK_VALU_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(tflops / PEAK_VALU_TFLOPS, 4),
-        "traffic": None,
+        "traffic": recorded_traffic(wl),
         "per_launch": {"updates": updates, "flops_per_update": FLOPS_PER_UPDATE,
                        "algorithmic_bytes": nbytes, "event_avg_us": round(ev_avg * 1e6, 2),
                        "event_min_us": round(float(durs.min()) * 1e6, 2)},

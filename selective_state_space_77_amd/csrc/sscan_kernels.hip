@@ -223,112 +223,108 @@ __global__ __launch_bounds__(kWave) void k_seg(
         }
     }
 
-    const T *xrow = x + (b * L) * dim + dbase;
-    const T *drow = delta + (b * L) * dim + dbase;
-    T *yrow = kMain ? y + (b * L) * dim + dbase : nullptr;
-    const float *bcrow = bc + (b * L) * (2 * NT);
+    // Descriptors cover exactly this segment: tokens past its end read x = delta
+    // = 0 (the state is left unchanged) and their stores are dropped, so the
+    // token loop has no per-token branches.
+    constexpr int ES = IO::kBytes;
+    constexpr int U = kUnroll;
+    const int nseg = int(t1 - t0);
+    const int last = nseg - 1;
+    const uint32_t voff = uint32_t((dbase + lane) * ES);
+    const uint32_t rowb = uint32_t(dim * ES);
+    const int64_t seg_bytes = int64_t(nseg) * dim * ES;
+    const rsrc_t rx = make_rsrc(x + (b * L + t0) * dim, seg_bytes);
+    const rsrc_t rd = make_rsrc(delta + (b * L + t0) * dim, seg_bytes);
+    const rsrc_t ry = make_rsrc(kMain ? y + (b * L + t0) * dim : nullptr, kMain ? seg_bytes : 0);
+    const float *bc0 = bc + (b * L + t0) * (2 * NT);
     const float dsk = (kMain && Dskip) ? Dskip[d] : 0.f;
     float dsum = 0.f;
 
-    T xr[kUnroll], dr[kUnroll];
+    T xr[U], dr[U];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        const int64_t t = min(t0 + u, t1 - 1);
-        xr[u] = xrow[t * dim + lo];
-        dr[u] = drow[t * dim + lo];
+    for (int u = 0; u < U; ++u) {
+        xr[u] = IO::bld(rx, voff, uint32_t(u) * rowb);
+        dr[u] = IO::bld(rd, voff, uint32_t(u) * rowb);
     }
+    float rowA[2 * NT], rowB[2 * NT];
+#pragma unroll
+    for (int i = 0; i < 2 * NT; ++i) rowA[i] = bc0[i];
 
-    if constexpr (kFast) {
-        float brow[2 * NT];
+    const float alpha = -a[0];
+    const float inv_alpha = 1.f / alpha;
+    const float a2 = a[0] * kLog2e;
+    float k[NT];
 #pragma unroll
-        for (int i = 0; i < 2 * NT; ++i) brow[i] = bcrow[t0 * (2 * NT) + i];
-        const float alpha = -a[0];
-        const float inv_alpha = 1.f / alpha;
-        const float a2 = a[0] * kLog2e;
-        float k[NT];
+    for (int n = 0; n < NT; ++n) k[n] = kFast ? h[n] * alpha : h[n];
+
+    // one token: structured-real update on the scaled state, or the general one
+    auto token = [&](int tau, float xv, float dv, const float *row) {
+        float yacc = 0.f;
+        if constexpr (kFast) {
+            const float r = exp2_hw(dv * a2);
+            float pw = r;
 #pragma unroll
-        for (int n = 0; n < NT; ++n) k[n] = h[n] * alpha;
-        for (int64_t tc = t0; tc < t1; tc += kUnroll) {
-            float xv[kUnroll], dv[kUnroll];
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                xv[u] = IO::cvt(xr[u]);
-                dv[u] = IO::cvt(dr[u]);
+            for (int n = 0; n < NT; ++n) {
+                const float e = fmaf(-row[n], xv, k[n]);
+                const float q = pw * e;
+                k[n] = fmaf(row[n], xv, q);
+                if (kMain) yacc = fmaf(row[NT + n], k[n], yacc);
+                pw *= r;
             }
+        } else {
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int64_t t = min(tc + kUnroll + u, t1 - 1);
-                xr[u] = xrow[t * dim + lo];
-                dr[u] = drow[t * dim + lo];
-            }
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int64_t t = tc + u;
-                if (t < t1) {
-                    float bnext[2 * NT];
-                    const int64_t tn = min(t + 1, t1 - 1);
-#pragma unroll
-                    for (int i = 0; i < 2 * NT; ++i) bnext[i] = bcrow[tn * (2 * NT) + i];
-                    const float r = exp2_hw(dv[u] * a2);
-                    float pw = r, yacc = 0.f;
-#pragma unroll
-                    for (int n = 0; n < NT; ++n) {
-                        const float e = fmaf(-brow[n], xv[u], k[n]);
-                        const float q = pw * e;
-                        k[n] = fmaf(brow[n], xv[u], q);
-                        if (kMain) yacc = fmaf(brow[NT + n], k[n], yacc);
-                        pw *= r;
-                    }
-                    if (kMain) {
-                        if (active) yrow[t * dim + lo] = IO::enc(fmaf(yacc, inv_alpha, dsk * xv[u]));
-                    } else {
-                        dsum += dv[u];
-                    }
-#pragma unroll
-                    for (int i = 0; i < 2 * NT; ++i) brow[i] = bnext[i];
-                }
+            for (int n = 0; n < NT; ++n) {
+                const float an = a[n];
+                const float abar = exp2_hw(dv * (an * kLog2e));
+                const float g = zoh_gain(dv, an, dv * an, abar);
+                k[n] = fmaf(abar, k[n], g * ((row[n] * float(n + 1)) * xv));
+                if (kMain) yacc = fmaf(row[NT + n], k[n], yacc);
             }
         }
+        if (kMain) {
+            const float yv = kFast ? fmaf(yacc, inv_alpha, dsk * xv) : fmaf(dsk, xv, yacc);
+            if (active) IO::bst(IO::enc(yv), ry, voff, uint32_t(tau) * rowb);
+        } else {
+            dsum += dv;
+        }
+    };
+    for (int g0 = 0; g0 < nseg; g0 += U) {
+        float xv[U], dv[U];
 #pragma unroll
-        for (int n = 0; n < NT; ++n) h[n] = k[n] * inv_alpha;
-    } else {
-        for (int64_t tc = t0; tc < t1; tc += kUnroll) {
-            float xv[kUnroll], dv[kUnroll];
+        for (int u = 0; u < U; ++u) {
+            xv[u] = IO::cvt(xr[u]);
+            dv[u] = IO::cvt(dr[u]);
+        }
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                xv[u] = IO::cvt(xr[u]);
-                dv[u] = IO::cvt(dr[u]);
+        for (int u = 0; u < U; ++u) {
+            xr[u] = IO::bld(rx, voff, uint32_t(g0 + U + u) * rowb);
+            dr[u] = IO::bld(rd, voff, uint32_t(g0 + U + u) * rowb);
+        }
+#pragma unroll
+        for (int u = 0; u < U; u += 2) {
+            const int tau = g0 + u;
+            __builtin_amdgcn_sched_barrier(0);
+            wait_scalar_loads();
+            {
+                const float *rn = bc0 + min(tau + 1, last) * (2 * NT);
+#pragma unroll
+                for (int i = 0; i < 2 * NT; ++i) rowB[i] = rn[i];
             }
+            __builtin_amdgcn_sched_barrier(0);
+            token(tau, xv[u], dv[u], rowA);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_scalar_loads();
+            {
+                const float *rn = bc0 + min(tau + 2, last) * (2 * NT);
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int64_t t = min(tc + kUnroll + u, t1 - 1);
-                xr[u] = xrow[t * dim + lo];
-                dr[u] = drow[t * dim + lo];
+                for (int i = 0; i < 2 * NT; ++i) rowA[i] = rn[i];
             }
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int64_t t = tc + u;
-                if (t < t1) {
-                    const float *row = bcrow + t * (2 * NT);
-                    const float dtv = dv[u];
-                    float yacc = 0.f;
-                    for (int n = 0; n < NT; ++n) {
-                        const float an = a[n];
-                        const float abar = exp2_hw(dtv * (an * kLog2e));
-                        const float g = zoh_gain(dtv, an, dtv * an, abar);
-                        const float bn = row[n] * float(n + 1);
-                        h[n] = fmaf(abar, h[n], g * (bn * xv[u]));
-                        if (kMain) yacc = fmaf(row[NT + n], h[n], yacc);
-                    }
-                    if (kMain) {
-                        if (active) yrow[t * dim + lo] = IO::enc(fmaf(dsk, xv[u], yacc));
-                    } else {
-                        dsum += dtv;
-                    }
-                }
-            }
+            __builtin_amdgcn_sched_barrier(0);
+            token(tau + 1, xv[u + 1], dv[u + 1], rowB);
         }
     }
+#pragma unroll
+    for (int n = 0; n < NT; ++n) h[n] = kFast ? k[n] * inv_alpha : k[n];
 
     if (!active) return;
     if (!kMain) {
