@@ -47,6 +47,8 @@ def _load():
         lib.oracle_forward.restype = ctypes.c_int
         lib.oracle_step.argtypes = [dp] * 8 + [i64] * 3
         lib.oracle_step.restype = ctypes.c_int
+        lib.oracle_backward.argtypes = [dp] * 16 + [i64] * 4 + [ctypes.c_int]
+        lib.oracle_backward.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -104,3 +106,27 @@ def step(state, x_t, delta_t, A, B_t, C_t, Dskip=None):
     if rc != 0:
         raise RuntimeError(f"oracle_step failed ({rc})")
     return y, st
+
+
+def backward(x, delta, A, B, C, Dskip, dy, h0=None, dhT=None, nthreads: int = 1):
+    """fp64 gradients of sum(dy * y) + sum(dhT * final_state) through forward().
+
+    Returns a dict with dx, ddelta (batch, L, dim), dA (dim, N), dB, dC (batch, L, N),
+    dDskip (dim,) and dh0 (batch, dim, N).  Dskip None means a zero skip (dDskip is
+    still returned)."""
+    x, delta, A, B, C, dy = map(_f64, (x, delta, A, B, C, dy))
+    Dskip, h0, dhT = _f64(Dskip), _f64(h0), _f64(dhT)
+    batch, L, dim = x.shape
+    N = A.shape[1]
+    if dy.shape != x.shape or delta.shape != x.shape or B.shape != (batch, L, N) or C.shape != B.shape:
+        raise ValueError("inconsistent shapes")
+    out = {"dx": np.empty_like(x), "ddelta": np.empty_like(x), "dA": np.empty((dim, N)),
+           "dB": np.empty((batch, L, N)), "dC": np.empty((batch, L, N)), "dDskip": np.empty(dim),
+           "dh0": np.empty((batch, dim, N))}
+    rc = _load().oracle_backward(_p(x), _p(delta), _p(A), _p(B), _p(C), _p(Dskip), _p(h0), _p(dy),
+                                 _p(dhT), _p(out["dx"]), _p(out["ddelta"]), _p(out["dA"]),
+                                 _p(out["dB"]), _p(out["dC"]), _p(out["dDskip"]), _p(out["dh0"]),
+                                 batch, L, dim, N, int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_backward failed ({rc})")
+    return out

@@ -44,11 +44,16 @@
  * The decode step uses (batch, dim) for x_t, delta_t, y_t and (batch, N) for
  * B_t, C_t, and updates state (batch, dim, N) in place.
  *
+ * The backward pass (oracle_backward, below) is the chain rule through the same
+ * definition.
+ *
  * Pins (tests, not this file): LTI case == explicit and FFT convolution,
  * ZOH step == the ODE solved analytically and by RK4, the 1-D GRU gate,
  * forgetting at large delta, identity at delta = 0, brute-force unrolling,
  * hand-worked exact examples in tests/golden, split-sequence and per-step
- * consistency, linearity and causality.  Every function here is pinned.
+ * consistency, linearity and causality; the backward pass by central finite
+ * differences of oracle_forward and the transpose identity of the x -> y map.
+ * Every function here is pinned.
  *
  * Threads: channels (b, d) are independent, so `nthreads` workers take
  * disjoint sets of channels; each channel's token loop stays sequential.
@@ -160,4 +165,144 @@ int oracle_step(double *state, const double *x_t, const double *delta_t, const d
     return ORACLE_OK;
 }
 
-int oracle_version(void) { return 1; }
+/*
+ * Backward pass: gradients of a scalar loss through the forward pass above.
+ * Given dy = dLoss/dy (batch, L, dim) and dhT = dLoss/d(final state) (NULL = 0),
+ * returns dx, ddelta (batch, L, dim), dA (dim, N), dB, dC (batch, L, N),
+ * dDskip (dim) and dh0 = dLoss/d(initial state) (batch, dim, N; NULL = not wanted).
+ *
+ * Plain chain rule on the definition, token by token backwards in time with the
+ * adjoint lam_t = dLoss/dh_t:
+ *     lam_t   = C_t * dy_t + Abar_{t+1} * lam_{t+1}      (lam_{L-1} gets dhT instead)
+ *     dx_t    = Dskip * dy_t + sum_n lam_t * Bbar_t
+ *     ddelta  = sum_n lam_t * (dAbar/ddelta * h_{t-1} + dgain/ddelta * B_t x_t)
+ *     dA      = sum_t lam_t * (dAbar/dA * h_{t-1} + dgain/dA * B_t x_t)
+ *     dB_t    = sum_d lam_t * gain_t * x_t,   dC_t = sum_d dy_t * h_t,   dDskip = sum dy * x
+ *     dh0     = Abar_0 * lam_0
+ * with Abar = exp(delta*A), gain = (exp(delta*A) - 1)/A (delta when A = 0) and
+ *     dAbar/ddelta = A*Abar,  dgain/ddelta = Abar,  dAbar/dA = delta*Abar,
+ *     dgain/dA = (delta*Abar - gain)/A  (delta^2/2 when A = 0).
+ * The forward states h_t of a channel are kept (L+1 rows of N doubles).
+ * Pinned in tests by central finite differences of oracle_forward.
+ */
+typedef struct {
+    const double *x, *delta, *A, *B, *C, *Dskip, *h0, *dy, *dhT;
+    double *dx, *ddelta, *dA, *dB, *dC, *dD, *dh0;
+    int64_t batch, L, dim, N;
+    int64_t d_first, d_last; /* channel range [d_first, d_last) of this worker, all batch rows */
+    double *hist;            /* (L+1)*N doubles */
+    double *lam;             /* N doubles */
+} bwd_job;
+
+static void *bwd_worker(void *arg) {
+    bwd_job *j = (bwd_job *)arg;
+    const int64_t L = j->L, dim = j->dim, N = j->N;
+    for (int64_t d = j->d_first; d < j->d_last; ++d) {
+        const double *Ar = j->A + d * N;
+        const double dsk = j->Dskip ? j->Dskip[d] : 0.0;
+        for (int64_t b = 0; b < j->batch; ++b) {
+            const int64_t c = b * dim + d;
+            double *h = j->hist; /* row 0 = h_{-1}, row t+1 = h_t */
+            for (int64_t n = 0; n < N; ++n) h[n] = j->h0 ? j->h0[c * N + n] : 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                const int64_t e = (b * L + t) * dim + d;
+                const int64_t r = (b * L + t) * N;
+                double *hp = h + t * N, *hn = h + (t + 1) * N;
+                for (int64_t n = 0; n < N; ++n) {
+                    const double z = j->delta[e] * Ar[n];
+                    const double abar = exp(z);
+                    const double gain = (Ar[n] != 0.0) ? expm1(z) / Ar[n] : j->delta[e];
+                    hn[n] = abar * hp[n] + gain * j->B[r + n] * j->x[e];
+                }
+            }
+            for (int64_t n = 0; n < N; ++n) j->lam[n] = j->dhT ? j->dhT[c * N + n] : 0.0;
+            for (int64_t t = L - 1; t >= 0; --t) {
+                const int64_t e = (b * L + t) * dim + d;
+                const int64_t r = (b * L + t) * N;
+                const double xv = j->x[e], dt = j->delta[e], g = j->dy[e];
+                const double *hp = h + t * N, *hn = h + (t + 1) * N;
+                double dxv = dsk * g, ddv = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    const double a = Ar[n];
+                    const double z = dt * a;
+                    const double abar = exp(z);
+                    const double gain = (a != 0.0) ? expm1(z) / a : dt;
+                    const double dgain_dA = (a != 0.0) ? (dt * abar - gain) / a : 0.5 * dt * dt;
+                    const double lam = j->lam[n] + j->C[r + n] * g; /* lam_t */
+                    const double bx = j->B[r + n] * xv;
+                    dxv += lam * gain * j->B[r + n];
+                    ddv += lam * (a * abar * hp[n] + abar * bx);
+                    j->dA[d * N + n] += lam * (dt * abar * hp[n] + dgain_dA * bx);
+                    j->dB[r + n] += lam * gain * xv;
+                    j->dC[r + n] += g * hn[n];
+                    j->lam[n] = abar * lam; /* carried to t-1 */
+                }
+                j->dx[e] = dxv;
+                j->ddelta[e] = ddv;
+                j->dD[d] += g * xv;
+            }
+            if (j->dh0)
+                for (int64_t n = 0; n < N; ++n) j->dh0[c * N + n] = j->lam[n];
+        }
+    }
+    return NULL;
+}
+
+int oracle_backward(const double *x, const double *delta, const double *A, const double *B,
+                    const double *C, const double *Dskip, const double *h0, const double *dy,
+                    const double *dhT, double *dx, double *ddelta, double *dA, double *dB, double *dC,
+                    double *dD, double *dh0, int64_t batch, int64_t L, int64_t dim, int64_t N,
+                    int nthreads) {
+    if (!x || !delta || !A || !B || !C || !dy || !dx || !ddelta || !dA || !dB || !dC || !dD)
+        return ORACLE_ERR_ARG;
+    if (batch < 0 || L < 0 || dim < 0 || N < 1) return ORACLE_ERR_ARG;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > dim) nthreads = dim > 0 ? (int)dim : 1;
+    const int64_t nbc = batch * L * N;
+    /* dB and dC are sums over channels: each worker accumulates its own copy, and the
+     * copies are added in worker order afterwards (deterministic). */
+    double *acc = (double *)calloc((size_t)(nthreads * 2 * nbc + 1), sizeof(double));
+    double *hist = (double *)calloc((size_t)(nthreads * ((L + 1) * N + N)), sizeof(double));
+    bwd_job *jobs = (bwd_job *)calloc((size_t)nthreads, sizeof(bwd_job));
+    pthread_t *tid = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    char *started = (char *)calloc((size_t)nthreads, 1);
+    if (!acc || !hist || !jobs || !tid || !started) {
+        free(acc); free(hist); free(jobs); free(tid); free(started);
+        return ORACLE_ERR_ARG;
+    }
+    for (int64_t i = 0; i < dim * N; ++i) dA[i] = 0.0;
+    for (int64_t i = 0; i < dim; ++i) dD[i] = 0.0;
+    for (int i = 0; i < nthreads; ++i) {
+        double *hi = hist + (int64_t)i * ((L + 1) * N + N);
+        bwd_job j = {x, delta, A, B, C, Dskip, h0, dy, dhT, dx, ddelta, dA,
+                     acc + (int64_t)i * 2 * nbc, acc + (int64_t)i * 2 * nbc + nbc, dD, dh0,
+                     batch, L, dim, N, dim * i / nthreads, dim * (i + 1) / nthreads,
+                     hi, hi + (L + 1) * N};
+        jobs[i] = j;
+    }
+    if (nthreads == 1) {
+        bwd_worker(&jobs[0]);
+    } else {
+        for (int i = 0; i < nthreads; ++i) {
+            if (pthread_create(&tid[i], NULL, bwd_worker, &jobs[i]) == 0)
+                started[i] = 1;
+            else
+                bwd_worker(&jobs[i]);
+        }
+        for (int i = 0; i < nthreads; ++i)
+            if (started[i]) pthread_join(tid[i], NULL);
+    }
+    for (int64_t k = 0; k < nbc; ++k) {
+        double sb = 0.0, sc = 0.0;
+        for (int i = 0; i < nthreads; ++i) {
+            sb += acc[(int64_t)i * 2 * nbc + k];
+            sc += acc[(int64_t)i * 2 * nbc + nbc + k];
+        }
+        dB[k] = sb;
+        dC[k] = sc;
+    }
+    free(acc); free(hist); free(jobs); free(tid); free(started);
+    return ORACLE_OK;
+}
+
+int oracle_version(void) { return 2; }

@@ -351,3 +351,81 @@ def test_missing_skip_is_zero_skip():
     y0, _ = oracle.forward(x, delta, A, B, C, None)
     yz, _ = oracle.forward(x, delta, A, B, C, np.zeros(2))
     np.testing.assert_array_equal(y0, yz)
+
+
+# ---------------------------------------------------------------- backward pass
+
+def _loss(inp, dy, dhT):
+    y, hs = oracle.forward(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["Dskip"],
+                           h0=inp["h0"])
+    return float(np.sum(dy * y) + np.sum(dhT * hs))
+
+
+def _grad_problem(seed):
+    rng = np.random.default_rng(seed)
+    batch, L, dim, N = 2, 7, 3, 3
+    x, delta, A, B, C, D = _rand_problem(rng, batch, L, dim, N)
+    A[1, 0] = 0.0            # the A -> 0 limit
+    A[2, 2] = 0.3            # a growing mode
+    inp = {"x": x, "delta": delta, "A": A, "B": B, "C": C, "Dskip": D,
+           "h0": rng.standard_normal((batch, dim, N))}
+    dy = rng.standard_normal((batch, L, dim))
+    dhT = rng.standard_normal((batch, dim, N))
+    return inp, dy, dhT
+
+
+@pytest.mark.parametrize("seed", [21, 22])
+def test_backward_matches_central_finite_differences(seed):
+    """Every gradient against (L(p + e) - L(p - e)) / 2e of the forward oracle's scalar loss
+    sum(dy * y) + sum(dhT * h_final); independent of how the backward pass is derived."""
+    inp, dy, dhT = _grad_problem(seed)
+    g = oracle.backward(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["Dskip"], dy,
+                        h0=inp["h0"], dhT=dhT)
+    names = {"x": "dx", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "Dskip": "dDskip",
+             "h0": "dh0"}
+    for key, gname in names.items():
+        p = inp[key]
+        num = np.zeros_like(p)
+        for idx in np.ndindex(p.shape):
+            eps = 1e-6 * max(1.0, abs(p[idx]))
+            old = p[idx]
+            p[idx] = old + eps
+            lp = _loss(inp, dy, dhT)
+            p[idx] = old - eps
+            lm = _loss(inp, dy, dhT)
+            p[idx] = old
+            num[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(g[gname], num, rtol=2e-6, atol=2e-7, err_msg=gname)
+
+
+def test_backward_dx_is_the_transpose_of_the_linear_map():
+    """With delta, B, C, A fixed and h0 = 0 the map x -> (y, h_final) is linear; the gradient
+    dx for incoming (dy, dhT) must satisfy <dy, y(v)> + <dhT, h(v)> = <dx, v> for any v."""
+    inp, dy, dhT = _grad_problem(23)
+    g = oracle.backward(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["Dskip"], dy,
+                        dhT=dhT)
+    rng = np.random.default_rng(24)
+    for _ in range(3):
+        v = rng.standard_normal(inp["x"].shape)
+        y, hs = oracle.forward(v, inp["delta"], inp["A"], inp["B"], inp["C"], inp["Dskip"])
+        lhs = np.sum(dy * y) + np.sum(dhT * hs)
+        assert abs(lhs - np.sum(g["dx"] * v)) <= 1e-10 * max(1.0, abs(lhs))
+
+
+def test_backward_is_linear_in_the_incoming_gradients_and_dD_is_closed_form():
+    inp, dy, dhT = _grad_problem(25)
+    args = (inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["Dskip"])
+    g1 = oracle.backward(*args, dy, h0=inp["h0"], dhT=dhT)
+    g2 = oracle.backward(*args, 3.0 * dy, h0=inp["h0"], dhT=3.0 * dhT)
+    for k in g1:
+        np.testing.assert_allclose(g2[k], 3.0 * g1[k], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(g1["dDskip"], np.einsum("bld,bld->d", dy, inp["x"]), rtol=1e-12)
+
+
+def test_backward_threads_do_not_change_the_result():
+    inp, dy, dhT = _grad_problem(26)
+    args = (inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["Dskip"], dy)
+    g1 = oracle.backward(*args, h0=inp["h0"], dhT=dhT, nthreads=1)
+    g3 = oracle.backward(*args, h0=inp["h0"], dhT=dhT, nthreads=3)
+    for k in g1:
+        np.testing.assert_array_equal(g1[k], g3[k])
