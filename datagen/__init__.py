@@ -39,7 +39,8 @@ import numpy as np
 
 TBLK = 256  # tokens per generator block
 
-_TENSOR_IDS = {"x": 1, "delta": 2, "B": 3, "C": 4, "A": 5, "Dskip": 6, "dt_bias": 7}
+_TENSOR_IDS = {"x": 1, "delta": 2, "B": 3, "C": 4, "A": 5, "Dskip": 6, "dt_bias": 7,
+               "dy": 8, "h0": 9, "dhT": 10}
 
 
 @dataclass(frozen=True)
@@ -149,7 +150,7 @@ def gen_dt_bias(wl: Workload, seed: int = 0) -> np.ndarray:
 
 
 def _width(wl: Workload, tensor: str) -> int:
-    return wl.dim if tensor in ("x", "delta") else wl.dstate
+    return wl.dim if tensor in ("x", "delta", "dy") else wl.dstate
 
 
 def _draw(g: np.random.Generator, shape, tensor: str, bias) -> np.ndarray:
@@ -235,3 +236,19 @@ def step_inputs(wl: Workload, step: int, seed: int = 0, bias: np.ndarray | None 
     if bias is None:
         bias = gen_dt_bias(wl, seed)
     return {t: gen_step(wl, t, step, seed, bias) for t in ("x", "delta", "B", "C")}
+
+
+def gen_state(wl: Workload, tensor: str, seed: int = 0) -> np.ndarray:
+    """A (batch, dim, N) fp32 state-shaped tensor, standard normal: "h0" (state
+    before token 0) or "dhT" (cotangent of the final state)."""
+    if tensor not in ("h0", "dhT"):
+        raise ValueError(f"not a state tensor: {tensor!r}")
+    g = _rng(seed, wl, tensor)
+    return g.standard_normal((wl.batch, wl.dim, wl.dstate)).astype(np.float32)
+
+
+def grad_inputs(wl: Workload, seed: int = 0, threads: int | None = None) -> dict:
+    """Cotangents for a backward pass: dy (batch, L, dim) in the I/O dtype's values,
+    standard normal like x, and dhT; plus an initial state h0."""
+    return {"dy": gen_seq(wl, "dy", seed=seed, threads=threads),
+            "h0": gen_state(wl, "h0", seed), "dhT": gen_state(wl, "dhT", seed)}

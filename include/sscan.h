@@ -120,6 +120,45 @@ int sscan_step(float *state, const void *x_t, const void *delta_t, const float *
                const void *B_t, const void *C_t, const float *Dskip, void *y_t, int64_t batch,
                int64_t dim, int64_t dstate, int io_dtype, void *stream);
 
+/*
+ * Backward pass of the whole-sequence scan: gradients of a scalar loss through
+ * sscan_forward_from_state, given dLoss/dy and dLoss/d(final_state).  The pages
+ * name the backward pass and its recomputation of the states from the inputs
+ * ("Mamba and State Space Models", the hardware-aware implementation; "Mamba
+ * matches the Transformer...", "Fuse the kernel and recompute"); the formulas
+ * are the chain rule through the forward definition above:
+ *   lam_t     = C_t dy_t + Abar_{t+1} lam_{t+1}   (lam_{L-1} = C dy + dfinal_state)
+ *   dx        = Dskip dy + sum_n lam Bbar           ddelta = sum_n lam (A h_t + B x)
+ *   dA[d,n]   = sum_{b,t} lam (delta Abar h_{t-1} + (delta Abar - gain)/A B x)
+ *   dB[b,t,n] = sum_d lam gain x                    dC[b,t,n] = sum_d dy h_t
+ *   dDskip[d] = sum_{b,t} dy x                      dinitial_state = Abar_0 lam_0
+ * with gain = (exp(delta A) - 1)/A (delta when A = 0).  The states are recomputed
+ * on chip; nothing from the forward pass is needed.
+ *
+ *   x, delta, A, B, C, Dskip, initial_state  [in]  as for sscan_forward_from_state
+ *                      (Dskip, initial_state may be NULL: zero).
+ *   dy           [in]  (batch, seqlen, dim), io_dtype: dLoss/dy.
+ *   dfinal_state [in]  (batch, dim, dstate) fp32 dLoss/d(final_state), or NULL (zero).
+ *   dx, ddelta   [out] (batch, seqlen, dim), io_dtype.
+ *   dA           [out] (dim, dstate) fp32, summed over batch and time.
+ *   dB, dC       [out] (batch, seqlen, dstate) fp32 (not io_dtype), summed over channels.
+ *   dDskip       [out] (dim) fp32, or NULL if not wanted.
+ *   dinitial_state [out] (batch, dim, dstate) fp32, or NULL if not wanted.
+ * dim may be at most 2^24 (SSCAN_ERR_UNSUPPORTED above).
+ * Outputs are overwritten, not accumulated, and must not overlap any argument.
+ * Every sum is taken in a fixed order: results are bitwise reproducible.  With
+ * seqlen == 0, dinitial_state receives a copy of dfinal_state (zeros if NULL) and
+ * dA, dDskip zeros; with dim == 0, dB and dC are zeros.
+ * Scratch (stream-ordered): about 4*dstate*(seqlen/32)*batch*dim bytes of saved
+ * states plus 128*batch*seqlen*ceil(dim/64) bytes of dB/dC partials (dstate
+ * rounded up to a power of two).
+ */
+int sscan_backward(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                   const float *Dskip, const float *initial_state, const void *dy,
+                   const float *dfinal_state, void *dx, void *ddelta, float *dA, float *dB,
+                   float *dC, float *dDskip, float *dinitial_state, int64_t batch, int64_t seqlen,
+                   int64_t dim, int64_t dstate, int io_dtype, void *stream);
+
 /* Static text for a status code (never NULL). */
 const char *sscan_status_string(int status);
 

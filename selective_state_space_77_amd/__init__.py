@@ -7,6 +7,7 @@ package raises.
 
     forward(x, delta, A, B, C, Dskip=None, y=None, final_state=None, stream=None,
             initial_state=None)
+    backward(x, delta, A, B, C, dy, Dskip=None, initial_state=None, dfinal_state=None, ...)
     step(state, x_t, delta_t, A, B_t, C_t, Dskip=None, y_t=None, stream=None)
 
 Shapes and layouts follow include/sscan.h: x, delta, y (batch, L, dim); B, C
@@ -47,6 +48,9 @@ def _load() -> ctypes.CDLL:
     lib.sscan_forward_from_state.argtypes = [vp, vp, fp, vp, vp, fp, fp, vp, fp, i64, i64, i64, i64,
                                              ctypes.c_int, vp]
     lib.sscan_forward_from_state.restype = ctypes.c_int
+    lib.sscan_backward.argtypes = [vp, vp, fp, vp, vp, fp, fp, vp, fp, vp, vp, fp, fp, fp, fp, fp,
+                                   i64, i64, i64, i64, ctypes.c_int, vp]
+    lib.sscan_backward.restype = ctypes.c_int
     lib.sscan_step.argtypes = [fp, vp, vp, fp, vp, vp, fp, vp, i64, i64, i64, ctypes.c_int, vp]
     lib.sscan_step.restype = ctypes.c_int
     lib.sscan_status_string.argtypes = [ctypes.c_int]
@@ -120,6 +124,41 @@ def forward(x, delta, A, B, C, Dskip=None, y=None, final_state=None, stream=None
                                       batch, L, dim, N, io, _stream(stream, x.device))
     _check(rc)
     return y
+
+
+def backward(x, delta, A, B, C, dy, Dskip=None, initial_state=None, dfinal_state=None,
+             want_dskip=True, want_dinitial=True, stream=None):
+    """Gradients of a scalar loss through forward(), given dy = dLoss/dy and
+    dfinal_state = dLoss/d(final state) (None: zero).
+
+    Returns a dict: dx, ddelta (like x), dA (dim, N), dB, dC (batch, L, N) fp32,
+    dDskip (dim,) and dinitial_state (batch, dim, N) fp32 when wanted (else None)."""
+    batch, L, dim = x.shape
+    N = A.shape[1]
+    if delta.shape != x.shape or dy.shape != x.shape or tuple(A.shape) != (dim, N) \
+            or B.shape != (batch, L, N) or C.shape != B.shape:
+        raise ValueError("inconsistent shapes")
+    io = _io_code(x, delta, B, C, dy)
+    for t, name, shape in ((Dskip, "Dskip", (dim,)), (initial_state, "initial_state", (batch, dim, N)),
+                           (dfinal_state, "dfinal_state", (batch, dim, N))):
+        if t is not None and tuple(t.shape) != shape:
+            raise ValueError(f"{name} must have shape {shape}")
+    f32 = dict(dtype=torch.float32, device=x.device)
+    out = {"dx": torch.empty_like(x), "ddelta": torch.empty_like(x),
+           "dA": torch.empty((dim, N), **f32), "dB": torch.empty((batch, L, N), **f32),
+           "dC": torch.empty((batch, L, N), **f32),
+           "dDskip": torch.empty((dim,), **f32) if want_dskip else None,
+           "dinitial_state": torch.empty((batch, dim, N), **f32) if want_dinitial else None}
+    rc = lib.sscan_backward(_dev(x, "x"), _dev(delta, "delta"), _dev(A, "A", torch.float32),
+                            _dev(B, "B"), _dev(C, "C"), _dev(Dskip, "Dskip", torch.float32),
+                            _dev(initial_state, "initial_state", torch.float32), _dev(dy, "dy"),
+                            _dev(dfinal_state, "dfinal_state", torch.float32),
+                            _dev(out["dx"], "dx"), _dev(out["ddelta"], "ddelta"), _dev(out["dA"], "dA"),
+                            _dev(out["dB"], "dB"), _dev(out["dC"], "dC"), _dev(out["dDskip"], "dDskip"),
+                            _dev(out["dinitial_state"], "dinitial_state"), batch, L, dim, N, io,
+                            _stream(stream, x.device))
+    _check(rc)
+    return out
 
 
 def step(state, x_t, delta_t, A, B_t, C_t, Dskip=None, y_t=None, stream=None):

@@ -145,6 +145,66 @@ int sscan_forward_from_state(const void *x, const void *delta, const float *A, c
                         dstate, io_dtype, stream);
 }
 
+int sscan_backward(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                   const float *Dskip, const float *initial_state, const void *dy,
+                   const float *dfinal_state, void *dx, void *ddelta, float *dA, float *dB,
+                   float *dC, float *dDskip, float *dinitial_state, int64_t batch, int64_t seqlen,
+                   int64_t dim, int64_t dstate, int io_dtype, void *stream) {
+    g_last_error[0] = '\0';
+    if (io_dtype != SSCAN_F32 && io_dtype != SSCAN_BF16)
+        return fail(SSCAN_ERR_UNSUPPORTED, "io_dtype must be SSCAN_F32 or SSCAN_BF16");
+    if (dstate < 1 || dstate > SSCAN_MAX_DSTATE)
+        return fail(SSCAN_ERR_UNSUPPORTED, "dstate must be in 1..16");
+    if (dim > (int64_t(1) << 24))
+        return fail(SSCAN_ERR_UNSUPPORTED, "backward: dim above 2^24 is not supported");
+    const int64_t es = io_dtype == SSCAN_BF16 ? 2 : 4;
+    int64_t bx, bbc, bbc32, ba, bd, bs, ws_guard;
+    if (!nbytes(&bx, es, batch, seqlen, dim) || !nbytes(&bbc, es, batch, seqlen, dstate) ||
+        !nbytes(&bbc32, 4, batch, seqlen, dstate) || !nbytes(&ba, 4, dim, dstate) ||
+        !nbytes(&bd, 4, dim) || !nbytes(&bs, 4, batch, dim, dstate) ||
+        !nbytes(&ws_guard, 2 * 16 * 4, batch, seqlen, dim / 64 + 1))
+        return fail(SSCAN_ERR_SHAPE, "negative size or byte size overflows int64");
+    const Span ins[] = {{x, bx, "x"}, {delta, bx, "delta"}, {A, ba, "A"}, {B, bbc, "B"},
+                        {C, bbc, "C"}, {Dskip, Dskip ? bd : 0, "Dskip"},
+                        {initial_state, initial_state ? bs : 0, "initial_state"}, {dy, bx, "dy"},
+                        {dfinal_state, dfinal_state ? bs : 0, "dfinal_state"}};
+    const Span outs[] = {{dx, bx, "dx"}, {ddelta, bx, "ddelta"}, {dA, ba, "dA"}, {dB, bbc32, "dB"},
+                         {dC, bbc32, "dC"}, {dDskip, dDskip ? bd : 0, "dDskip"},
+                         {dinitial_state, dinitial_state ? bs : 0, "dinitial_state"}};
+    const Span req[] = {ins[0], ins[1], ins[2], ins[3], ins[4], ins[7], outs[0], outs[1], outs[2],
+                        outs[3], outs[4]};
+    int rc = check_ptrs(req, 11);
+    if (rc) return rc;
+    rc = check_alias(outs, 7, ins, 9);
+    if (rc) return rc;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (batch == 0 || dim == 0 || seqlen == 0) {
+        // sums over an empty set: dA, dDskip (and dB, dC when dim == 0) are zero;
+        // with no tokens the gradient passes through to the initial state
+        hipError_t e = sscan::launch_copy_or_zero(dA, nullptr, dim * dstate, s);
+        if (e == hipSuccess && dDskip) e = sscan::launch_copy_or_zero(dDskip, nullptr, dim, s);
+        if (e == hipSuccess) e = sscan::launch_copy_or_zero(dB, nullptr, batch * seqlen * dstate, s);
+        if (e == hipSuccess) e = sscan::launch_copy_or_zero(dC, nullptr, batch * seqlen * dstate, s);
+        if (e == hipSuccess && dinitial_state)
+            e = sscan::launch_copy_or_zero(dinitial_state, seqlen == 0 ? dfinal_state : nullptr,
+                                           batch * dim * dstate, s);
+        return e == hipSuccess ? SSCAN_OK : fail_hip("zero-fill launch", e);
+    }
+
+    const sscan::BwdPlan plan = sscan::plan_backward(batch, seqlen, dim, dstate);
+    void *ws = nullptr;
+    hipError_t e = hipMallocAsync(&ws, plan.ws_bytes, s);
+    if (e != hipSuccess) return fail_hip("hipMallocAsync (scratch)", e);
+    sscan::BwdArgs a{x,  delta, A,  B,  C,  Dskip,  initial_state,  dy, dfinal_state, dx, ddelta, dA,
+                     dB, dC,    dDskip, dinitial_state, batch, seqlen, dim, int(dstate), io_dtype};
+    e = sscan::launch_backward(a, plan, ws, s);
+    const hipError_t ef = hipFreeAsync(ws, s);
+    if (e != hipSuccess) return fail_hip("backward launch", e);
+    if (ef != hipSuccess) return fail_hip("hipFreeAsync (scratch)", ef);
+    return SSCAN_OK;
+}
+
 int sscan_step(float *state, const void *x_t, const void *delta_t, const float *A,
                const void *B_t, const void *C_t, const float *Dskip, void *y_t, int64_t batch,
                int64_t dim, int64_t dstate, int io_dtype, void *stream) {

@@ -1,0 +1,86 @@
+// Device helpers shared by the forward, decode-step and backward kernels.
+// Private to the library; included by the .hip translation units only.
+#pragma once
+
+#include <math.h>
+
+#include "sscan_internal.h"
+
+namespace sscan {
+namespace dev {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+__device__ __forceinline__ float exp2_hw(float v) { return __builtin_amdgcn_exp2f(v); }
+
+// s_waitcnt lgkmcnt(0) alone (gfx9 encoding: vmcnt and expcnt fields left at
+// their "no wait" maxima).  Scalar loads return out of order, so the only wait
+// for one is lgkmcnt(0); issuing it before the next token's loads makes that
+// wait cover only the loads issued one token earlier.
+__device__ __forceinline__ void wait_scalar_loads() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// ZOH input gain g = (exp(z) - 1)/A with z = dt*A (dt when A == 0), given
+// abar = exp(z).  For |z| < 1/4 it uses dt * expm1(z)/z as the Taylor
+// polynomial 1 + z/2 + ... + z^6/7! (truncation below 2e-9 relative), which
+// avoids the cancellation in abar - 1 and needs no division; otherwise
+// (abar - 1)/A has no cancellation.
+__device__ __forceinline__ float zoh_gain(float dt, float a, float z, float abar) {
+    if (fabsf(z) < 0.25f) {
+        float p = 1.f / 5040.f;
+        p = fmaf(p, z, 1.f / 720.f);
+        p = fmaf(p, z, 1.f / 120.f);
+        p = fmaf(p, z, 1.f / 24.f);
+        p = fmaf(p, z, 1.f / 6.f);
+        p = fmaf(p, z, 0.5f);
+        p = fmaf(p, z, 1.f);
+        return dt * p;
+    }
+    return (abar - 1.f) / a;
+}
+
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float v) {
+    // round to nearest even (the gfx950 conversion instruction)
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
+}
+
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+
+// Raw buffer descriptor over `bytes` bytes from `base` (stride 0).  Accesses at
+// or past `bytes` read 0 and drop stores; the hardware range check is what
+// keeps loads of tokens past the end of the sequence in bounds.
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    const int64_t n = bytes < 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), short(0), int(n), 0x00020000);
+}
+
+struct IoF32 {
+    using T = float;
+    static constexpr int kBytes = 4;
+    __device__ static float ld(const T *p, int64_t i) { return p[i]; }
+    __device__ static float cvt(T v) { return v; }
+    __device__ static T enc(float v) { return v; }
+    __device__ static T bld(rsrc_t r, uint32_t voff, uint32_t soff) {
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+    }
+    __device__ static void bst(T v, rsrc_t r, uint32_t voff, uint32_t soff) {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+    }
+};
+
+struct IoBF16 {
+    using T = uint16_t;
+    static constexpr int kBytes = 2;
+    __device__ static float ld(const T *p, int64_t i) { return __uint_as_float(uint32_t(p[i]) << 16); }
+    __device__ static float cvt(T v) { return __uint_as_float(uint32_t(v) << 16); }
+    __device__ static T enc(float v) { return f32_to_bf16(v); }
+    __device__ static T bld(rsrc_t r, uint32_t voff, uint32_t soff) {
+        return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+    }
+    __device__ static void bst(T v, rsrc_t r, uint32_t voff, uint32_t soff) {
+        __builtin_amdgcn_raw_buffer_store_b16(v, r, voff, soff, 0);
+    }
+};
+
+}  // namespace dev
+}  // namespace sscan

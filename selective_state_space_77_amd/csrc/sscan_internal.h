@@ -63,6 +63,42 @@ struct FwdArgs {
 // Enqueue the forward pass; `ws` points at plan.ws_bytes of device scratch.
 hipError_t launch_forward(const FwdArgs &a, const FwdPlan &plan, void *ws, hipStream_t s);
 
+// Enqueue the prologue shared by the forward and backward passes: B/(n+1) and C
+// of each of `rows` tokens as fp32 rows of 2*nt floats into `bc`, and one flag
+// per 64-channel tile into `tile_fast` (1 when every A row of the tile is
+// A[d,n] = (n+1)*A[d,0] with A[d,0] < 0).
+hipError_t launch_prep(const void *B, const void *C, const float *A, float *bc, int *tile_fast,
+                       int64_t rows, int64_t dim, int N, int nt, int io, hipStream_t s);
+
+// Backward pass: one workgroup per (batch row, 64-channel tile) walks the whole
+// sequence; scratch holds the staged B/C rows, tile flags, the state entering
+// every chunk, per-tile dB/dC partials and per-batch-row dA/dDskip partials.
+struct BwdPlan {
+    int64_t tiles_per_batch, tiles;
+    int nt;
+    size_t off_bc, off_flags, off_ckpt, off_pbc, off_pad;
+    size_t ws_bytes;
+};
+
+BwdPlan plan_backward(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+
+struct BwdArgs {
+    const void *x, *delta;
+    const float *A;
+    const void *B, *C;
+    const float *Dskip;
+    const float *h0;   // NULL = zero
+    const void *dy;
+    const float *dhT;  // NULL = zero
+    void *dx, *ddelta;
+    float *dA, *dB, *dC, *dD, *dh0;  // dD, dh0 may be NULL
+    int64_t batch, L, dim;
+    int N;
+    int io;
+};
+
+hipError_t launch_backward(const BwdArgs &a, const BwdPlan &plan, void *ws, hipStream_t s);
+
 // Enqueue dst[i] = src ? src[i] : 0 for `count` floats (final_state at seqlen 0).
 hipError_t launch_copy_or_zero(float *dst, const float *src, int64_t count, hipStream_t s);
 

@@ -38,83 +38,12 @@
 
 #include <math.h>
 
-#include "sscan_internal.h"
+#include "sscan_device.h"
 
 namespace sscan {
 namespace {
 
-constexpr float kLog2e = 1.44269504088896340736f;
-
-__device__ __forceinline__ float exp2_hw(float v) { return __builtin_amdgcn_exp2f(v); }
-
-// s_waitcnt lgkmcnt(0) alone (gfx9 encoding: vmcnt and expcnt fields left at
-// their "no wait" maxima).  Scalar loads return out of order, so the only wait
-// for one is lgkmcnt(0); issuing it before the next token's loads makes that
-// wait cover only the loads issued one token earlier.
-__device__ __forceinline__ void wait_scalar_loads() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-
-// ZOH input gain g = (exp(z) - 1)/A with z = dt*A (dt when A == 0), given
-// abar = exp(z).  For |z| < 1/4 it uses dt * expm1(z)/z as the Taylor
-// polynomial 1 + z/2 + ... + z^6/7! (truncation below 2e-9 relative), which
-// avoids the cancellation in abar - 1 and needs no division; otherwise
-// (abar - 1)/A has no cancellation.
-__device__ __forceinline__ float zoh_gain(float dt, float a, float z, float abar) {
-    if (fabsf(z) < 0.25f) {
-        float p = 1.f / 5040.f;
-        p = fmaf(p, z, 1.f / 720.f);
-        p = fmaf(p, z, 1.f / 120.f);
-        p = fmaf(p, z, 1.f / 24.f);
-        p = fmaf(p, z, 1.f / 6.f);
-        p = fmaf(p, z, 0.5f);
-        p = fmaf(p, z, 1.f);
-        return dt * p;
-    }
-    return (abar - 1.f) / a;
-}
-
-
-__device__ __forceinline__ uint16_t f32_to_bf16(float v) {
-    // round to nearest even (the gfx950 conversion instruction)
-    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
-}
-
-using rsrc_t = __amdgpu_buffer_rsrc_t;
-
-// Raw buffer descriptor over `bytes` bytes from `base` (stride 0).  Accesses at
-// or past `bytes` read 0 and drop stores; the hardware range check is what
-// keeps loads of tokens past the end of the sequence in bounds.
-__device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes) {
-    const int64_t n = bytes < 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), short(0), int(n), 0x00020000);
-}
-
-struct IoF32 {
-    using T = float;
-    static constexpr int kBytes = 4;
-    __device__ static float ld(const T *p, int64_t i) { return p[i]; }
-    __device__ static float cvt(T v) { return v; }
-    __device__ static T enc(float v) { return v; }
-    __device__ static T bld(rsrc_t r, uint32_t voff, uint32_t soff) {
-        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
-    }
-    __device__ static void bst(T v, rsrc_t r, uint32_t voff, uint32_t soff) {
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
-    }
-};
-
-struct IoBF16 {
-    using T = uint16_t;
-    static constexpr int kBytes = 2;
-    __device__ static float ld(const T *p, int64_t i) { return __uint_as_float(uint32_t(p[i]) << 16); }
-    __device__ static float cvt(T v) { return __uint_as_float(uint32_t(v) << 16); }
-    __device__ static T enc(float v) { return f32_to_bf16(v); }
-    __device__ static T bld(rsrc_t r, uint32_t voff, uint32_t soff) {
-        return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
-    }
-    __device__ static void bst(T v, rsrc_t r, uint32_t voff, uint32_t soff) {
-        __builtin_amdgcn_raw_buffer_store_b16(v, r, voff, soff, 0);
-    }
-};
+using namespace dev;
 
 // ----------------------------------------------------------------------------
 // Prologue of every forward pass, one launch with two roles:
@@ -643,6 +572,30 @@ int round_nt(int64_t N) { return N <= 1 ? 1 : N <= 2 ? 2 : N <= 4 ? 4 : N <= 8 ?
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 template <class IO, int NT>
+void prep_t(const void *B, const void *C, const float *A, float *bc, int *flags, int64_t rows,
+            int64_t dim, int N, hipStream_t s) {
+    using T = typename IO::T;
+    const int64_t tiles_per_batch = (dim + kWave - 1) / kWave;
+    const int64_t prep_blocks = (rows * NT + 255) / 256;
+    const int64_t cls_blocks = (tiles_per_batch + 3) / 4;
+    hipLaunchKernelGGL((k_prep<IO, NT>), dim3(unsigned(prep_blocks + cls_blocks)), dim3(256), 0, s,
+                       static_cast<const T *>(B), static_cast<const T *>(C), bc, rows, N, A, dim,
+                       flags, tiles_per_batch, prep_blocks);
+}
+
+template <class IO>
+void prep_io(const void *B, const void *C, const float *A, float *bc, int *flags, int64_t rows,
+             int64_t dim, int N, int nt, hipStream_t s) {
+    switch (nt) {
+        case 1: return prep_t<IO, 1>(B, C, A, bc, flags, rows, dim, N, s);
+        case 2: return prep_t<IO, 2>(B, C, A, bc, flags, rows, dim, N, s);
+        case 4: return prep_t<IO, 4>(B, C, A, bc, flags, rows, dim, N, s);
+        case 8: return prep_t<IO, 8>(B, C, A, bc, flags, rows, dim, N, s);
+        default: return prep_t<IO, 16>(B, C, A, bc, flags, rows, dim, N, s);
+    }
+}
+
+template <class IO, int NT>
 hipError_t forward_t(const FwdArgs &a, const FwdPlan &p, void *ws, hipStream_t s) {
     using T = typename IO::T;
     char *base = static_cast<char *>(ws);
@@ -652,12 +605,7 @@ hipError_t forward_t(const FwdArgs &a, const FwdPlan &p, void *ws, hipStream_t s
     float *agg_h = reinterpret_cast<float *>(base + p.off_h);
     const T *x = static_cast<const T *>(a.x), *dl = static_cast<const T *>(a.delta);
     T *y = static_cast<T *>(a.y);
-    const int64_t rows = a.batch * a.L;
-    const int64_t prep_blocks = (rows * NT + 255) / 256;
-    const int64_t cls_blocks = (p.tiles_per_batch + 3) / 4;
-    hipLaunchKernelGGL((k_prep<IO, NT>), dim3(unsigned(prep_blocks + cls_blocks)), dim3(256), 0, s,
-                       static_cast<const T *>(a.B), static_cast<const T *>(a.C), bc, rows, a.N, a.A,
-                       a.dim, flags, p.tiles_per_batch, prep_blocks);
+    prep_t<IO, NT>(a.B, a.C, a.A, bc, flags, a.batch * a.L, a.dim, a.N, s);
     const dim3 seg_agg(unsigned((p.segments - 1) * p.tiles)), seg_main(unsigned(p.segments * p.tiles));
 #define SSCAN_SEG(MAIN, FAST, GRID)                                                                 \
     hipLaunchKernelGGL((k_seg<IO, NT, MAIN, FAST>), GRID, dim3(kWave), 0, s, x, dl, a.A, bc, a.Dskip,  \
@@ -761,6 +709,15 @@ FwdPlan plan_forward(int64_t batch, int64_t L, int64_t dim, int64_t N) {
 
 hipError_t launch_forward(const FwdArgs &a, const FwdPlan &p, void *ws, hipStream_t s) {
     return a.io == 1 ? forward_io<IoBF16>(a, p, ws, s) : forward_io<IoF32>(a, p, ws, s);
+}
+
+hipError_t launch_prep(const void *B, const void *C, const float *A, float *bc, int *tile_fast,
+                       int64_t rows, int64_t dim, int N, int nt, int io, hipStream_t s) {
+    if (io == 1)
+        prep_io<IoBF16>(B, C, A, bc, tile_fast, rows, dim, N, nt, s);
+    else
+        prep_io<IoF32>(B, C, A, bc, tile_fast, rows, dim, N, nt, s);
+    return hipGetLastError();
 }
 
 hipError_t launch_copy_or_zero(float *dst, const float *src, int64_t count, hipStream_t s) {

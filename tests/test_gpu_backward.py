@@ -1,0 +1,186 @@
+"""GPU parity of sscan_backward against the fp64 oracle's backward pass, through the C ABI.
+
+Every gradient (dx, ddelta, dA, dB, dC, dDskip, dinitial_state) is compared element
+by element with oracle.backward on the same inputs (bf16 workloads: the same
+bf16-rounded values).  Shapes cover both A paths (structured-real and general),
+ragged L around the 32-token chunk and 4-token run, ragged dim, every N bucket,
+A = 0 and A > 0, mixed A inside a 64-channel tile, missing optional arguments,
+empty inputs, determinism, and the benchmarked 4 x 8192 x 4096 bf16 workload.
+
+Tolerance: dx, ddelta, dinitial_state are per-channel quantities with the
+forward pass's precision (fp32 state; bf16 outputs for bf16 workloads), so the
+forward gates apply.  dA, dDskip (sums over batch and time) and dB, dC (sums
+over channels) are fp32 sums of up to batch*L or dim terms, taken in a
+different order from the oracle's; their bound is the accumulated rounding
+n*u*sum|terms| with u = 2^-24, and with terms of mixed sign the realistic
+growth is sqrt(n)*u relative to sum|terms|, which stays below 1e-4 of the
+metric's scale (max(|ref|, rms(ref))) for the n <= 32768 of these shapes.
+Both are checked against the forward gates.
+"""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+from oracle.compare import TOL, rel_err
+from tests.gpuutil import announce, oracle_threads, to_dev, to_host, upload_scan
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import selective_state_space_77_amd as sscan  # noqa: E402
+
+KEYS = ("dx", "ddelta", "dA", "dB", "dC", "dDskip", "dh0")
+
+
+def _gpu_bwd(inp, g, io, with_h0=True, with_dhT=True, Dskip=True, want=True):
+    t = upload_scan(inp, io)
+    dy = to_dev(g["dy"], io)
+    h0 = torch.from_numpy(g["h0"]).cuda() if with_h0 else None
+    dhT = torch.from_numpy(g["dhT"]).cuda() if with_dhT else None
+    out = sscan.backward(t["x"], t["delta"], t["A"], t["B"], t["C"], dy,
+                         Dskip=t["Dskip"] if Dskip else None, initial_state=h0, dfinal_state=dhT,
+                         want_dskip=want, want_dinitial=want)
+    torch.cuda.synchronize()
+    res = {k: (to_host(v) if v is not None else None) for k, v in out.items()}
+    res["dh0"] = res.pop("dinitial_state")
+    return res
+
+
+def _oracle_bwd(inp, g, with_h0=True, with_dhT=True, Dskip=True):
+    return oracle.backward(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"],
+                           inp["Dskip"] if Dskip else None, g["dy"],
+                           g["h0"] if with_h0 else None, g["dhT"] if with_dhT else None,
+                           nthreads=oracle_threads())
+
+
+def _compare(got, ref, io, keys=KEYS):
+    errs = {}
+    for k in keys:
+        errs[k] = rel_err(got[k], ref[k])
+    announce("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for k, e in errs.items():
+        assert e <= TOL[io], (k, e)
+    return errs
+
+
+def _check(wl, seed=0, inp=None, **kw):
+    announce(f"backward {wl.name} b={wl.batch} L={wl.seqlen} dim={wl.dim} N={wl.dstate} "
+             f"io={wl.io} A={wl.a_init} {kw}")
+    inp = inp or datagen.scan_inputs(wl, seed)
+    g = datagen.grad_inputs(wl, seed)
+    got = _gpu_bwd(inp, g, wl.io, **kw)
+    ref = _oracle_bwd(inp, g, **{k: v for k, v in kw.items() if k != "want"})
+    keys = KEYS if kw.get("want", True) else tuple(k for k in KEYS if k not in ("dDskip", "dh0"))
+    return _compare(got, ref, wl.io, keys)
+
+
+# ---------------------------------------------------------------- paths and shapes
+
+def test_tiny_general_A():
+    _check(datagen.workload("tiny_f32"))
+
+
+@pytest.mark.parametrize("batch,L,dim,N,io,a_init", [
+    (2, 300, 130, 16, "f32", "s4d_real"),    # ragged L and dim, fast path
+    (2, 300, 130, 16, "f32", "loguniform"),  # same, general path
+    (1, 1, 64, 16, "f32", "s4d_real"),       # one token
+    (3, 31, 65, 8, "f32", "s4d_real"),       # one partial chunk, 2 tiles
+    (2, 33, 64, 5, "f32", "loguniform"),     # one token into the second chunk, NT=8
+    (1, 64, 200, 3, "f32", "s4d_real"),      # NT=4
+    (2, 97, 70, 2, "f32", "loguniform"),     # NT=2
+    (2, 129, 64, 1, "f32", "s4d_real"),      # NT=1
+    (2, 517, 96, 16, "bf16", "s4d_real"),    # bf16 I/O
+    (1, 700, 64, 4, "bf16", "loguniform"),
+])
+def test_edge_shapes(batch, L, dim, N, io, a_init):
+    _check(datagen.custom("bwd_edge", batch, L, dim, N, io, a_init))
+
+
+@pytest.mark.parametrize("opts", [
+    dict(with_h0=False), dict(with_dhT=False), dict(with_h0=False, with_dhT=False),
+    dict(Dskip=False), dict(want=False)])
+def test_optional_arguments(opts):
+    _check(datagen.custom("bwd_opt", 2, 150, 80, 16, "f32", "s4d_real"), **opts)
+
+
+def test_mixed_A_in_a_tile_and_special_rows():
+    """Structured rows beside unstructured ones (the tile takes the general path),
+    A = 0 rows (gain = delta) and a row with A > 0."""
+    wl = datagen.custom("bwd_mixed", 2, 260, 130, 16, "f32", "s4d_real")
+    inp = datagen.scan_inputs(wl)
+    A = inp["A"].copy()
+    A[5] = -np.linspace(0.3, 3.0, 16, dtype=np.float32)   # unstructured row in tile 0
+    A[70] = 0.0                                            # A = 0 row in tile 1
+    A[71, :4] = 0.0                                        # partly zero row
+    A[72] = np.float32(0.01) * np.arange(1, 17, dtype=np.float32)  # A > 0 (grows)
+    A[130 - 1] = A[0] * 1e-4                               # tiny A: series branches
+    inp["A"] = A
+    _check(wl, inp=inp)
+
+
+def test_large_delta_and_small_delta():
+    """delta spanning 1e-6 .. 30: both branches of the ZOH gain and of dgain/dA."""
+    wl = datagen.custom("bwd_delta", 1, 200, 64, 16, "f32", "s4d_real")
+    inp = datagen.scan_inputs(wl)
+    rng = np.random.default_rng(5)
+    inp["delta"] = np.exp(rng.uniform(np.log(1e-6), np.log(30.0), inp["delta"].shape)).astype(np.float32)
+    _check(wl, inp=inp)
+
+
+def test_mamba130m_width_f32_full():
+    _check(datagen.workload("mamba130m_f32"))
+
+
+def test_mamba1p4b_width_bf16_full():
+    """The benchmarked workload, every gradient element checked."""
+    _check(datagen.workload("mamba1p4b_bf16"))
+
+
+# ---------------------------------------------------------------- properties
+
+def test_deterministic():
+    wl = datagen.custom("bwd_det", 2, 300, 200, 16, "bf16", "s4d_real")
+    inp = datagen.scan_inputs(wl)
+    g = datagen.grad_inputs(wl)
+    announce("backward determinism")
+    a = _gpu_bwd(inp, g, wl.io)
+    b = _gpu_bwd(inp, g, wl.io)
+    for k in KEYS:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_empty_sequence_passes_the_state_gradient_through():
+    announce("backward L=0")
+    dev = "cuda"
+    batch, dim, N = 2, 70, 16
+    x = torch.empty(batch, 0, dim, device=dev)
+    B = torch.empty(batch, 0, N, device=dev)
+    A = -torch.ones(dim, N, device=dev)
+    dhT = torch.randn(batch, dim, N, device=dev)
+    out = sscan.backward(x, x, A, B, B, x, Dskip=torch.ones(dim, device=dev), dfinal_state=dhT)
+    torch.cuda.synchronize()
+    assert torch.equal(out["dinitial_state"], dhT)
+    assert torch.count_nonzero(out["dA"]) == 0 and torch.count_nonzero(out["dDskip"]) == 0
+    out = sscan.backward(x, x, A, B, B, x)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out["dinitial_state"]) == 0
+
+
+def test_empty_batch_and_dim():
+    announce("backward batch=0, dim=0")
+    dev = "cuda"
+    A = -torch.ones(5, 4, device=dev)
+    x = torch.empty(0, 7, 5, device=dev)
+    B = torch.empty(0, 7, 4, device=dev)
+    out = sscan.backward(x, x, A, B, B, x)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out["dA"]) == 0
+    x = torch.empty(2, 7, 0, device=dev)
+    B = torch.randn(2, 7, 4, device=dev)
+    out = sscan.backward(x, x, torch.empty(0, 4, device=dev), B, B, x)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out["dB"]) == 0 and torch.count_nonzero(out["dC"]) == 0
