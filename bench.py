@@ -11,7 +11,10 @@ a roofline object for the scan and the fp64 oracle's throughput on a bounded
 sample on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
-                    [--no-cpu-baseline] [--calib-copy]
+                    [--pass forward|backward] [--no-cpu-baseline] [--calib-copy]
+
+--pass backward times sscan_backward instead (all seven gradients, the same
+workload, dy and dfinal_state seeded like x).
 """
 from __future__ import annotations
 
@@ -32,25 +35,40 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 # lane-ops/s; an FMA counts 2 flops -> 78.6 TFLOP/s (the published 157.3
 # TFLOP/s fp32-vector figure needs the packed forms, which this build never emits).
 PEAK_VALU_TFLOPS = 78.6
-FLOPS_PER_UPDATE = 8           # per (b,t,d,n): 3 FMA + 2 MUL in the fused S4D-real update
+FLOPS_PER_UPDATE = 8           # per (b,t,d,n): 4 FMA: w - k, the state update, the 1 - Abar recurrence, the readout
+# backward, per (b,t,d,n): the recomputed forward update (8) plus the adjoint and
+# gradient terms, each an FMA (2) or a multiply (1): lam = C*dy + carry (2),
+# lam*gain (1), dx += .*B (2), B*x (1), A*h_t + Bx (2), ddelta += lam*. (2),
+# delta*Abar (1), .*h_{t-1} + dgain/dA*Bx (3), dA += lam*. (2), dB term lam*gain*x (1),
+# dC term dy*h_t (1), carry Abar*lam (1)
+FLOPS_PER_UPDATE_BWD = 8 + 19
 
 
-def recorded_traffic(wl):
-    """HBM bytes per launch of the dominant kernel from the committed counter summary
-    (FETCH_SIZE + WRITE_SIZE, calibrated with a plain copy), or None when there is no summary
-    for this workload or the kernel source has changed since the counters were taken."""
+CSRC = os.path.join(ROOT, "selective_state_space_77_amd", "csrc")
+FWD_SOURCES = ("sscan_kernels.hip", "sscan_device.h", "sscan_internal.h")
+BWD_SOURCES = ("sscan_bwd.hip", "sscan_device.h", "sscan_internal.h")
+
+
+def source_fingerprint(files) -> str:
     import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(summary: str, sources):
+    """HBM bytes per launch of the dominant kernel from a committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated with a plain copy), or None when the summary is
+    missing or the kernel sources have changed since the counters were taken."""
     import re
-    prof = os.path.join(ROOT, "profiles", f"k_lockstep_{wl.name}_hbm_counters.md")
-    src = os.path.join(ROOT, "selective_state_space_77_amd", "csrc", "sscan_kernels.hip")
+    prof = os.path.join(ROOT, "profiles", summary)
     if not os.path.exists(prof):
         return None
     text = open(prof).read()
     m_t = re.search(r"^traffic_bytes: (\d+)$", text, re.M)
     m_h = re.search(r"^kernel_src_sha256_16: ([0-9a-f]+)$", text, re.M)
-    if not (m_t and m_h):
-        return None
-    if hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != m_h.group(1):
+    if not (m_t and m_h) or source_fingerprint(sources) != m_h.group(1):
         return None
     return int(m_t.group(1))
 
@@ -93,6 +111,117 @@ def cpu_baseline(wl, target_s: float = 10.0) -> dict:
     return {"value": elems / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
             "sample": f"batch rows [0,{rows}), tokens [0,{T}), all {wl.dim} channels, N={wl.dstate} "
                       f"({elems} elements, {dt:.2f} s wall, fp64, {threads} threads)"}
+
+
+def _calib_copy(dev):
+    """A plain 1 GiB device copy: the reference point for the HBM byte counters."""
+    import torch
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def _upload(wl, t, dev):
+    import torch
+
+    import datagen
+    a = datagen.gen_seq(wl, t)
+    if wl.io == "bf16":
+        return torch.from_numpy(datagen.bf16_bits(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(a).to(dev)
+
+
+def _time(call, steps, warmup, stream):
+    """W untimed calls, then exactly K timed calls with HIP events on the launch stream.
+    Returns (wall seconds per call, event seconds per call: mean, min)."""
+    import torch
+    for _ in range(warmup):
+        call()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(stream)
+        call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    durs = np.array([e0.elapsed_time(e1) for e0, e1 in ev]) * 1e-3
+    return wall, float(durs.mean()), float(durs.min())
+
+
+def cpu_baseline_backward(wl, target_s: float = 10.0) -> dict:
+    """The oracle's backward pass on a token prefix of batch row 0, sized to about target_s."""
+    import datagen
+    import oracle
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    T = min(wl.seqlen, 64)
+    while True:
+        inp = {k: datagen.gen_seq(wl, k, 0, T, batch_rows=[0]) for k in ("x", "delta", "B", "C", "dy")}
+        A, D = datagen.gen_A(wl), datagen.gen_Dskip(wl)
+        t0 = time.perf_counter()
+        oracle.backward(inp["x"], inp["delta"], A, inp["B"], inp["C"], D, inp["dy"], nthreads=threads)
+        dt = time.perf_counter() - t0
+        if dt >= target_s * 0.5 or T >= wl.seqlen:
+            break
+        T = min(wl.seqlen, int(T * min(8.0, max(2.0, target_s / max(dt, 1e-3)))))
+    elems = T * wl.dim
+    return {"value": elems / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
+            "sample": f"backward, batch row 0, tokens [0,{T}), all {wl.dim} channels, N={wl.dstate} "
+                      f"({elems} elements, {dt:.2f} s wall, fp64, {threads} threads)"}
+
+
+def bench_backward(wl, args, dev) -> int:
+    """One step = one sscan_backward call over the whole workload (recomputed states, all
+    gradients), inputs and cotangents resident in HBM."""
+    import torch
+
+    import datagen
+    import selective_state_space_77_amd as sscan
+
+    x, delta, B, C, dy = (_upload(wl, t, dev) for t in ("x", "delta", "B", "C", "dy"))
+    A = torch.from_numpy(datagen.gen_A(wl)).to(dev)
+    D = torch.from_numpy(datagen.gen_Dskip(wl)).to(dev)
+    dhT = torch.from_numpy(datagen.gen_state(wl, "dhT")).to(dev)
+    stream = torch.cuda.current_stream(dev)
+    print(f"[bench] backward {wl.name}: batch={wl.batch} L={wl.seqlen} dim={wl.dim} N={wl.dstate} "
+          f"io={wl.io}", file=sys.stderr, flush=True)
+    wall, ev_avg, ev_min = _time(
+        lambda: sscan.backward(x, delta, A, B, C, dy, Dskip=D, dfinal_state=dhT, stream=stream),
+        args.steps, args.warmup, stream)
+    if args.calib_copy:
+        _calib_copy(dev)
+    es = 2 if wl.io == "bf16" else 4
+    nbytes = (wl.elements * 5 * es                                  # x, delta, dy in; dx, ddelta out
+              + wl.batch * wl.seqlen * wl.dstate * (2 * es + 2 * 4)  # B, C in; dB, dC (fp32) out
+              + 2 * (wl.dim * wl.dstate * 4 + wl.dim * 4)           # A, Dskip in; dA, dDskip out
+              + 2 * wl.batch * wl.dim * wl.dstate * 4)              # dfinal_state in, dinitial_state out
+    updates = wl.elements * wl.dstate
+    tflops = updates * FLOPS_PER_UPDATE_BWD / ev_avg / 1e12
+    gbs = nbytes / ev_avg / 1e9
+    print(json.dumps({
+        "metric": "selective-scan backward: B*L*D elements/s",
+        "value": wl.elements / wall, "unit": "elements/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded; x,B,C,dy~N(0,1), delta=softplus(0.5N+bias))",
+        "config": {"workload": wl.name, "pass": "backward", "batch": wl.batch, "seqlen": wl.seqlen,
+                   "dim": wl.dim, "dstate": wl.dstate, "io_dtype": wl.io, "a_init": wl.a_init},
+        "roofline": {"kernel": "k_bwd (timed: the whole sscan_backward call on its stream)",
+                     "bound": "alu", "achieved": round(tflops, 3), "peak": PEAK_VALU_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_VALU_TFLOPS, 4),
+                     "traffic": recorded_traffic(f"k_bwd_{wl.name}_hbm_counters.md", BWD_SOURCES),
+                     "per_launch": {"updates": updates, "flops_per_update": FLOPS_PER_UPDATE_BWD,
+                                    "algorithmic_bytes": nbytes,
+                                    "event_avg_us": round(ev_avg * 1e6, 2),
+                                    "event_min_us": round(ev_min * 1e6, 2)},
+                     "hbm": {"achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": round(gbs / PEAK_HBM_GBS, 4)}},
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_backward(wl)}), flush=True)
+    return 0
 
 
 def bench_step(wl, args, dev) -> int:
@@ -154,6 +283,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mamba1p4b_bf16")
+    ap.add_argument("--pass", dest="which", choices=("forward", "backward"), default="forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 1 GiB device copy (HBM-counter calibration under rocprofv3)")
@@ -173,6 +303,8 @@ def main() -> int:
     torch.cuda.set_device(dev)
     if wl.mode == "step":
         return bench_step(wl, args, dev)
+    if args.which == "backward":
+        return bench_backward(wl, args, dev)
 
     # ---- inputs resident in HBM (generated per token block, seeded)
     def up(t):
@@ -213,10 +345,7 @@ def main() -> int:
     ev_avg = float(durs.mean())
 
     if args.calib_copy:
-        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
+        _calib_copy(dev)
 
     nbytes = algorithmic_bytes(wl, with_state=True)
     updates = wl.elements * wl.dstate
@@ -229,7 +358,7 @@ def main() -> int:
         "peak": PEAK_VALU_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(tflops / PEAK_VALU_TFLOPS, 4),
-        "traffic": recorded_traffic(wl),
+        "traffic": recorded_traffic(f"k_lockstep_{wl.name}_hbm_counters.md", FWD_SOURCES),
         "per_launch": {"updates": updates, "flops_per_update": FLOPS_PER_UPDATE,
                        "algorithmic_bytes": nbytes, "event_avg_us": round(ev_avg * 1e6, 2),
                        "event_min_us": round(float(durs.min()) * 1e6, 2)},

@@ -12,12 +12,12 @@
 //     dB      += lam * gain * x             (summed over channels)
 //     dC      += dy * h_t                   (summed over channels)
 // with dgain/dA = (delta Abar - gain)/A = delta^2 psi(delta A),
-// psi(z) = (z exp(z) - exp(z) + 1)/z^2 (delta^2/2 at A = 0); dh0 = Abar_0 lam_0.  This is the chain
-// rule through the definition of the forward pass ("The loop that beats
-// attention", eqs. (1)-(2)); the pages name the backward pass and its
-// recomputation of the states ("Mamba and State Space Models", the
-// hardware-aware implementation; "Mamba matches the Transformer...", "Fuse
-// the kernel and recompute") without spelling it out.
+// psi(z) = (z exp(z) - exp(z) + 1)/z^2 (delta^2/2 at A = 0), and
+// dh0 = Abar_0 lam_0.  This is the chain rule through the definition of the
+// forward pass ("The loop that beats attention", eqs. (1)-(2)); the pages name
+// the backward pass and its recomputation of the states ("Mamba and State
+// Space Models", the hardware-aware implementation; "Mamba matches the
+// Transformer...", "Fuse the kernel and recompute") without spelling it out.
 //
 // Mapping.  One workgroup of BW waves owns one 64-channel tile (lane = channel,
 // B/C wave-uniform in SGPRs, as in the forward kernels) for the whole
@@ -25,15 +25,19 @@
 //   pass 1, chunks in order: each run is scanned from zero (run 0 from the
 //     chunk's entering state), the runs are composed through LDS with the
 //     associative combine, and the state entering every chunk is saved;
-//   pass 2, chunks in reverse: each run scans its tokens forward (end state)
-//     and backward (adjoint from zero at its right end); the forward
+//   pass 2, chunks in reverse: each run scans its tokens forward from zero
+//     (run 0: from the chunk's entering state), keeping the BT states in
+//     VGPRs, and backward (adjoint from zero at its right end); the forward
 //     aggregates are folded left to right (state entering each run) and the
 //     reverse ones right to left (adjoint entering each run from the right);
-//     every run then recomputes its BT states from its exact entering state,
-//     keeps them in VGPRs, and walks them backwards with its exact adjoint.
+//     every run then adds (decay since its start) x (entering state) to its
+//     kept states, which makes them exact, and walks them backwards with its
+//     exact adjoint.
 // dB/dC are summed over the 64 lanes through LDS and written as one partial
 // per tile; dA/dDskip as one partial per batch row; k_bwd_reduce adds the
 // partials in a fixed order, so the result is deterministic.
+
+#include <type_traits>
 
 #include "sscan_device.h"
 
@@ -55,20 +59,33 @@ __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// ZOH gain (exp(z) - 1)/A for z = dt*A, given abar = exp(z) and 1/A: the
-// Taylor polynomial dt*(1 + z/2 + ... + z^6/7!) for |z| < 1/4 (truncation
-// below 2e-9 relative; no cancellation in abar - 1), the closed form
-// otherwise.  Both are evaluated and one selected: no divergent branch.
-__device__ __forceinline__ float gain_of(float dt, float z, float abar, float a_inv) {
+// A copy of v that the compiler cannot prove equal to v: per-token
+// coefficients are recomputed in each phase instead of being kept live
+// across phases.
+__device__ __forceinline__ float opaque(float v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// Polynomial (expm1(z)/z - 1)/z = 1/2 + z/6 + ... + z^5/7! for |z| < 1/4
+// (truncation below 2e-9 relative).
+__device__ __forceinline__ float phi1m1_over_z(float z) {
     float p = 1.f / 5040.f;
     p = fmaf(p, z, 1.f / 720.f);
     p = fmaf(p, z, 1.f / 120.f);
     p = fmaf(p, z, 1.f / 24.f);
     p = fmaf(p, z, 1.f / 6.f);
-    p = fmaf(p, z, 0.5f);
-    p = fmaf(p, z, 1.f);
+    return fmaf(p, z, 0.5f);
+}
+
+// ZOH gain (exp(z) - 1)/A for z = dt*A, given abar = exp(z) and 1/A: the
+// Taylor polynomial dt*(1 + z/2 + ... + z^6/7!) for |z| < 1/4 (no
+// cancellation in abar - 1), the closed form otherwise.  Both are evaluated
+// and one selected: no divergent branch.
+__device__ __forceinline__ float gain_of(float dt, float z, float abar, float a_inv) {
+    const float series = dt * fmaf(z, phi1m1_over_z(z), 1.f);
     const float direct = (abar - 1.f) * a_inv;
-    return fabsf(z) < 0.25f ? dt * p : direct;
+    return fabsf(z) < 0.25f ? series : direct;
 }
 
 // dgain/dA = (dt*abar - gain)/A for one state, given z = dt*A, abar = exp(z),
@@ -89,66 +106,178 @@ __device__ __forceinline__ float dgain_da(float dt, float z, float abar, float g
     return fabsf(z) < 0.5f ? (dt * dt) * p : direct;
 }
 
-// Per-lane view of the channel's A row.  each(dt, f) calls f(n, Abar, gain,
-// dgain/dA) for n = 0..NT-1 of one token; the coefficients are produced state
-// by state so only the current state's are live (what f leaves unused is
-// dropped by the compiler).
-template <int NT, bool kFast>
-struct Coef {
+// ---------------------------------------------------------------------------
+// Per-token arithmetic, in two policies that share the kernel's structure.
+// Both keep the state in an internal form (`to_state`), compose it with the
+// same run decays, and provide: fwd (one token of the forward update), rev
+// (one token of the local reverse adjoint), correct (add decay x entering
+// state to a state computed from zero) and walk (one token of the gradient).
+//
+// GenMath (any A): the state is h itself; every token needs, per state,
+// Abar = exp(dt*A), the gain and dgain/dA.
+//
+// FastMath (structured-real A: A[d,n] = (n+1) A[d,0], A[d,0] < 0): as in the
+// forward kernels the state is kept scaled, k = alpha*h with alpha = -A[d,0],
+// so that with r = exp(dt*A[d,0]) and w_n = (B_n/(n+1)) x
+//     k_n <- k_n + (1 - r^(n+1)) (w_n - k_n)   (sr_update),
+// and gain_n = g0 s_n/(n+1) with g0 = (1 - r)/alpha, s_n = 1 + r + ... + r^n.
+// The gradient with respect to A uses the identity
+//     A dh/dA = delta dh/ddelta - gain B x
+// (both sides equal delta A Abar h_{t-1} + (delta Abar - gain) B x), which in
+// the scaled variables reads
+//     alpha dh_n/dA_n = (gain_n - delta) w_n + delta k_n,
+// with gain_n - delta = E_n/(n+1),
+//     E_n = sum_{j<=n} (g0 r^j - delta) = E_{n-1} + (g0 - delta) - g0 (1 - r) s_{n-1}:
+// terms of one sign (z < 0 makes g0 < delta and r < 1), so there is no
+// cancellation for any delta and no per-state series.  Likewise
+//     ddelta = sum_n (n+1) lam_n (w_n - k_n),
+//     dx     = D dy + g0 sum_n lam_n s_n B_n/(n+1),
+//     dB_n   = sum over lanes of lam_n g0 s_n x, times 1/(n+1),
+//     dC_n   = sum over lanes of (dy/alpha) k_n,
+//     dA_n   = (sum over tokens of lam_n alpha dh_n/dA_n)/alpha.
+
+// Per-lane view of one wave's [value][lane] reduction buffer.
+struct RedRow {
+    float *p;  // &buf[0][lane]
+    __device__ __forceinline__ void put(int j, float v) const { p[j * kWave] = v; }
+};
+
+template <int NT>
+struct FastMath {
+    float a0, alpha, inv_alpha, a2, inv_a0;
+
+    __device__ void init(const float *A, int64_t d, int N) {
+        a0 = A[d * N];
+        alpha = -a0;
+        inv_alpha = 1.f / alpha;
+        inv_a0 = -inv_alpha;
+        a2 = a0 * kLog2e;
+    }
+    __device__ float to_state(float h) const { return h * alpha; }
+    __device__ float run_decay(int n, float s) const { return exp2_hw(s * (a2 * float(n + 1))); }
+    // scale of the dB partial of state j after the lane sum, and of dA at the end
+    __device__ static float b_scale(int j) { return 1.f / float(j + 1); }
+    __device__ float a_scale() const { return inv_alpha; }
+
+    __device__ __forceinline__ void fwd(float dv, float xv, const float *row, float *k) const {
+        const float r = exp2_hw(dv * a2);
+        sr_update<NT>(r, one_minus_exp(dv * a0, r), xv, row, k, [](int) {});
+    }
+    __device__ __forceinline__ void rev(float dv, float gv, const float *row, float *l) const {
+        const float r = exp2_hw(dv * a2);
+        float pw = r;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            l[n] = pw * fmaf(row[NT + n], gv, l[n]);
+            pw *= r;
+        }
+    }
+    // k += (decay over deltas summing to dsum) * P
+    __device__ __forceinline__ void correct(float dsum, const float *P, float *k) const {
+        const float rho = exp2_hw(dsum * a2);
+        float pw = rho;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            k[n] = fmaf(pw, P[n], k[n]);
+            pw *= rho;
+        }
+    }
+    // One token of the walk: kt = state after the token (kp, the state before,
+    // is not needed here); lc = adjoint carried in from the right, updated to
+    // the one carried further left; dA accumulates; returns dx without D*dy.
+    __device__ __forceinline__ float walk(float dv, float xv, float gv, const float *row,
+                                          const float *kt, const float * /*kp*/, float *lc,
+                                          float *dA, float &ddv, RedRow red) const {
+        const float r = exp2_hw(dv * a2);
+        const float z0 = dv * a0;
+        const float p = phi1m1_over_z(z0);
+        const bool small = fabsf(z0) < 0.25f;
+        const float g0 = small ? dv * fmaf(z0, p, 1.f) : (r - 1.f) * inv_a0;  // (1 - r)/alpha
+        const float d0 = small ? (dv * z0) * p : g0 - dv;                       // g0 - delta
+        const float ngq = -g0 * (g0 * alpha);                                  // -g0 (1 - r)
+        const float qx = g0 * xv, gva = gv * inv_alpha;
+        float pw = r, s = 1.f, sprev = 0.f, E = 0.f, dxa = 0.f, dda = 0.f;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            E = fmaf(ngq, sprev, E + d0);
+            const float l = fmaf(row[NT + n], gv, lc[n]);
+            lc[n] = pw * l;
+            const float ls = l * s;
+            dxa = fmaf(ls, row[n], dxa);
+            red.put(n, ls * qx);
+            red.put(NT + n, gva * kt[n]);
+            const float w = row[n] * xv;
+            dda = fmaf(l * (w - kt[n]), float(n + 1), dda);
+            dA[n] = fmaf(l, fmaf(E * w, 1.f / float(n + 1), dv * kt[n]), dA[n]);
+            sprev = s;
+            s += pw;
+            pw *= r;
+        }
+        ddv = dda;
+        return g0 * dxa;
+    }
+};
+
+template <int NT>
+struct GenMath {
     float a[NT];      // A[d, n] (0 for padded states)
-    float a_inv[NT];  // 1/A[d, n], general path (0 for A = 0, where the series is used)
-    float a0, inv_a0, a2;
+    float a_inv[NT];  // 1/A[d, n] (0 for A = 0, where the series forms are used)
 
     __device__ void init(const float *A, int64_t d, int N) {
 #pragma unroll
-        for (int n = 0; n < NT; ++n) a[n] = (n < N) ? A[d * N + n] : 0.f;
-        a0 = a[0];
-        inv_a0 = 1.f / a0;
-        a2 = a0 * kLog2e;
-        if constexpr (!kFast) {
-#pragma unroll
-            for (int n = 0; n < NT; ++n) a_inv[n] = a[n] != 0.f ? 1.f / a[n] : 0.f;
+        for (int n = 0; n < NT; ++n) {
+            a[n] = (n < N) ? A[d * N + n] : 0.f;
+            a_inv[n] = a[n] != 0.f ? 1.f / a[n] : 0.f;
         }
     }
-
-    template <class F>
-    __device__ __forceinline__ void each(float dt, F &&f) const {
-        if constexpr (kFast) {
-            // A[d,n] = (n+1) A[d,0]: Abar_n = r^(n+1) and, from
-            // 1 - r^(n+1) = (1 - r)(1 + r + ... + r^n), gain_n = gain_0 s_n/(n+1)
-            // with s_n = 1 + r + ... + r^n: no cancellation, one exp per token.
-            const float z0 = dt * a0;
-            const float r = exp2_hw(dt * a2);
-            const float g0 = gain_of(dt, z0, r, inv_a0);
-            float pw = r, s = 1.f;
-#pragma unroll
-            for (int n = 0; n < NT; ++n) {
-                const float rn = 1.f / float(n + 1);
-                const float gain = g0 * s * rn;
-                f(n, pw, gain, dgain_da(dt, z0 * float(n + 1), pw, gain, inv_a0 * rn));
-                s += pw;
-                pw *= r;
-            }
-        } else {
-#pragma unroll
-            for (int n = 0; n < NT; ++n) {
-                const float z = dt * a[n];
-                const float abar = exp2_hw(dt * (a[n] * kLog2e));
-                const float gain = gain_of(dt, z, abar, a_inv[n]);
-                f(n, abar, gain, dgain_da(dt, z, abar, gain, a_inv[n]));
-            }
-        }
-    }
-    // decay of a run whose deltas sum to s, for state n
+    __device__ float to_state(float h) const { return h; }
     __device__ float run_decay(int n, float s) const { return exp2_hw(s * (a[n] * kLog2e)); }
-};
+    __device__ static float b_scale(int) { return 1.f; }
+    __device__ float a_scale() const { return 1.f; }
 
-// A copy of v that the compiler cannot prove equal to v: the coefficients of a
-// token are recomputed in each phase instead of being kept live across phases.
-__device__ __forceinline__ float opaque(float v) {
-    asm volatile("" : "+v"(v));
-    return v;
-}
+    __device__ __forceinline__ void fwd(float dv, float xv, const float *row, float *k) const {
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            const float z = dv * a[n];
+            const float abar = exp2_hw(dv * (a[n] * kLog2e));
+            const float g = gain_of(dv, z, abar, a_inv[n]);
+            k[n] = fmaf(abar, k[n], g * (row[n] * float(n + 1) * xv));
+        }
+    }
+    __device__ __forceinline__ void rev(float dv, float gv, const float *row, float *l) const {
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+            l[n] = exp2_hw(dv * (a[n] * kLog2e)) * fmaf(row[NT + n], gv, l[n]);
+    }
+    __device__ __forceinline__ void correct(float dsum, const float *P, float *k) const {
+#pragma unroll
+        for (int n = 0; n < NT; ++n) k[n] = fmaf(run_decay(n, dsum), P[n], k[n]);
+    }
+    __device__ __forceinline__ float walk(float dv, float xv, float gv, const float *row,
+                                          const float *kt, const float *kp, float *lc, float *dA,
+                                          float &ddv, RedRow red) const {
+        float dxa = 0.f, dda = 0.f;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            const float z = dv * a[n];
+            const float abar = exp2_hw(dv * (a[n] * kLog2e));
+            const float g = gain_of(dv, z, abar, a_inv[n]);
+            const float dg = dgain_da(dv, z, abar, g, a_inv[n]);
+            const float bn = row[n] * float(n + 1);
+            const float bxn = bn * xv;
+            const float l = fmaf(row[NT + n], gv, lc[n]);
+            const float lg = l * g;
+            dxa = fmaf(lg, bn, dxa);
+            dda = fmaf(l, fmaf(a[n], kt[n], bxn), dda);
+            dA[n] = fmaf(l, fmaf(dv * abar, kp[n], dg * bxn), dA[n]);
+            red.put(n, lg * xv);
+            red.put(NT + n, gv * kt[n]);
+            lc[n] = abar * l;
+        }
+        ddv = dda;
+        return dxa;
+    }
+};
 
 template <class IO, int NT, bool kFast>
 __global__ __launch_bounds__(BW *kWave) void k_bwd(
@@ -161,6 +290,7 @@ __global__ __launch_bounds__(BW *kWave) void k_bwd(
     const int *__restrict__ tile_fast, int64_t batch, int64_t L, int64_t dim, int N,
     int64_t tiles_per_batch) {
     using T = typename IO::T;
+    using Math = std::conditional_t<kFast, FastMath<NT>, GenMath<NT>>;
     constexpr int NPW = (NT + BW - 1) / BW;  // states each wave folds
     constexpr int ES = IO::kBytes;
     __shared__ float s_sum[BW][kWave];
@@ -186,28 +316,28 @@ __global__ __launch_bounds__(BW *kWave) void k_bwd(
     const int64_t dbase = dt_ * kWave;
     const bool active = dbase + lane < dim;
     const int64_t d = active ? dbase + lane : dim - 1;
-    Coef<NT, kFast> cf;
-    cf.init(A, d, N);
+    Math m;
+    m.init(A, d, N);
     const float dsk = Dskip ? Dskip[d] : 0.f;
     const float *bcrow = bc + (b * L) * (2 * NT);
     const int64_t nchunks = (L + BCH - 1) / BCH;
     // inactive lanes (channels past dim) read channel dim-1 and use x = dy = 0,
-    // so they add nothing to the dB/dC lane sums
+    // so they add nothing to the dB/dC lane sums; their stores are dropped
     const uint32_t voff = uint32_t(d * ES);
-    const uint32_t voff_st = active ? voff : 0x80000000u;  // past every range: store dropped
+    const uint32_t voff_st = active ? voff : 0x80000000u;  // past every range
     const float amask = active ? 1.f : 0.f;
     const uint32_t rowb = uint32_t(dim * ES);
     auto rsrc_at = [&](const T *base, int64_t t0) {
         return make_rsrc(base + (b * L + t0) * dim, (L - t0) * dim * ES);
     };
     auto ck = [&](int64_t c, int n) -> float & { return ckpt[((c * batch + b) * NT + n) * dim + d]; };
-    // B[t, n] from the staged row (which holds B/(n+1)) and C[t, n]
-    auto Bof = [](const float *row, int n) { return row[n] * float(n + 1); };
+    const RedRow red{&s_red[w][0][lane]};
 
     // ---------------- pass 1: states entering every chunk
     float k[NT];
 #pragma unroll
-    for (int n = 0; n < NT; ++n) k[n] = (w == 0 && h0 && n < N) ? h0[(b * dim + d) * N + n] : 0.f;
+    for (int n = 0; n < NT; ++n)
+        k[n] = (w == 0 && h0 && n < N) ? m.to_state(h0[(b * dim + d) * N + n]) : 0.f;
     for (int64_t c = 0; c < nchunks; ++c) {
         const int64_t t0 = c * BCH + int64_t(w) * BT;
         const rsrc_t rx = rsrc_at(x, t0), rd = rsrc_at(delta, t0);
@@ -231,10 +361,7 @@ __global__ __launch_bounds__(BW *kWave) void k_bwd(
         for (int tau = 0; tau < BT; ++tau) {
             const float xv = amask * IO::cvt(IO::bld(rx, voff, uint32_t(tau) * rowb));
             const float dv = IO::cvt(IO::bld(rd, voff, uint32_t(tau) * rowb));
-            const float *row = bc0 + min(tau, last) * (2 * NT);
-            cf.each(dv, [&](int n, float abar, float gain, float) {
-                k[n] = fmaf(abar, k[n], gain * (Bof(row, n) * xv));
-            });
+            m.fwd(dv, xv, bc0 + min(tau, last) * (2 * NT), k);
             dsum += dv;
         }
         s_sum[w][lane] = dsum;
@@ -246,7 +373,7 @@ __global__ __launch_bounds__(BW *kWave) void k_bwd(
             const int n = w * NPW + i;
             if (n < NT) {
                 float P = s_k[0][n][lane];
-                for (int j = 1; j < BW; ++j) P = fmaf(cf.run_decay(n, s_sum[j][lane]), P, s_k[j][n][lane]);
+                for (int j = 1; j < BW; ++j) P = fmaf(m.run_decay(n, s_sum[j][lane]), P, s_k[j][n][lane]);
                 s_pre[0][n][lane] = P;
             }
         }
@@ -281,33 +408,29 @@ __global__ __launch_bounds__(BW *kWave) void k_bwd(
             gs[tau] = amask * IO::cvt(IO::bld(rg, voff, uint32_t(tau) * rowb));
         }
 
-        // phase A: end state of the run (from the chunk's entering state for
-        // run 0, from zero otherwise) and its adjoint scanned from zero
+        // phase A: the run's states from its entering state (run 0: the chunk's,
+        // exact; other runs: zero, corrected below) and its adjoint from zero
+        float hist[BT + 1][NT];  // hist[0]: entering state, hist[tau+1]: after token tau
+        float dcum[BT];          // delta summed from the run start through token tau
+#pragma unroll
+        for (int n = 0; n < NT; ++n) hist[0][n] = (w == 0) ? ck(c, n) : 0.f;
         float dsum = 0.f;
 #pragma unroll
-        for (int n = 0; n < NT; ++n) k[n] = (w == 0) ? ck(c, n) : 0.f;
-#pragma unroll
         for (int tau = 0; tau < BT; ++tau) {
-            const float *row = bc0 + min(tau, last) * (2 * NT);
-            const float xv = xs[tau];
-            cf.each(opaque(ds[tau]), [&](int n, float abar, float gain, float) {
-                k[n] = fmaf(abar, k[n], gain * (Bof(row, n) * xv));
-            });
+#pragma unroll
+            for (int n = 0; n < NT; ++n) hist[tau + 1][n] = hist[tau][n];
+            m.fwd(opaque(ds[tau]), xs[tau], bc0 + min(tau, last) * (2 * NT), hist[tau + 1]);
             dsum += ds[tau];
+            dcum[tau] = dsum;
         }
         s_sum[w][lane] = dsum;
 #pragma unroll
-        for (int n = 0; n < NT; ++n) s_k[w][n][lane] = k[n];
+        for (int n = 0; n < NT; ++n) s_k[w][n][lane] = hist[BT][n];
 #pragma unroll
-        for (int n = 0; n < NT; ++n) k[n] = 0.f;  // reused as the run's adjoint
+        for (int n = 0; n < NT; ++n) k[n] = 0.f;  // the run's adjoint from zero
 #pragma unroll
-        for (int tau = BT - 1; tau >= 0; --tau) {
-            const float *row = bc0 + min(tau, last) * (2 * NT);
-            const float gv = gs[tau];
-            cf.each(opaque(ds[tau]), [&](int n, float abar, float, float) {
-                k[n] = abar * fmaf(row[NT + n], gv, k[n]);
-            });
-        }
+        for (int tau = BT - 1; tau >= 0; --tau)
+            m.rev(opaque(ds[tau]), gs[tau], bc0 + min(tau, last) * (2 * NT), k);
 #pragma unroll
         for (int n = 0; n < NT; ++n) s_q[w][n][lane] = k[n];
         __syncthreads();
@@ -320,53 +443,37 @@ __global__ __launch_bounds__(BW *kWave) void k_bwd(
                 float P = s_k[0][n][lane];  // run 0 started from the chunk's entering state
                 for (int j = 1; j < BW; ++j) {
                     s_pre[j][n][lane] = P;
-                    P = fmaf(cf.run_decay(n, s_sum[j][lane]), P, s_k[j][n][lane]);
+                    P = fmaf(m.run_decay(n, s_sum[j][lane]), P, s_k[j][n][lane]);
                 }
                 float M = mu[i];
                 for (int j = BW - 1; j >= 1; --j) {
                     s_mu[j][n][lane] = M;
-                    M = fmaf(cf.run_decay(n, s_sum[j][lane]), M, s_q[j][n][lane]);
+                    M = fmaf(m.run_decay(n, s_sum[j][lane]), M, s_q[j][n][lane]);
                 }
                 s_mu[0][n][lane] = M;
-                mu[i] = fmaf(cf.run_decay(n, s_sum[0][lane]), M, s_q[0][n][lane]);
+                mu[i] = fmaf(m.run_decay(n, s_sum[0][lane]), M, s_q[0][n][lane]);
             }
         }
         __syncthreads();
-        // phase B: states of the run from its exact entering state, then the
-        // walk back with the exact adjoint
-        float hist[BT + 1][NT];
         float lc[NT];  // adjoint carried into the token being walked
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-            hist[0][n] = (w == 0) ? ck(c, n) : s_pre[w][n][lane];
-            lc[n] = s_mu[w][n][lane];
+        for (int n = 0; n < NT; ++n) lc[n] = s_mu[w][n][lane];
+        if (w != 0) {
+#pragma unroll
+            for (int n = 0; n < NT; ++n) hist[0][n] = s_pre[w][n][lane];
+#pragma unroll
+            for (int tau = 0; tau < BT; ++tau) m.correct(dcum[tau], hist[0], hist[tau + 1]);
         }
         __syncthreads();  // s_pre/s_mu become the reduction buffer
-#pragma unroll
-        for (int tau = 0; tau < BT; ++tau) {
-            const float *row = bc0 + min(tau, last) * (2 * NT);
-            const float xv = xs[tau];
-            cf.each(opaque(ds[tau]), [&](int n, float abar, float gain, float) {
-                hist[tau + 1][n] = fmaf(abar, hist[tau][n], gain * (Bof(row, n) * xv));
-            });
-        }
+
+        // phase B: walk the run backwards
 #pragma unroll
         for (int tau = BT - 1; tau >= 0; --tau) {
             const float *row = bc0 + min(tau, last) * (2 * NT);
-            const float xv = xs[tau], dv = ds[tau], gv = gs[tau];
-            float dxv = dsk * gv, ddv = 0.f;
-            cf.each(opaque(dv), [&](int n, float abar, float gain, float dgda) {
-                const float bn = Bof(row, n);
-                const float bxn = bn * xv;
-                const float l = fmaf(row[NT + n], gv, lc[n]);  // lam_t
-                const float lg = l * gain;
-                dxv = fmaf(lg, bn, dxv);
-                ddv = fmaf(l, fmaf(cf.a[n], hist[tau + 1][n], bxn), ddv);
-                dA_acc[n] = fmaf(l, fmaf(dv * abar, hist[tau][n], dgda * bxn), dA_acc[n]);
-                s_red[w][n][lane] = lg * xv;                    // dB partial
-                s_red[w][NT + n][lane] = gv * hist[tau + 1][n];  // dC partial
-                lc[n] = abar * l;
-            });
+            const float xv = xs[tau], gv = gs[tau];
+            float ddv;
+            const float dxv = fmaf(dsk, gv, m.walk(opaque(ds[tau]), xv, gv, row, hist[tau + 1],
+                                                   hist[tau], lc, dA_acc, ddv, red));
             dD_acc = fmaf(gv, xv, dD_acc);
             IO::bst(IO::enc(dxv), rdx, voff_st, uint32_t(tau) * rowb);
             IO::bst(IO::enc(ddv), rdd, voff_st, uint32_t(tau) * rowb);
@@ -383,7 +490,8 @@ __global__ __launch_bounds__(BW *kWave) void k_bwd(
             }
             acc += __shfl_xor(acc, 32);
             if (lane < 2 * NT && t0 + tau < L)
-                part_bc[((dt_ * batch + b) * L + t0 + tau) * (2 * NT) + lane] = acc;
+                part_bc[((dt_ * batch + b) * L + t0 + tau) * (2 * NT) + lane] =
+                    lane < NT ? acc * Math::b_scale(lane) : acc;
             wave_sync_lds();
         }
     }
@@ -403,10 +511,11 @@ __global__ __launch_bounds__(BW *kWave) void k_bwd(
     s_sum[w][lane] = dD_acc;
     __syncthreads();
     if (w == 0 && active) {
+        const float as = m.a_scale();
         for (int n = 0; n < NT; ++n) {
             float sacc = 0.f;
             for (int j = 0; j < BW; ++j) sacc += s_k[j][n][lane];
-            part_ad[(b * dim + d) * (NT + 1) + n] = sacc;
+            part_ad[(b * dim + d) * (NT + 1) + n] = sacc * as;
         }
         float sd = 0.f;
         for (int j = 0; j < BW; ++j) sd += s_sum[j][lane];

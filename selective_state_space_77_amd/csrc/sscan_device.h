@@ -38,6 +38,41 @@ __device__ __forceinline__ float zoh_gain(float dt, float a, float z, float abar
     return (abar - 1.f) / a;
 }
 
+// 1 - exp(z) given r = exp(z), without the cancellation of 1 - r near z = 0:
+// -z (1 + z/2 + z^2/6 + ... + z^5/720) for |z| < 1/8 (truncation below 1e-9
+// relative), 1 - r otherwise (there the cancellation costs at most a factor
+// 1/(1 - exp(-1/8)) < 9 on the rounding of r).  Both are evaluated and one
+// selected.
+__device__ __forceinline__ float one_minus_exp(float z, float r) {
+    float p = 1.f / 720.f;
+    p = fmaf(p, z, 1.f / 120.f);
+    p = fmaf(p, z, 1.f / 24.f);
+    p = fmaf(p, z, 1.f / 6.f);
+    p = fmaf(p, z, 0.5f);
+    p = fmaf(p, z, 1.f);
+    return fabsf(z) < 0.125f ? -z * p : 1.f - r;
+}
+
+// Structured-real state update shared by the scan kernels.  With A[d,n] =
+// (n+1) A[d,0], r = exp(delta A[d,0]), the state kept scaled, k = -A[d,0] h, and
+// w_n = (B_n/(n+1)) x, the zero-order-hold step is
+//     k_n <- k_n + (1 - r^(n+1)) (w_n - k_n).
+// 1 - r^(n+1) runs as q_0 = 1 - r, q_n = r q_{n-1} + q_0: terms of one sign,
+// no cancellation.  Each rounding is relative to the state and to the change
+// written into it, never to w_n alone, so small delta*A (a slowly moving
+// state) keeps full precision.  Three VALU operations per state.
+template <int NT, class F>
+__device__ __forceinline__ void sr_update(float r, float q, float xv, const float *brow, float *k,
+                                          F &&after) {
+    float qn = q;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        const float e = fmaf(brow[n], xv, -k[n]);
+        k[n] = fmaf(qn, e, k[n]);
+        after(n);
+        qn = fmaf(qn, r, q);
+    }
+}
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
     // round to nearest even (the gfx950 conversion instruction)

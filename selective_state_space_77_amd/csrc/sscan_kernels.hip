@@ -30,8 +30,9 @@
 // A[d,n] = (n+1)*A[d,0] with A[d,0] < 0, Abar_n = r^(n+1) with
 // r = exp(delta*A[d,0]): one exp per (t,d) instead of N.  The state is kept
 // scaled, k_n = -A[d,0]*h_n, which turns the ZOH update into
-//     k_n <- w_n + Abar_n*(k_n - w_n),   w_n = (B[t,n]/(n+1)) * x
-// (two FMAs and one multiply; it never forms 1 - Abar) and the readout into
+//     k_n <- k_n + (1 - Abar_n)*(w_n - k_n),   w_n = (B[t,n]/(n+1)) * x
+// with 1 - Abar_n built by a positive recurrence from 1 - r (sr_update: two
+// FMAs per state plus one for the recurrence), and the readout into
 // y = (sum_n C_n k_n) / (-A[d,0]) + Dskip*x.  B/(n+1) is staged once per
 // token by k_prep, which also classifies each tile; any other A takes the
 // general path (exp2 and the ZOH gain per state).
@@ -191,15 +192,9 @@ __global__ __launch_bounds__(kWave) void k_seg(
         float yacc = 0.f;
         if constexpr (kFast) {
             const float r = exp2_hw(dv * a2);
-            float pw = r;
-#pragma unroll
-            for (int n = 0; n < NT; ++n) {
-                const float e = fmaf(-row[n], xv, k[n]);
-                const float q = pw * e;
-                k[n] = fmaf(row[n], xv, q);
+            sr_update<NT>(r, one_minus_exp(dv * a[0], r), xv, row, k, [&](int n) {
                 if (kMain) yacc = fmaf(row[NT + n], k[n], yacc);
-                pw *= r;
-            }
+            });
         } else {
 #pragma unroll
             for (int n = 0; n < NT; ++n) {
@@ -370,15 +365,9 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
             cum *= r;
             rho[tau] = cum;
             dsum += dv;
-            float pw = r, yacc = 0.f;
-#pragma unroll
-            for (int n = 0; n < NT; ++n) {
-                const float e = fmaf(-row[n], xv, k[n]);
-                const float q = pw * e;
-                k[n] = fmaf(row[n], xv, q);
-                yacc = fmaf(row[NT + n], k[n], yacc);
-                pw *= r;
-            }
+            float yacc = 0.f;
+            sr_update<NT>(r, one_minus_exp(dv * a0, r), xv, row, k,
+                          [&](int n) { yacc = fmaf(row[NT + n], k[n], yacc); });
             yl[tau] = fmaf(yacc, inv_alpha, dsk * xv);
         };
 #pragma unroll

@@ -131,6 +131,17 @@ def test_large_delta_and_small_delta():
     _check(wl, inp=inp)
 
 
+def test_small_delta_times_A():
+    """delta ~ 1e-3 and A scales down to 1e-4 on the structured-real path: the
+    state moves little per token; gradients keep fp32 precision."""
+    wl = datagen.custom("bwd_slow", 2, 1500, 128, 16, "f32", "s4d_real")
+    inp = datagen.scan_inputs(wl)
+    rng = np.random.default_rng(19)
+    inp["delta"] = (1e-3 * np.exp(0.5 * rng.standard_normal(inp["delta"].shape))).astype(np.float32)
+    inp["A"] = (inp["A"] * np.geomspace(1e-4, 1.0, 128).astype(np.float32)[:, None]).astype(np.float32)
+    _check(wl, inp=inp)
+
+
 def test_mamba130m_width_f32_full():
     _check(datagen.workload("mamba130m_f32"))
 

@@ -197,6 +197,26 @@ def test_s4d_scaled_rows_take_the_fast_path_correctly():
     _check_full(wl, inp=inp)
 
 
+def _slow_memory_inputs(wl, scales):
+    """Small steps (delta ~ 1e-3, the low end of a usual dt range) and per-channel
+    A scales down to 1e-4: delta*A is tiny, each token moves the state very little
+    and the state integrates thousands of tokens.  fp32 must keep full precision
+    there (a formulation whose rounding is relative to B*x rather than to the
+    state loses about two digits)."""
+    inp = datagen.scan_inputs(wl)
+    rng = np.random.default_rng(17)
+    inp["delta"] = (1e-3 * np.exp(0.5 * rng.standard_normal(inp["delta"].shape))).astype(np.float32)
+    inp["A"] = (inp["A"] * scales[:, None]).astype(np.float32)
+    return inp
+
+
+@pytest.mark.parametrize("batch", [1, 256])  # segment kernels / lockstep kernel
+def test_small_delta_times_A_keeps_fp32_precision(batch):
+    wl = datagen.custom("slowmem", batch, 2048 if batch == 1 else 600, 128, 16, "f32", "s4d_real", key=12)
+    scales = np.geomspace(1e-4, 1.0, 128).astype(np.float32)
+    _check_full(wl, inp=_slow_memory_inputs(wl, scales))
+
+
 def test_empty_inputs():
     dev = "cuda"
     x = torch.empty(1, 0, 8, device=dev)
