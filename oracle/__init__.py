@@ -49,6 +49,9 @@ def _load():
         lib.oracle_step.restype = ctypes.c_int
         lib.oracle_backward.argtypes = [dp] * 16 + [i64] * 4 + [ctypes.c_int]
         lib.oracle_backward.restype = ctypes.c_int
+        lib.oracle_frontend.argtypes = [dp, dp, dp, ctypes.c_int, ctypes.c_int, dp, dp, dp, dp, dp, dp,
+                                        i64, i64, i64]
+        lib.oracle_frontend.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -130,3 +133,38 @@ def backward(x, delta, A, B, C, Dskip, dy, h0=None, dhT=None, nthreads: int = 1)
     if rc != 0:
         raise RuntimeError(f"oracle_backward failed ({rc})")
     return out
+
+
+def frontend(xin, conv_w, delta_raw, conv_bias=None, delta_bias=None, act: int = 0,
+             conv_state=None):
+    """fp64 front end: (u, delta, conv_state_out).
+
+    xin, delta_raw: (batch, L, dim); conv_w: (dim, K); conv_bias, delta_bias: (dim,) or None;
+    act: 0 none, 1 SiLU; conv_state: (batch, K-1, dim) inputs before token 0, or None (zeros).
+    u = act(causal depthwise convolution of xin), delta = softplus(delta_raw + delta_bias),
+    conv_state_out = the last K-1 inputs, (batch, K-1, dim)."""
+    xin, conv_w, delta_raw = map(_f64, (xin, conv_w, delta_raw))
+    conv_bias, delta_bias, conv_state = map(_f64, (conv_bias, delta_bias, conv_state))
+    batch, L, dim = xin.shape
+    K = conv_w.shape[1]
+    if delta_raw.shape != xin.shape or conv_w.shape != (dim, K):
+        raise ValueError("inconsistent shapes")
+    if conv_state is not None and conv_state.shape != (batch, K - 1, dim):
+        raise ValueError("conv_state must have shape (batch, K-1, dim)")
+    u = np.empty_like(xin)
+    delta = np.empty_like(xin)
+    cs = np.empty((batch, K - 1, dim))
+    rc = _load().oracle_frontend(_p(xin), _p(conv_w), _p(conv_bias), K, int(act), _p(conv_state),
+                                 _p(delta_raw), _p(delta_bias), _p(u), _p(delta), _p(cs), batch, L, dim)
+    if rc != 0:
+        raise RuntimeError(f"oracle_frontend failed ({rc})")
+    return u, delta, cs
+
+
+def forward_fused(xin, conv_w, delta_raw, A, B, C, Dskip=None, conv_bias=None, delta_bias=None,
+                  act: int = 0, conv_state=None, h0=None, nthreads: int = 1):
+    """The fused entry point's definition: frontend() then forward() on its outputs.
+    Returns (y, final_state, conv_state_out)."""
+    u, delta, cs = frontend(xin, conv_w, delta_raw, conv_bias, delta_bias, act, conv_state)
+    y, hs = forward(u, delta, A, B, C, Dskip, h0=h0, nthreads=nthreads)
+    return y, hs, cs

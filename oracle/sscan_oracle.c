@@ -47,12 +47,18 @@
  * The backward pass (oracle_backward, below) is the chain rule through the same
  * definition.
  *
+ * The front end of the fused entry points (oracle_frontend, below) is the
+ * softplus of the step size and the short causal convolution in front of the
+ * scan.
+ *
  * Pins (tests, not this file): LTI case == explicit and FFT convolution,
  * ZOH step == the ODE solved analytically and by RK4, the 1-D GRU gate,
  * forgetting at large delta, identity at delta = 0, brute-force unrolling,
  * hand-worked exact examples in tests/golden, split-sequence and per-step
  * consistency, linearity and causality; the backward pass by central finite
- * differences of oracle_forward and the transpose identity of the x -> y map.
+ * differences of oracle_forward and the transpose identity of the x -> y map;
+ * the front end by numpy's correlate and logaddexp, impulse responses, the
+ * SiLU reflection identity and streaming in pieces.
  * Every function here is pinned.
  *
  * Threads: channels (b, d) are independent, so `nthreads` workers take
@@ -305,4 +311,71 @@ int oracle_backward(const double *x, const double *delta, const double *A, const
     return ORACLE_OK;
 }
 
-int oracle_version(void) { return 2; }
+/*
+ * Front end that feeds the scan, for the fused entry points.
+ *
+ * Step size ("Mamba and State Space Models", the selective pseudocode;
+ * knowledge-base entry on Mamba, section 3.2, algorithm 2): the projection of
+ * the token plus a bias, made positive by softplus(v) = log(1 + e^v):
+ *     delta[b,t,d] = softplus(delta_raw[b,t,d] + delta_bias[d])
+ * evaluated as max(v,0) + log1p(exp(-|v|)), which is the same function
+ * without overflow.  NULL delta_bias means 0.
+ *
+ * Short convolution in front of the SSM ("Mamba and State Space Models",
+ * "How this shows up in practice", d_conv): causal, per channel, of width K:
+ *     c[b,t,d] = conv_bias[d] + sum_{k=0}^{K-1} w[d,k] * xin[b, t-K+1+k, d]
+ * where inputs before token 0 are the K-1 rows of conv_state (row j is token
+ * j-(K-1)), or zero when conv_state is NULL; NULL conv_bias means 0.  The
+ * pages name no nonlinearity after it: act = 0 leaves c as the scan input,
+ * act = 1 applies SiLU, u = c / (1 + exp(-c)).
+ * conv_state_out (may be NULL) receives the last K-1 inputs (the state a
+ * following call continues from), rows in token order.
+ *
+ * Layouts: xin, delta_raw, u, delta (batch, L, dim); w (dim, K); conv_bias,
+ * delta_bias (dim); conv_state, conv_state_out (batch, K-1, dim).
+ */
+static double softplus(double v) {
+    return (v > 0.0 ? v : 0.0) + log1p(exp(-fabs(v)));
+}
+
+int oracle_frontend(const double *xin, const double *w, const double *conv_bias, int K, int act,
+                    const double *conv_state, const double *delta_raw, const double *delta_bias,
+                    double *u, double *delta, double *conv_state_out, int64_t batch, int64_t L,
+                    int64_t dim) {
+    if (!xin || !w || !delta_raw || !u || !delta || K < 1 || batch < 0 || L < 0 || dim < 0 ||
+        (act != 0 && act != 1))
+        return ORACLE_ERR_ARG;
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t d = 0; d < dim; ++d) {
+            for (int64_t t = 0; t < L; ++t) {
+                double c = conv_bias ? conv_bias[d] : 0.0;
+                for (int k = 0; k < K; ++k) {
+                    const int64_t s = t - (K - 1) + k; /* input token of tap k */
+                    double v;
+                    if (s >= 0)
+                        v = xin[(b * L + s) * dim + d];
+                    else /* row s + K - 1 of the carried inputs */
+                        v = conv_state ? conv_state[(b * (K - 1) + (s + K - 1)) * dim + d] : 0.0;
+                    c += w[d * K + k] * v;
+                }
+                const int64_t e = (b * L + t) * dim + d;
+                u[e] = act == 1 ? c / (1.0 + exp(-c)) : c;
+                delta[e] = softplus(delta_raw[e] + (delta_bias ? delta_bias[d] : 0.0));
+            }
+            if (conv_state_out) {
+                for (int j = 0; j < K - 1; ++j) {
+                    const int64_t s = L - (K - 1) + j; /* token of row j */
+                    double v;
+                    if (s >= 0)
+                        v = xin[(b * L + s) * dim + d];
+                    else
+                        v = conv_state ? conv_state[(b * (K - 1) + (s + K - 1)) * dim + d] : 0.0;
+                    conv_state_out[(b * (K - 1) + j) * dim + d] = v;
+                }
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
+int oracle_version(void) { return 3; }

@@ -429,3 +429,101 @@ def test_backward_threads_do_not_change_the_result():
     g3 = oracle.backward(*args, h0=inp["h0"], dhT=dhT, nthreads=3)
     for k in g1:
         np.testing.assert_array_equal(g1[k], g3[k])
+
+
+# ---------------------------------------------------------------- front end of the fused entry points
+# The short causal convolution in front of the scan ("Mamba and State Space Models",
+# "How this shows up in practice", d_conv) and delta = softplus(raw + bias) (the selective
+# pseudocode).  Pinned against numpy routines and identities, not against its own formula.
+
+def _fe_inputs(rng, batch=2, L=37, dim=5, K=4):
+    return (rng.standard_normal((batch, L, dim)), rng.standard_normal((dim, K)),
+            rng.standard_normal((batch, L, dim)) * 3.0, rng.standard_normal(dim),
+            rng.standard_normal(dim), rng.standard_normal((batch, K - 1, dim)))
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 4])
+def test_frontend_conv_is_numpy_correlate_over_the_carried_inputs(K):
+    rng = np.random.default_rng(40 + K)
+    x, w, dr, cb, db, cs = _fe_inputs(rng, K=K)
+    u, _, cs_out = oracle.frontend(x, w, dr, conv_bias=cb, delta_bias=db, act=0, conv_state=cs)
+    for b in range(x.shape[0]):
+        for d in range(x.shape[2]):
+            seq = np.concatenate([cs[b, :, d], x[b, :, d]])
+            ref = np.correlate(seq, w[d], mode="valid") + cb[d]
+            np.testing.assert_allclose(u[b, :, d], ref, rtol=1e-12, atol=1e-12)
+            np.testing.assert_array_equal(cs_out[b, :, d], seq[len(seq) - (K - 1):] if K > 1 else seq[:0])
+
+
+def test_frontend_impulse_response_is_the_reversed_taps_and_zero_state_means_zeros():
+    K, L, t0 = 4, 12, 5
+    w = np.array([[0.5, -1.0, 2.0, 3.0]])
+    x = np.zeros((1, L, 1)); x[0, t0, 0] = 1.0
+    u, _, _ = oracle.frontend(x, w, np.zeros_like(x))
+    expect = np.zeros(L)
+    for j in range(K):
+        expect[t0 + j] = w[0, K - 1 - j]   # tap K-1 sees the current token
+    np.testing.assert_array_equal(u[0, :, 0], expect)
+    # a unit carried input at row j (token j-(K-1)) reaches token 0 through tap j-... only
+    cs = np.zeros((1, K - 1, 1)); cs[0, K - 2, 0] = 1.0   # the token just before 0
+    u, _, _ = oracle.frontend(np.zeros((1, L, 1)), w, np.zeros((1, L, 1)), conv_state=cs)
+    np.testing.assert_array_equal(u[0, :4, 0], [w[0, K - 2], w[0, K - 3], w[0, K - 4], 0.0])
+
+
+def test_frontend_softplus_is_logaddexp():
+    v = np.concatenate([np.linspace(-60, 60, 241), [0.0, 1e-300, -1e-300, 700.0, -700.0]])
+    dr = v.reshape(1, -1, 1)
+    _, delta, _ = oracle.frontend(np.zeros_like(dr), np.ones((1, 1)), dr)
+    np.testing.assert_allclose(delta[0, :, 0], np.logaddexp(0.0, v), rtol=1e-14, atol=0)
+    assert abs(delta[0, 241, 0] - np.log(2.0)) < 1e-16          # softplus(0) = ln 2
+    # the bias is added before the softplus
+    rng = np.random.default_rng(7)
+    dr = rng.standard_normal((2, 9, 4)); db = rng.standard_normal(4)
+    _, d1, _ = oracle.frontend(np.zeros_like(dr), np.ones((4, 1)), dr, delta_bias=db)
+    np.testing.assert_allclose(d1, np.logaddexp(0.0, dr + db), rtol=1e-14)
+
+
+def test_frontend_silu_reflection_and_zero():
+    """silu(-c) = silu(c) - c (from sigmoid(-c) = 1 - sigmoid(c)); silu(0) = 0."""
+    rng = np.random.default_rng(9)
+    x, w, dr, _, _, cs = _fe_inputs(rng)
+    c, _, _ = oracle.frontend(x, w, dr, act=0, conv_state=cs)
+    up, _, _ = oracle.frontend(x, w, dr, act=1, conv_state=cs)
+    un, _, _ = oracle.frontend(-x, w, dr, act=1, conv_state=-cs)
+    np.testing.assert_allclose(un, up - c, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(up, c / (1.0 + np.exp(-c)), rtol=1e-13)   # against its definition
+    z, _, _ = oracle.frontend(np.zeros_like(x), w, dr, act=1)
+    assert not z.any()
+
+
+def test_frontend_is_causal_and_streams_in_pieces():
+    rng = np.random.default_rng(11)
+    x, w, dr, cb, db, cs = _fe_inputs(rng, L=40)
+    u, dl, cso = oracle.frontend(x, w, dr, cb, db, act=1, conv_state=cs)
+    x2 = x.copy(); x2[:, 23, :] += 1.0
+    u2, _, _ = oracle.frontend(x2, w, dr, cb, db, act=1, conv_state=cs)
+    np.testing.assert_array_equal(u2[:, :23], u[:, :23])
+    assert np.all(u2[:, 23] != u[:, 23])
+    for L1 in (1, 2, 17):   # pieces shorter than the window too
+        ua, da, csa = oracle.frontend(x[:, :L1], w, dr[:, :L1], cb, db, act=1, conv_state=cs)
+        ub, db_, csb = oracle.frontend(x[:, L1:], w, dr[:, L1:], cb, db, act=1, conv_state=csa)
+        np.testing.assert_array_equal(np.concatenate([ua, ub], axis=1), u)
+        np.testing.assert_array_equal(np.concatenate([da, db_], axis=1), dl)
+        np.testing.assert_array_equal(csb, cso)
+
+
+def test_fused_forward_is_frontend_then_scan():
+    rng = np.random.default_rng(13)
+    x, w, dr, cb, db, cs = _fe_inputs(rng, L=30, dim=3)
+    A = -np.exp(rng.uniform(-1, 1, (3, 4)))
+    B, C = rng.standard_normal((2, 30, 4)), rng.standard_normal((2, 30, 4))
+    D = rng.standard_normal(3)
+    y, hs, cso = oracle.forward_fused(x, w, dr, A, B, C, D, cb, db, act=1, conv_state=cs)
+    u = np.empty_like(x)
+    for b in range(2):
+        for d in range(3):
+            c = np.correlate(np.concatenate([cs[b, :, d], x[b, :, d]]), w[d], "valid") + cb[d]
+            u[b, :, d] = c / (1.0 + np.exp(-c))
+    y2, hs2 = oracle.forward(u, np.logaddexp(0.0, dr + db), A, B, C, D)
+    np.testing.assert_allclose(y, y2, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(hs, hs2, rtol=1e-11, atol=1e-12)
