@@ -14,7 +14,9 @@ sample on the host cores.
                     [--pass forward|backward] [--no-cpu-baseline] [--calib-copy]
 
 --pass backward times sscan_backward instead (all seven gradients, the same
-workload, dy and dfinal_state seeded like x).
+workload, dy and dfinal_state seeded like x); --pass fused times
+sscan_forward_fused (d_conv = 4, SiLU, carried inputs and biases) on the same
+workload, x being the convolution's raw input and delta the raw step size.
 """
 from __future__ import annotations
 
@@ -42,6 +44,10 @@ FLOPS_PER_UPDATE = 8           # per (b,t,d,n): 4 FMA: w - k, the state update, 
 # delta*Abar (1), .*h_{t-1} + dgain/dA*Bx (3), dA += lam*. (2), dB term lam*gain*x (1),
 # dC term dy*h_t (1), carry Abar*lam (1)
 FLOPS_PER_UPDATE_BWD = 8 + 19
+# fused front end, per (b,t,d) element: 4 conv taps + bias (8), SiLU (exp, add, reciprocal,
+# multiply: 4), softplus of the biased raw step (add, exp, add, log, multiply, max: 6)
+FLOPS_PER_ELEMENT_FE = 18
+D_CONV = 4
 
 
 CSRC = os.path.join(ROOT, "selective_state_space_77_amd", "csrc")
@@ -224,6 +230,63 @@ def bench_backward(wl, args, dev) -> int:
     return 0
 
 
+def bench_fused(wl, args, dev) -> int:
+    """One step = one sscan_forward_fused call: the causal convolution (d_conv = 4, SiLU) of x
+    and softplus(delta_raw + bias) formed inside the scan kernels, then the scan."""
+    import torch
+
+    import datagen
+    import selective_state_space_77_amd as sscan
+
+    fe = datagen.frontend_inputs(wl, D_CONV)
+    x, B, C = (_upload(wl, t, dev) for t in ("x", "B", "C"))
+    to = (lambda a: torch.from_numpy(datagen.bf16_bits(a).view(np.int16)).to(dev).view(torch.bfloat16)) \
+        if wl.io == "bf16" else (lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev))
+    draw, cs = to(fe["delta_raw"]), to(fe["conv_state"])
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+    cw, cb, db = f32(fe["conv_w"]), f32(fe["conv_b"]), f32(fe["delta_bias"])
+    A = torch.from_numpy(datagen.gen_A(wl)).to(dev)
+    D = torch.from_numpy(datagen.gen_Dskip(wl)).to(dev)
+    y = torch.empty_like(x)
+    hs = torch.empty(wl.batch, wl.dim, wl.dstate, device=dev)
+    cso = torch.empty_like(cs)
+    stream = torch.cuda.current_stream(dev)
+    print(f"[bench] fused {wl.name}: batch={wl.batch} L={wl.seqlen} dim={wl.dim} N={wl.dstate} "
+          f"io={wl.io} d_conv={D_CONV} silu", file=sys.stderr, flush=True)
+    wall, ev_avg, ev_min = _time(
+        lambda: sscan.forward_fused(x, cw, draw, A, B, C, D, conv_bias=cb, delta_bias=db,
+                                    activation="silu", conv_state=cs, y=y, final_state=hs,
+                                    conv_state_out=cso, stream=stream),
+        args.steps, args.warmup, stream)
+    if args.calib_copy:
+        _calib_copy(dev)
+    nbytes = algorithmic_bytes(wl, with_state=True) + wl.dim * (D_CONV + 2) * 4 \
+        + 2 * wl.batch * (D_CONV - 1) * wl.dim * (2 if wl.io == "bf16" else 4)
+    updates = wl.elements * wl.dstate
+    flops = updates * FLOPS_PER_UPDATE + wl.elements * FLOPS_PER_ELEMENT_FE
+    tflops = flops / ev_avg / 1e12
+    gbs = nbytes / ev_avg / 1e9
+    print(json.dumps({
+        "metric": "selective-scan with fused front end: B*L*D elements/s",
+        "value": wl.elements / wall, "unit": "elements/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded; x,B,C~N(0,1), delta_raw=0.5N, conv taps U(+-1/2))",
+        "config": {"workload": wl.name, "pass": "fused", "d_conv": D_CONV, "activation": "silu",
+                   "batch": wl.batch, "seqlen": wl.seqlen, "dim": wl.dim, "dstate": wl.dstate,
+                   "io_dtype": wl.io, "a_init": wl.a_init},
+        "roofline": {"kernel": "k_lockstep<.., FE> (timed: the whole sscan_forward_fused call)",
+                     "bound": "alu", "achieved": round(tflops, 3), "peak": PEAK_VALU_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_VALU_TFLOPS, 4), "traffic": None,
+                     "per_launch": {"updates": updates, "flops": flops, "algorithmic_bytes": nbytes,
+                                    "event_avg_us": round(ev_avg * 1e6, 2),
+                                    "event_min_us": round(ev_min * 1e6, 2)},
+                     "hbm": {"achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": round(gbs / PEAK_HBM_GBS, 4)}},
+        "cpu_baseline": None}), flush=True)
+    return 0
+
+
 def bench_step(wl, args, dev) -> int:
     """Decode workload: one step = one sscan_step over (batch, dim, N) fp32 state in HBM."""
     import torch
@@ -283,7 +346,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mamba1p4b_bf16")
-    ap.add_argument("--pass", dest="which", choices=("forward", "backward"), default="forward")
+    ap.add_argument("--pass", dest="which", choices=("forward", "backward", "fused"), default="forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 1 GiB device copy (HBM-counter calibration under rocprofv3)")
@@ -305,6 +368,8 @@ def main() -> int:
         return bench_step(wl, args, dev)
     if args.which == "backward":
         return bench_backward(wl, args, dev)
+    if args.which == "fused":
+        return bench_fused(wl, args, dev)
 
     # ---- inputs resident in HBM (generated per token block, seeded)
     def up(t):

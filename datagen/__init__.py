@@ -40,7 +40,8 @@ import numpy as np
 TBLK = 256  # tokens per generator block
 
 _TENSOR_IDS = {"x": 1, "delta": 2, "B": 3, "C": 4, "A": 5, "Dskip": 6, "dt_bias": 7,
-               "dy": 8, "h0": 9, "dhT": 10}
+               "dy": 8, "h0": 9, "dhT": 10, "delta_raw": 11, "conv_w": 12, "conv_b": 13,
+               "conv_state": 14}
 
 
 @dataclass(frozen=True)
@@ -150,13 +151,15 @@ def gen_dt_bias(wl: Workload, seed: int = 0) -> np.ndarray:
 
 
 def _width(wl: Workload, tensor: str) -> int:
-    return wl.dim if tensor in ("x", "delta", "dy") else wl.dstate
+    return wl.dim if tensor in ("x", "delta", "dy", "delta_raw") else wl.dstate
 
 
 def _draw(g: np.random.Generator, shape, tensor: str, bias) -> np.ndarray:
     z = g.standard_normal(shape)
     if tensor == "delta":
         return np.logaddexp(0.0, 0.5 * z + bias)  # softplus of the biased draw
+    if tensor == "delta_raw":
+        return 0.5 * z                             # the same draw before bias and softplus
     return z
 
 
@@ -252,3 +255,21 @@ def grad_inputs(wl: Workload, seed: int = 0, threads: int | None = None) -> dict
     standard normal like x, and dhT; plus an initial state h0."""
     return {"dy": gen_seq(wl, "dy", seed=seed, threads=threads),
             "h0": gen_state(wl, "h0", seed), "dhT": gen_state(wl, "dhT", seed)}
+
+
+def frontend_inputs(wl: Workload, d_conv: int, seed: int = 0, threads: int | None = None) -> dict:
+    """Inputs of the fused front end: delta_raw (batch, L, dim) = 0.5 N(0,1) in the I/O
+    dtype's values (with delta_bias below, softplus(delta_raw + delta_bias) has the
+    distribution of the generated delta), delta_bias = the per-channel dt bias (fp32),
+    conv_w (dim, d_conv) and conv_b (dim) ~ U(-1/sqrt(d_conv), 1/sqrt(d_conv)) fp32, and
+    conv_state (batch, d_conv-1, dim) ~ N(0,1) in the I/O dtype's values.  The raw
+    convolution input is gen_seq(wl, "x")."""
+    lim = 1.0 / np.sqrt(d_conv)
+    return {
+        "delta_raw": gen_seq(wl, "delta_raw", seed=seed, threads=threads),
+        "delta_bias": gen_dt_bias(wl, seed).astype(np.float32),
+        "conv_w": _rng(seed, wl, "conv_w").uniform(-lim, lim, (wl.dim, d_conv)).astype(np.float32),
+        "conv_b": _rng(seed, wl, "conv_b").uniform(-lim, lim, wl.dim).astype(np.float32),
+        "conv_state": _to_io(_rng(seed, wl, "conv_state").standard_normal((wl.batch, d_conv - 1, wl.dim)),
+                             wl.io),
+    }

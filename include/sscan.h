@@ -50,6 +50,11 @@ extern "C" {
 
 #define SSCAN_ABI_VERSION 1
 #define SSCAN_MAX_DSTATE 16 /* N = 1 .. 16 */
+#define SSCAN_MAX_DCONV 4   /* front-end convolution width d_conv = 1 .. 4 */
+
+/* Activation after the front-end convolution. */
+#define SSCAN_ACT_NONE 0
+#define SSCAN_ACT_SILU 1
 
 typedef enum { SSCAN_F32 = 0, SSCAN_BF16 = 1 } sscan_dtype;
 
@@ -158,6 +163,62 @@ int sscan_backward(const void *x, const void *delta, const float *A, const void 
                    const float *dfinal_state, void *dx, void *ddelta, float *dA, float *dB,
                    float *dC, float *dDskip, float *dinitial_state, int64_t batch, int64_t seqlen,
                    int64_t dim, int64_t dstate, int io_dtype, void *stream);
+
+/*
+ * Forward pass with the front end fused in: the scan input and the step size are
+ * formed inside the scan kernels from their raw forms, so neither is written to or
+ * read back from memory.  Step size ("Mamba and State Space Models", the selective
+ * pseudocode; knowledge-base entry on Mamba, section 3.2, algorithm 2):
+ *     delta[b,t,d] = softplus(delta_raw[b,t,d] + delta_bias[d]),  softplus(v) = log(1 + e^v)
+ * Scan input: the short causal convolution in front of the SSM ("Mamba and State
+ * Space Models", "How this shows up in practice", d_conv), per channel,
+ *     c[b,t,d] = conv_bias[d] + sum_{k<d_conv} conv_weight[d,k] * x[b, t-d_conv+1+k, d]
+ *     u[b,t,d] = c (activation SSCAN_ACT_NONE) or c / (1 + e^-c) (SSCAN_ACT_SILU),
+ * with the inputs before token 0 taken from conv_state_in.  Then exactly
+ * sscan_forward_from_state on (u, delta): y = C.h + Dskip * u.
+ *
+ *   x              [in]  (batch, seqlen, dim), io_dtype: the convolution's input.
+ *   conv_weight    [in]  (dim, d_conv) fp32 (a depthwise conv1d weight without its
+ *                        middle axis).
+ *   conv_bias      [in]  (dim) fp32, or NULL (0).
+ *   d_conv              1 .. SSCAN_MAX_DCONV.
+ *   activation          SSCAN_ACT_NONE or SSCAN_ACT_SILU.
+ *   conv_state_in  [in]  (batch, d_conv-1, dim), io_dtype: the raw inputs of the
+ *                        d_conv-1 tokens before token 0, oldest first; NULL = zeros.
+ *   delta_raw      [in]  (batch, seqlen, dim), io_dtype.
+ *   delta_bias     [in]  (dim) fp32, or NULL (0).
+ *   A, B, C, Dskip, initial_state, y, final_state: as for sscan_forward_from_state.
+ *   conv_state_out [out] (batch, d_conv-1, dim), io_dtype, or NULL: the raw inputs of
+ *                        the last d_conv-1 tokens (with seqlen < d_conv-1, partly the
+ *                        carried ones), the conv_state_in of a following call or of
+ *                        sscan_step_fused.  Must not overlap conv_state_in or x.
+ * Returns SSCAN_OK or a negative sscan_status (SSCAN_ERR_UNSUPPORTED for a bad
+ * d_conv or activation).
+ */
+int sscan_forward_fused(const void *x, const float *conv_weight, const float *conv_bias, int d_conv,
+                        int activation, const void *conv_state_in, const void *delta_raw,
+                        const float *delta_bias, const float *A, const void *B, const void *C,
+                        const float *Dskip, const float *initial_state, void *y, float *final_state,
+                        void *conv_state_out, int64_t batch, int64_t seqlen, int64_t dim,
+                        int64_t dstate, int io_dtype, void *stream);
+
+/*
+ * One decode step with the front end fused in (the recurrent form of
+ * sscan_forward_fused): x_t and delta_raw_t are the raw token inputs.
+ *
+ *   state          [in/out] as for sscan_step.
+ *   conv_state     [in/out] (batch, d_conv-1, dim), io_dtype: the raw inputs of the
+ *                        d_conv-1 previous tokens, oldest first; shifted by one token
+ *                        in place (x_t appended).  May be NULL only when d_conv == 1.
+ *   x_t, delta_raw_t [in] (batch, dim), io_dtype.
+ *   conv_weight, conv_bias, d_conv, activation, delta_bias: as for sscan_forward_fused.
+ *   A, B_t, C_t, Dskip, y_t, batch, dim, dstate, io_dtype, stream: as for sscan_step.
+ */
+int sscan_step_fused(float *state, void *conv_state, const void *x_t, const float *conv_weight,
+                     const float *conv_bias, int d_conv, int activation, const void *delta_raw_t,
+                     const float *delta_bias, const float *A, const void *B_t, const void *C_t,
+                     const float *Dskip, void *y_t, int64_t batch, int64_t dim, int64_t dstate,
+                     int io_dtype, void *stream);
 
 /* Static text for a status code (never NULL). */
 const char *sscan_status_string(int status);

@@ -7,8 +7,13 @@ package raises.
 
     forward(x, delta, A, B, C, Dskip=None, y=None, final_state=None, stream=None,
             initial_state=None)
+    forward_fused(x, conv_weight, delta_raw, A, B, C, Dskip=None, conv_bias=None, delta_bias=None,
+                  activation=None, conv_state=None, initial_state=None, y=None, final_state=None,
+                  conv_state_out=None, stream=None)
     backward(x, delta, A, B, C, dy, Dskip=None, initial_state=None, dfinal_state=None, ...)
     step(state, x_t, delta_t, A, B_t, C_t, Dskip=None, y_t=None, stream=None)
+    step_fused(state, conv_state, x_t, conv_weight, delta_raw_t, A, B_t, C_t, Dskip=None,
+               conv_bias=None, delta_bias=None, activation=None, y_t=None, stream=None)
 
 Shapes and layouts follow include/sscan.h: x, delta, y (batch, L, dim); B, C
 (batch, L, N); A (dim, N) fp32; Dskip (dim,) fp32; states (batch, dim, N) fp32.
@@ -26,6 +31,8 @@ LIB_PATH = os.path.join(_HERE, "libsscan.so")
 
 F32, BF16 = 0, 1
 MAX_DSTATE = 16
+MAX_DCONV = 4
+ACT = {None: 0, "none": 0, "silu": 1}
 
 STATUS = {0: "SSCAN_OK", -1: "SSCAN_ERR_NULL", -2: "SSCAN_ERR_SHAPE", -3: "SSCAN_ERR_UNSUPPORTED",
           -4: "SSCAN_ERR_ALIAS", -5: "SSCAN_ERR_HIP"}
@@ -51,6 +58,13 @@ def _load() -> ctypes.CDLL:
     lib.sscan_backward.argtypes = [vp, vp, fp, vp, vp, fp, fp, vp, fp, vp, vp, fp, fp, fp, fp, fp,
                                    i64, i64, i64, i64, ctypes.c_int, vp]
     lib.sscan_backward.restype = ctypes.c_int
+    ci = ctypes.c_int
+    lib.sscan_forward_fused.argtypes = [vp, fp, fp, ci, ci, vp, vp, fp, fp, vp, vp, fp, fp, vp, fp, vp,
+                                        i64, i64, i64, i64, ci, vp]
+    lib.sscan_forward_fused.restype = ctypes.c_int
+    lib.sscan_step_fused.argtypes = [fp, vp, vp, fp, fp, ci, ci, vp, fp, fp, vp, vp, fp, vp,
+                                     i64, i64, i64, ci, vp]
+    lib.sscan_step_fused.restype = ctypes.c_int
     lib.sscan_step.argtypes = [fp, vp, vp, fp, vp, vp, fp, vp, i64, i64, i64, ctypes.c_int, vp]
     lib.sscan_step.restype = ctypes.c_int
     lib.sscan_status_string.argtypes = [ctypes.c_int]
@@ -124,6 +138,77 @@ def forward(x, delta, A, B, C, Dskip=None, y=None, final_state=None, stream=None
                                       batch, L, dim, N, io, _stream(stream, x.device))
     _check(rc)
     return y
+
+
+def _act_code(activation) -> int:
+    if activation not in ACT:
+        raise ValueError(f"activation must be None, 'none' or 'silu', not {activation!r}")
+    return ACT[activation]
+
+
+def forward_fused(x, conv_weight, delta_raw, A, B, C, Dskip=None, conv_bias=None, delta_bias=None,
+                  activation=None, conv_state=None, initial_state=None, y=None, final_state=None,
+                  conv_state_out=None, stream=None):
+    """Selective scan with the front end fused: u = act(causal depthwise conv(x)),
+    delta = softplus(delta_raw + delta_bias), then the scan on (u, delta); returns y.
+
+    conv_weight: (dim, d_conv) fp32; conv_state / conv_state_out: (batch, d_conv-1, dim) in
+    x's dtype (the raw inputs before token 0 / of the last d_conv-1 tokens)."""
+    batch, L, dim = x.shape
+    N = A.shape[1]
+    if conv_weight.dim() != 2 or conv_weight.shape[0] != dim:
+        raise ValueError("conv_weight must have shape (dim, d_conv)")
+    K = conv_weight.shape[1]
+    if delta_raw.shape != x.shape or tuple(A.shape) != (dim, N) or B.shape != (batch, L, N) \
+            or C.shape != B.shape:
+        raise ValueError("inconsistent shapes")
+    for t, name, shape in ((Dskip, "Dskip", (dim,)), (conv_bias, "conv_bias", (dim,)),
+                           (delta_bias, "delta_bias", (dim,)),
+                           (conv_state, "conv_state", (batch, K - 1, dim)),
+                           (conv_state_out, "conv_state_out", (batch, K - 1, dim)),
+                           (initial_state, "initial_state", (batch, dim, N)),
+                           (final_state, "final_state", (batch, dim, N))):
+        if t is not None and tuple(t.shape) != shape:
+            raise ValueError(f"{name} must have shape {shape}")
+    if y is None:
+        y = torch.empty_like(x)
+    io = _io_code(x, delta_raw, B, C, y, *(t for t in (conv_state, conv_state_out) if t is not None))
+    rc = lib.sscan_forward_fused(
+        _dev(x, "x"), _dev(conv_weight, "conv_weight", torch.float32),
+        _dev(conv_bias, "conv_bias", torch.float32), K, _act_code(activation),
+        _dev(conv_state, "conv_state"), _dev(delta_raw, "delta_raw"),
+        _dev(delta_bias, "delta_bias", torch.float32), _dev(A, "A", torch.float32), _dev(B, "B"),
+        _dev(C, "C"), _dev(Dskip, "Dskip", torch.float32),
+        _dev(initial_state, "initial_state", torch.float32), _dev(y, "y"),
+        _dev(final_state, "final_state", torch.float32), _dev(conv_state_out, "conv_state_out"),
+        batch, L, dim, N, io, _stream(stream, x.device))
+    _check(rc)
+    return y
+
+
+def step_fused(state, conv_state, x_t, conv_weight, delta_raw_t, A, B_t, C_t, Dskip=None,
+               conv_bias=None, delta_bias=None, activation=None, y_t=None, stream=None):
+    """One decode step with the front end fused; updates `state` and `conv_state`
+    ((batch, d_conv-1, dim), x_t's dtype) in place and returns y_t."""
+    batch, dim, N = state.shape
+    K = conv_weight.shape[1]
+    if x_t.shape != (batch, dim) or delta_raw_t.shape != (batch, dim) or tuple(A.shape) != (dim, N) \
+            or B_t.shape != (batch, N) or C_t.shape != (batch, N) or tuple(conv_weight.shape) != (dim, K):
+        raise ValueError("inconsistent shapes")
+    if conv_state is not None and tuple(conv_state.shape) != (batch, K - 1, dim):
+        raise ValueError("conv_state must have shape (batch, d_conv-1, dim)")
+    if y_t is None:
+        y_t = torch.empty_like(x_t)
+    io = _io_code(x_t, delta_raw_t, B_t, C_t, y_t, *(() if conv_state is None else (conv_state,)))
+    rc = lib.sscan_step_fused(
+        _dev(state, "state", torch.float32), _dev(conv_state, "conv_state"), _dev(x_t, "x_t"),
+        _dev(conv_weight, "conv_weight", torch.float32), _dev(conv_bias, "conv_bias", torch.float32),
+        K, _act_code(activation), _dev(delta_raw_t, "delta_raw_t"),
+        _dev(delta_bias, "delta_bias", torch.float32), _dev(A, "A", torch.float32), _dev(B_t, "B_t"),
+        _dev(C_t, "C_t"), _dev(Dskip, "Dskip", torch.float32), _dev(y_t, "y_t"), batch, dim, N, io,
+        _stream(stream, state.device))
+    _check(rc)
+    return y_t
 
 
 def backward(x, delta, A, B, C, dy, Dskip=None, initial_state=None, dfinal_state=None,

@@ -84,36 +84,59 @@ const char *sscan_status_string(int status) {
     }
 }
 
+// Front end of the fused entry points (d_conv == 0: none).
+struct FrontEnd {
+    const float *conv_weight = nullptr, *conv_bias = nullptr, *delta_bias = nullptr;
+    const void *conv_state_in = nullptr;
+    void *conv_state_out = nullptr;
+    int d_conv = 0, activation = 0;
+};
+
 static int forward_impl(const void *x, const void *delta, const float *A, const void *B,
                         const void *C, const float *Dskip, const float *initial_state, void *y,
                         float *final_state, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
-                        int io_dtype, void *stream) {
+                        int io_dtype, void *stream, const FrontEnd &fe = FrontEnd()) {
     g_last_error[0] = '\0';
     if (io_dtype != SSCAN_F32 && io_dtype != SSCAN_BF16)
         return fail(SSCAN_ERR_UNSUPPORTED, "io_dtype must be SSCAN_F32 or SSCAN_BF16");
     if (dstate < 1 || dstate > SSCAN_MAX_DSTATE)
         return fail(SSCAN_ERR_UNSUPPORTED, "dstate must be in 1..16");
+    const bool fused = fe.d_conv > 0;
+    if (fused && fe.d_conv > SSCAN_MAX_DCONV)
+        return fail(SSCAN_ERR_UNSUPPORTED, "d_conv must be in 1..4");
+    if (fused && fe.activation != SSCAN_ACT_NONE && fe.activation != SSCAN_ACT_SILU)
+        return fail(SSCAN_ERR_UNSUPPORTED, "activation must be SSCAN_ACT_NONE or SSCAN_ACT_SILU");
     const int64_t es = io_dtype == SSCAN_BF16 ? 2 : 4;
-    int64_t bx, bbc, ba, bd, bs, ws_guard;
+    int64_t bx, bbc, ba, bd, bs, ws_guard, bw = 0, bcs = 0;
     if (!nbytes(&bx, es, batch, seqlen, dim) || !nbytes(&bbc, es, batch, seqlen, dstate) ||
         !nbytes(&ba, 4, dim, dstate) || !nbytes(&bd, 4, dim) || !nbytes(&bs, 4, batch, dim, dstate) ||
-        !nbytes(&ws_guard, 2 * 16 * 4, batch, seqlen))
+        !nbytes(&ws_guard, 2 * 16 * 4, batch, seqlen) ||
+        (fused && (!nbytes(&bw, 4, dim, fe.d_conv) || !nbytes(&bcs, es, batch, fe.d_conv - 1, dim))))
         return fail(SSCAN_ERR_SHAPE, "negative size or byte size overflows int64");
-    const Span ins[] = {{x, bx, "x"}, {delta, bx, "delta"}, {A, ba, "A"}, {B, bbc, "B"},
+    const Span ins[] = {{x, bx, "x"}, {delta, bx, fused ? "delta_raw" : "delta"}, {A, ba, "A"}, {B, bbc, "B"},
                         {C, bbc, "C"}, {Dskip, Dskip ? bd : 0, "Dskip"},
-                        {initial_state, initial_state ? bs : 0, "initial_state"}};
-    const Span outs[] = {{y, bx, "y"}, {final_state, final_state ? bs : 0, "final_state"}};
-    const Span req[] = {ins[0], ins[1], ins[2], ins[3], ins[4], outs[0]};
-    int rc = check_ptrs(req, 6);
+                        {initial_state, initial_state ? bs : 0, "initial_state"},
+                        {fe.conv_weight, bw, "conv_weight"},
+                        {fe.conv_bias, fe.conv_bias ? bd : 0, "conv_bias"},
+                        {fe.delta_bias, fe.delta_bias ? bd : 0, "delta_bias"},
+                        {fe.conv_state_in, fe.conv_state_in ? bcs : 0, "conv_state_in"}};
+    const Span outs[] = {{y, bx, "y"}, {final_state, final_state ? bs : 0, "final_state"},
+                         {fe.conv_state_out, fe.conv_state_out ? bcs : 0, "conv_state_out"}};
+    const Span req[] = {ins[0], ins[1], ins[2], ins[3], ins[4], outs[0], ins[7]};
+    int rc = check_ptrs(req, fused ? 7 : 6);
     if (rc) return rc;
-    rc = check_alias(outs, 2, ins, 7);
+    rc = check_alias(outs, 3, ins, 11);
     if (rc) return rc;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
+    sscan::FeArgs fa{};
+    if (fused) fa = {fe.conv_weight, fe.conv_bias, fe.delta_bias, fe.conv_state_in, fe.d_conv, fe.activation};
     if (batch == 0 || dim == 0) return SSCAN_OK;
     if (seqlen == 0) {
-        if (!final_state) return SSCAN_OK;
-        hipError_t e = sscan::launch_copy_or_zero(final_state, initial_state, batch * dim * dstate, s);
+        hipError_t e = hipSuccess;
+        if (final_state) e = sscan::launch_copy_or_zero(final_state, initial_state, batch * dim * dstate, s);
+        if (e == hipSuccess && fused && fe.conv_state_out)
+            e = sscan::launch_conv_tail(x, fa, fe.conv_state_out, batch, 0, dim, io_dtype, s);
         return e == hipSuccess ? SSCAN_OK : fail_hip("state copy launch", e);
     }
 
@@ -121,8 +144,9 @@ static int forward_impl(const void *x, const void *delta, const float *A, const 
     void *ws = nullptr;
     hipError_t e = hipMallocAsync(&ws, plan.ws_bytes, s);
     if (e != hipSuccess) return fail_hip("hipMallocAsync (scratch)", e);
-    sscan::FwdArgs a{x, delta, A, B, C, Dskip, initial_state, y, final_state, batch, seqlen, dim,
-                     int(dstate), io_dtype};
+    sscan::FwdArgs a{x,   delta,  A,           B,      C,   Dskip,         initial_state,
+                     y,   final_state, batch, seqlen, dim, int(dstate), io_dtype,
+                     fa,  fe.conv_state_out};
     e = sscan::launch_forward(a, plan, ws, s);
     const hipError_t ef = hipFreeAsync(ws, s);
     if (e != hipSuccess) return fail_hip("forward launch", e);
@@ -205,31 +229,89 @@ int sscan_backward(const void *x, const void *delta, const float *A, const void 
     return SSCAN_OK;
 }
 
-int sscan_step(float *state, const void *x_t, const void *delta_t, const float *A,
-               const void *B_t, const void *C_t, const float *Dskip, void *y_t, int64_t batch,
-               int64_t dim, int64_t dstate, int io_dtype, void *stream) {
+int sscan_forward_fused(const void *x, const float *conv_weight, const float *conv_bias, int d_conv,
+                        int activation, const void *conv_state_in, const void *delta_raw,
+                        const float *delta_bias, const float *A, const void *B, const void *C,
+                        const float *Dskip, const float *initial_state, void *y, float *final_state,
+                        void *conv_state_out, int64_t batch, int64_t seqlen, int64_t dim,
+                        int64_t dstate, int io_dtype, void *stream) {
+    g_last_error[0] = '\0';
+    if (d_conv < 1) return fail(SSCAN_ERR_UNSUPPORTED, "d_conv must be in 1..4");
+    FrontEnd fe;
+    fe.conv_weight = conv_weight;
+    fe.conv_bias = conv_bias;
+    fe.delta_bias = delta_bias;
+    fe.conv_state_in = conv_state_in;
+    fe.conv_state_out = conv_state_out;
+    fe.d_conv = d_conv;
+    fe.activation = activation;
+    return forward_impl(x, delta_raw, A, B, C, Dskip, initial_state, y, final_state, batch, seqlen, dim,
+                        dstate, io_dtype, stream, fe);
+}
+
+static int step_impl(float *state, const void *x_t, const void *delta_t, const float *A,
+                     const void *B_t, const void *C_t, const float *Dskip, void *y_t, int64_t batch,
+                     int64_t dim, int64_t dstate, int io_dtype, void *stream, const FrontEnd &fe,
+                     void *conv_state) {
     g_last_error[0] = '\0';
     if (io_dtype != SSCAN_F32 && io_dtype != SSCAN_BF16)
         return fail(SSCAN_ERR_UNSUPPORTED, "io_dtype must be SSCAN_F32 or SSCAN_BF16");
     if (dstate < 1 || dstate > SSCAN_MAX_DSTATE)
         return fail(SSCAN_ERR_UNSUPPORTED, "dstate must be in 1..16");
+    const bool fused = fe.d_conv > 0;
+    if (fused && fe.d_conv > SSCAN_MAX_DCONV)
+        return fail(SSCAN_ERR_UNSUPPORTED, "d_conv must be in 1..4");
+    if (fused && fe.activation != SSCAN_ACT_NONE && fe.activation != SSCAN_ACT_SILU)
+        return fail(SSCAN_ERR_UNSUPPORTED, "activation must be SSCAN_ACT_NONE or SSCAN_ACT_SILU");
     const int64_t es = io_dtype == SSCAN_BF16 ? 2 : 4;
-    int64_t bx, bbc, ba, bd, bs;
+    int64_t bx, bbc, ba, bd, bs, bw = 0, bcs = 0;
     if (!nbytes(&bx, es, batch, dim) || !nbytes(&bbc, es, batch, dstate) || !nbytes(&ba, 4, dim, dstate) ||
-        !nbytes(&bd, 4, dim) || !nbytes(&bs, 4, batch, dim, dstate))
+        !nbytes(&bd, 4, dim) || !nbytes(&bs, 4, batch, dim, dstate) ||
+        (fused && (!nbytes(&bw, 4, dim, fe.d_conv) || !nbytes(&bcs, es, batch, fe.d_conv - 1, dim))))
         return fail(SSCAN_ERR_SHAPE, "negative size or byte size overflows int64");
-    const Span ins[] = {{x_t, bx, "x_t"}, {delta_t, bx, "delta_t"}, {A, ba, "A"}, {B_t, bbc, "B_t"},
-                        {C_t, bbc, "C_t"}, {Dskip, Dskip ? bd : 0, "Dskip"}};
-    const Span outs[] = {{state, bs, "state"}, {y_t, bx, "y_t"}};
-    const Span req[] = {ins[0], ins[1], ins[2], ins[3], ins[4], outs[0], outs[1]};
-    int rc = check_ptrs(req, 7);
+    const Span ins[] = {{x_t, bx, "x_t"}, {delta_t, bx, fused ? "delta_raw_t" : "delta_t"}, {A, ba, "A"},
+                        {B_t, bbc, "B_t"}, {C_t, bbc, "C_t"}, {Dskip, Dskip ? bd : 0, "Dskip"},
+                        {fe.conv_weight, bw, "conv_weight"},
+                        {fe.conv_bias, fe.conv_bias ? bd : 0, "conv_bias"},
+                        {fe.delta_bias, fe.delta_bias ? bd : 0, "delta_bias"}};
+    const Span outs[] = {{state, bs, "state"}, {y_t, bx, "y_t"}, {conv_state, bcs, "conv_state"}};
+    const Span req[] = {ins[0], ins[1], ins[2], ins[3], ins[4], outs[0], outs[1], ins[6], outs[2]};
+    int rc = check_ptrs(req, fused ? 9 : 7);
     if (rc) return rc;
-    rc = check_alias(outs, 2, ins, 6);
+    rc = check_alias(outs, 3, ins, 9);
     if (rc) return rc;
     if (batch == 0 || dim == 0) return SSCAN_OK;
     sscan::StepArgs a{state, x_t, delta_t, A, B_t, C_t, Dskip, y_t, batch, dim, int(dstate), io_dtype};
+    if (fused) {
+        a.fe = {fe.conv_weight, fe.conv_bias, fe.delta_bias, conv_state, fe.d_conv, fe.activation};
+        a.conv_state = conv_state;
+    }
     const hipError_t e = sscan::launch_step(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SSCAN_OK : fail_hip("step launch", e);
+}
+
+int sscan_step_fused(float *state, void *conv_state, const void *x_t, const float *conv_weight,
+                     const float *conv_bias, int d_conv, int activation, const void *delta_raw_t,
+                     const float *delta_bias, const float *A, const void *B_t, const void *C_t,
+                     const float *Dskip, void *y_t, int64_t batch, int64_t dim, int64_t dstate,
+                     int io_dtype, void *stream) {
+    g_last_error[0] = '\0';
+    if (d_conv < 1) return fail(SSCAN_ERR_UNSUPPORTED, "d_conv must be in 1..4");
+    FrontEnd fe;
+    fe.conv_weight = conv_weight;
+    fe.conv_bias = conv_bias;
+    fe.delta_bias = delta_bias;
+    fe.d_conv = d_conv;
+    fe.activation = activation;
+    return step_impl(state, x_t, delta_raw_t, A, B_t, C_t, Dskip, y_t, batch, dim, dstate, io_dtype, stream,
+                     fe, conv_state);
+}
+
+int sscan_step(float *state, const void *x_t, const void *delta_t, const float *A,
+               const void *B_t, const void *C_t, const float *Dskip, void *y_t, int64_t batch,
+               int64_t dim, int64_t dstate, int io_dtype, void *stream) {
+    return step_impl(state, x_t, delta_t, A, B_t, C_t, Dskip, y_t, batch, dim, dstate, io_dtype, stream,
+                     FrontEnd(), nullptr);
 }
 
 }  // extern "C"

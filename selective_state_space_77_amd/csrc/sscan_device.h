@@ -74,6 +74,55 @@ __device__ __forceinline__ void sr_update(float r, float q, float xv, const floa
     }
 }
 
+// ---------------------------------------------------------------------------
+// Front end of the fused entry points, one channel per lane.
+constexpr float kLn2 = 0.69314718055994530942f;
+
+// softplus(v) = log(1 + e^v) = max(v, 0) + log1p(e), e = e^-|v| in (0, 1] from the
+// hardware exp2.  log1p(e) is the series e - e^2/2 + e^3/3 - e^4/4 for e < 1/64
+// (truncation below e^4/5 relative, 2e-8) and log2(1 + e) ln 2 otherwise (the
+// rounding of 1 + e then costs at most 2^-24/e <= 2^-18 relative).  Both are
+// evaluated and one selected.
+__device__ __forceinline__ float softplus_f(float v) {
+    const float e = exp2_hw(-fabsf(v) * kLog2e);
+    float p = fmaf(e, -0.25f, 1.f / 3.f);
+    p = fmaf(e, p, -0.5f);
+    p = fmaf(e, p, 1.f);
+    const float lg = __builtin_amdgcn_logf(1.f + e) * kLn2;  // hardware log2
+    return fmaxf(v, 0.f) + (e < 0.015625f ? e * p : lg);
+}
+
+// Per-lane front-end coefficients: the K taps right-aligned in a window of
+// kMaxConv inputs (w3 multiplies the current token, w0 the token 3 before;
+// taps beyond K are 0), the convolution bias and the step-size bias.
+struct FeLane {
+    float w0, w1, w2, w3, cb, db;
+    float silu;  // 1 for SiLU, 0 for none (a blend factor: no branch on it)
+
+    __device__ void init(const FeArgs &fe, int64_t d) {
+        const int K = fe.K;
+        auto tap = [&](int j) {  // window position j (0: t-3 ... 3: t)
+            const int k = j - (kMaxConv - K);
+            return k >= 0 ? fe.conv_w[d * K + k] : 0.f;
+        };
+        w0 = tap(0);
+        w1 = tap(1);
+        w2 = tap(2);
+        w3 = tap(3);
+        cb = fe.conv_b ? fe.conv_b[d] : 0.f;
+        db = fe.delta_bias ? fe.delta_bias[d] : 0.f;
+        silu = fe.act == 1 ? 1.f : 0.f;
+    }
+    // scan input of a token from its raw input x and the raw inputs 1, 2 and 3
+    // tokens before it (sum in the order oldest tap first, bias first)
+    __device__ __forceinline__ float u(float p3, float p2, float p1, float x) const {
+        const float c = fmaf(w3, x, fmaf(w2, p1, fmaf(w1, p2, fmaf(w0, p3, cb))));
+        const float sig = __builtin_amdgcn_rcpf(1.f + exp2_hw(-c * kLog2e));  // sigmoid(c)
+        return c * fmaf(silu, sig - 1.f, 1.f);  // c * sigmoid(c), or c
+    }
+    __device__ __forceinline__ float delta(float raw) const { return softplus_f(raw + db); }
+};
+
 __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
     // round to nearest even (the gfx950 conversion instruction)
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));

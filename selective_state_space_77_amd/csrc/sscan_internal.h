@@ -30,6 +30,20 @@ constexpr int kLockT = SSCAN_LOCK_T;
 constexpr int64_t kLockMinTiles = SSCAN_LOCK_MIN_TILES;
 constexpr int64_t kTargetWaves = SSCAN_TARGET_WAVES;  // segment kernels: waves to aim for
 
+// Front end of the fused entry points: the scan input is the causal depthwise
+// convolution (width K, optional bias, optional SiLU) of x, and the step size
+// is softplus(delta_raw + delta_bias).  K == 0: no front end (x and delta are
+// the scan's inputs as given).
+constexpr int kMaxConv = 4;
+struct FeArgs {
+    const float *conv_w;      // (dim, K) fp32; tap k multiplies x[t - K + 1 + k]
+    const float *conv_b;      // (dim) fp32, or NULL
+    const float *delta_bias;  // (dim) fp32, or NULL
+    const void *conv_state;   // (batch, K-1, dim) I/O dtype: inputs before token 0, or NULL (zero)
+    int K;                    // 0 (no front end) or 1..kMaxConv
+    int act;                  // 0 none, 1 SiLU
+};
+
 // Work split of one forward pass.  Segment kernels cut the sequence into
 // `segments` time segments of `seg_len` tokens (the last may be shorter); each
 // wave scans one segment of 64 channels of one batch row.  The lockstep kernel
@@ -58,6 +72,8 @@ struct FwdArgs {
     int64_t batch, L, dim;
     int N;
     int io;  // 0 fp32, 1 bf16
+    FeArgs fe;             // front end (fe.K == 0: none)
+    void *conv_state_out;  // (batch, K-1, dim) I/O dtype, or NULL; front end only
 };
 
 // Enqueue the forward pass; `ws` points at plan.ws_bytes of device scratch.
@@ -99,6 +115,11 @@ struct BwdArgs {
 
 hipError_t launch_backward(const BwdArgs &a, const BwdPlan &plan, void *ws, hipStream_t s);
 
+// Enqueue conv_state_out[b, j, d] = raw input of token seqlen-(K-1)+j (from x, or
+// from fe.conv_state for tokens before 0, zero when absent); fe.K >= 2.
+hipError_t launch_conv_tail(const void *x, const FeArgs &fe, void *conv_state_out, int64_t batch,
+                            int64_t seqlen, int64_t dim, int io, hipStream_t s);
+
 // Enqueue dst[i] = src ? src[i] : 0 for `count` floats (final_state at seqlen 0).
 hipError_t launch_copy_or_zero(float *dst, const float *src, int64_t count, hipStream_t s);
 
@@ -112,6 +133,8 @@ struct StepArgs {
     int64_t batch, dim;
     int N;
     int io;
+    FeArgs fe;         // front end (fe.K == 0: none); fe.conv_state is read and
+    void *conv_state;  // updated in place through this pointer (same buffer)
 };
 
 hipError_t launch_step(const StepArgs &a, hipStream_t s);

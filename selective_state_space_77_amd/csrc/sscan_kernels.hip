@@ -94,20 +94,62 @@ __global__ __launch_bounds__(256) void k_copy_or_zero(float *__restrict__ dst,
 }
 
 // ----------------------------------------------------------------------------
+// Front end: raw inputs of the three tokens before token ts of batch row b,
+// channel d -- from x for tokens >= 0, from the carried inputs for tokens < 0
+// (row K-1+t of conv_state; zero when it is absent or the row does not exist).
+template <class IO>
+__device__ void fe_prefix(const typename IO::T *x, const FeArgs &fe, int64_t b, int64_t L,
+                          int64_t dim, int64_t d, int64_t ts, float &p3, float &p2, float &p1) {
+    using T = typename IO::T;
+    const T *cs = static_cast<const T *>(fe.conv_state);
+    auto raw = [&](int64_t t) -> float {
+        if (t >= 0) return t < L ? IO::ld(x, (b * L + t) * dim + d) : 0.f;
+        const int64_t r = fe.K - 1 + t;
+        return (cs && r >= 0) ? IO::ld(cs, (b * (fe.K - 1) + r) * dim + d) : 0.f;
+    };
+    p3 = raw(ts - 3);
+    p2 = raw(ts - 2);
+    p1 = raw(ts - 1);
+}
+
+// conv_state_out[b, j, d] = raw input of token L-(K-1)+j: from x, or, for
+// sequences shorter than K-1, from the carried inputs (zero when absent).
+template <class IO>
+__global__ __launch_bounds__(256) void k_conv_tail(const typename IO::T *__restrict__ x,
+                                                   FeArgs fe, typename IO::T *__restrict__ out,
+                                                   int64_t batch, int64_t L, int64_t dim) {
+    using T = typename IO::T;
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t rows = fe.K - 1;
+    if (i >= batch * rows * dim) return;
+    const int64_t d = i % dim;
+    const int64_t j = (i / dim) % rows;
+    const int64_t b = i / (dim * rows);
+    const int64_t t = L - rows + j;
+    const T *cs = static_cast<const T *>(fe.conv_state);
+    T v = T(0);
+    if (t >= 0)
+        v = x[(b * L + t) * dim + d];
+    else if (cs)
+        v = cs[(b * rows + (t + rows)) * dim + d];
+    out[i] = v;
+}
+
+// ----------------------------------------------------------------------------
 // Segment scan: one wave = 64 channels x one time segment.  kMain = false:
 // aggregate pass; kMain = true: carried-state scan with readout.  kFast picks
 // the structured-real (one exp per token) or general (exp and expm1 per state)
 // update; a wave whose tile flag says otherwise exits at once.
 constexpr int kUnroll = 8;  // tokens of x/delta prefetched ahead
 
-template <class IO, int NT, bool kMain, bool kFast>
+template <class IO, int NT, bool kMain, bool kFast, bool FE>
 __global__ __launch_bounds__(kWave) void k_seg(
     const typename IO::T *__restrict__ x, const typename IO::T *__restrict__ delta,
     const float *__restrict__ A, const float *__restrict__ bc, const float *__restrict__ Dskip,
     const float *__restrict__ h0, typename IO::T *__restrict__ y, float *__restrict__ final_state,
     float *__restrict__ agg_sum, float *__restrict__ agg_h, const int *__restrict__ tile_fast,
     int64_t batch, int64_t L, int64_t dim, int N, int64_t seg_len, int segments,
-    int64_t tiles_per_batch, int64_t tiles) {
+    int64_t tiles_per_batch, int64_t tiles, FeArgs fe) {
     using T = typename IO::T;
     const int lane = threadIdx.x;
     const int64_t wid = blockIdx.x;
@@ -186,6 +228,14 @@ __global__ __launch_bounds__(kWave) void k_seg(
     float k[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) k[n] = kFast ? h[n] * alpha : h[n];
+    // front end: per-lane coefficients and the raw inputs of the 3 tokens before
+    // the segment (the convolution window, carried through the token loop)
+    FeLane fl{};
+    float p3 = 0.f, p2 = 0.f, p1 = 0.f;
+    if constexpr (FE) {
+        fl.init(fe, d);
+        fe_prefix<IO>(x, fe, b, L, dim, d, t0, p3, p2, p1);
+    }
 
     // one token: structured-real update on the scaled state, or the general one
     auto token = [&](int tau, float xv, float dv, const float *row) {
@@ -216,8 +266,22 @@ __global__ __launch_bounds__(kWave) void k_seg(
         float xv[U], dv[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            xv[u] = IO::cvt(xr[u]);
-            dv[u] = IO::cvt(dr[u]);
+            if constexpr (FE) {
+                // tokens past the segment would not be neutral after the front end
+                // (softplus(bias) > 0): they are zeroed explicitly
+                // (a 0/1 factor rather than a select, so nothing is branched around)
+                const float xr0 = IO::cvt(xr[u]);
+                const float vm = g0 + u < nseg ? 1.f : 0.f;
+                const float uu = fl.u(p3, p2, p1, xr0);
+                p3 = p2;
+                p2 = p1;
+                p1 = xr0;
+                xv[u] = uu * vm;
+                dv[u] = fl.delta(IO::cvt(dr[u])) * vm;
+            } else {
+                xv[u] = IO::cvt(xr[u]);
+                dv[u] = IO::cvt(dr[u]);
+            }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -279,12 +343,13 @@ __global__ __launch_bounds__(kWave) void k_seg(
 //   3. after a second barrier waves 1..W-1 add the contribution of the state
 //      they entered with, sum_n C_n rho_tau^(n+1) k_in[n], evaluated as a
 //      Horner polynomial in rho_tau, and store y.
-template <class IO, int NT, int W, int TS>
+template <class IO, int NT, int W, int TS, bool FE>
 __global__ __launch_bounds__(W *kWave) void k_lockstep(
     const typename IO::T *__restrict__ x, const typename IO::T *__restrict__ delta,
     const float *__restrict__ A, const float *__restrict__ bc, const float *__restrict__ Dskip,
     const float *__restrict__ h0, typename IO::T *__restrict__ y, float *__restrict__ final_state,
-    const int *__restrict__ tile_fast, int64_t L, int64_t dim, int N, int64_t tiles_per_batch) {
+    const int *__restrict__ tile_fast, int64_t L, int64_t dim, int N, int64_t tiles_per_batch,
+    FeArgs fe) {
     using T = typename IO::T;
     constexpr int U = kUnroll;
     static_assert(TS % U == 0 && U % 2 == 0, "TS must be a multiple of the prefetch group");
@@ -331,6 +396,17 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
     float k[NT];  // wave 0 enters chunk 0 with the state before token 0 (scaled)
 #pragma unroll
     for (int n = 0; n < NT; ++n) k[n] = (w == 0 && h0 && n < N) ? h0[(b * dim + d) * N + n] * alpha : 0.f;
+    // front end: per-lane coefficients; the convolution window (raw inputs of
+    // the 3 tokens before the current one) starts from the tokens before this
+    // wave's first run, and the 3 tokens before its next run are prefetched with
+    // that run's first group
+    FeLane fl{};
+    float p3 = 0.f, p2 = 0.f, p1 = 0.f;
+    T pr[3] = {T(0), T(0), T(0)};
+    if constexpr (FE) {
+        fl.init(fe, d);
+        fe_prefix<IO>(x, fe, b, L, dim, d, int64_t(w) * TS, p3, p2, p1);
+    }
 
     for (int64_t c = 0; c < nchunks; ++c) {
         const int64_t t0 = c * CH + int64_t(w) * TS;
@@ -345,6 +421,13 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
         } else {
 #pragma unroll
             for (int n = 0; n < NT; ++n) k[n] = 0.f;
+        }
+        if constexpr (FE) {
+            if (c > 0) {
+                p3 = IO::cvt(pr[0]);
+                p2 = IO::cvt(pr[1]);
+                p1 = IO::cvt(pr[2]);
+            }
         }
         float yl[TS], rho[TS];
         float cum = 1.f, dsum = 0.f;
@@ -375,8 +458,22 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
             float xv[U], dv[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                xv[u] = IO::cvt(xr[u]);
-                dv[u] = IO::cvt(dr[u]);
+                if constexpr (FE) {
+                    // tokens past the end are not neutral after the front end
+                    // (softplus(bias) > 0): they are zeroed explicitly
+                    // (a 0/1 factor rather than a select, so nothing is branched around)
+                    const float xr0 = IO::cvt(xr[u]);
+                    const float vm = g * U + u < nv ? 1.f : 0.f;
+                    const float uu = fl.u(p3, p2, p1, xr0);
+                    p3 = p2;
+                    p2 = p1;
+                    p1 = xr0;
+                    xv[u] = uu * vm;
+                    dv[u] = fl.delta(IO::cvt(dr[u])) * vm;
+                } else {
+                    xv[u] = IO::cvt(xr[u]);
+                    dv[u] = IO::cvt(dr[u]);
+                }
             }
             // prefetch the next group of this wave's stream: the rest of this run,
             // then the start of its run in the next chunk
@@ -385,6 +482,12 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
             for (int u = 0; u < U; ++u) {
                 xr[u] = IO::bld(rx, voff, (nxt + u) * rowb);
                 dr[u] = IO::bld(rd, voff, (nxt + u) * rowb);
+            }
+            if constexpr (FE) {
+                if (g + 1 == TS / U) {
+#pragma unroll
+                    for (int i = 0; i < 3; ++i) pr[i] = IO::bld(rx, voff, uint32_t(CH - 3 + i) * rowb);
+                }
             }
 #pragma unroll
             for (int u = 0; u < U; u += 2) {
@@ -484,7 +587,10 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
 // (16 B for N = 16), so a wave reads and writes one contiguous 1 KB span of
 // the (batch, dim, N) state.  The partial readouts are summed across the LPC
 // lanes.  Memory bound; per state one hardware exp2 and the gain above.
-template <class IO, int NT, bool kVec>
+// With the front end (FE), x and delta are the raw token inputs: the step
+// reads the K-1 carried raw inputs of its channel from conv_state, forms the
+// convolution and softplus, and shifts conv_state by one token in place.
+template <class IO, int NT, bool kVec, bool FE>
 __global__ __launch_bounds__(256) void k_step(float *__restrict__ state,
                                               const typename IO::T *__restrict__ x,
                                               const typename IO::T *__restrict__ delta,
@@ -493,7 +599,9 @@ __global__ __launch_bounds__(256) void k_step(float *__restrict__ state,
                                               const typename IO::T *__restrict__ C,
                                               const float *__restrict__ Dskip,
                                               typename IO::T *__restrict__ y, int64_t batch,
-                                              int64_t dim, int N) {
+                                              int64_t dim, int N, FeArgs fe,
+                                              typename IO::T *__restrict__ conv_state) {
+    using T = typename IO::T;
     constexpr int SPL = NT < 4 ? NT : 4;
     constexpr int LPC = NT / SPL;
     const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -504,8 +612,30 @@ __global__ __launch_bounds__(256) void k_step(float *__restrict__ state,
     const int64_t c = active ? c0 : chans - 1;
     const int64_t b = c / dim;
     const int64_t d = c - b * dim;
-    const float xv = IO::ld(x, c);
-    const float dt = IO::ld(delta, c);
+    float xv = IO::ld(x, c);
+    float dt = IO::ld(delta, c);
+    if constexpr (FE) {
+        // carried raw inputs of this channel: row r of conv_state is the token
+        // K-1-r before this one
+        const int rows = fe.K - 1;
+        T cr[kMaxConv - 1];
+#pragma unroll
+        for (int r = 0; r < kMaxConv - 1; ++r) cr[r] = r < rows ? conv_state[(b * rows + r) * dim + d] : T(0);
+        auto back = [&](int j) {  // raw input of token t-j (selects: no indexed local array)
+            const int r = rows - j;
+            return r == 0 ? IO::cvt(cr[0]) : r == 1 ? IO::cvt(cr[1]) : r == 2 ? IO::cvt(cr[2]) : 0.f;
+        };
+        FeLane fl;
+        fl.init(fe, d);
+        const T xraw = x[c];
+        xv = fl.u(back(3), back(2), back(1), xv);
+        dt = fl.delta(dt);
+        if (active && q == 0) {
+#pragma unroll
+            for (int r = 0; r < kMaxConv - 1; ++r)
+                if (r < rows) conv_state[(b * rows + r) * dim + d] = r + 1 < rows ? cr[r + 1] : xraw;
+        }
+    }
 
     float h[SPL], av[SPL], bv[SPL], cv[SPL];
     float *sp = state + c * N + q * SPL;
@@ -584,7 +714,12 @@ void prep_io(const void *B, const void *C, const float *A, float *bc, int *flags
     }
 }
 
-template <class IO, int NT>
+// Lockstep workgroup of the fused (front-end) variant: 8 waves, so each lane may
+// hold 256 VGPRs -- room for the convolution window and coefficients without
+// spilling.
+constexpr int kLockWFe = 8;
+
+template <class IO, int NT, bool FE>
 hipError_t forward_t(const FwdArgs &a, const FwdPlan &p, void *ws, hipStream_t s) {
     using T = typename IO::T;
     char *base = static_cast<char *>(ws);
@@ -597,39 +732,42 @@ hipError_t forward_t(const FwdArgs &a, const FwdPlan &p, void *ws, hipStream_t s
     prep_t<IO, NT>(a.B, a.C, a.A, bc, flags, a.batch * a.L, a.dim, a.N, s);
     const dim3 seg_agg(unsigned((p.segments - 1) * p.tiles)), seg_main(unsigned(p.segments * p.tiles));
 #define SSCAN_SEG(MAIN, FAST, GRID)                                                                 \
-    hipLaunchKernelGGL((k_seg<IO, NT, MAIN, FAST>), GRID, dim3(kWave), 0, s, x, dl, a.A, bc, a.Dskip,  \
-                       a.h0, y, a.final_state, agg_sum, agg_h, flags, a.batch, a.L, a.dim, a.N,        \
-                       p.seg_len,                                                                     \
-                       p.segments, p.tiles_per_batch, p.tiles)
+    hipLaunchKernelGGL((k_seg<IO, NT, MAIN, FAST, FE>), GRID, dim3(kWave), 0, s, x, dl, a.A, bc,       \
+                       a.Dskip, a.h0, y, a.final_state, agg_sum, agg_h, flags, a.batch, a.L, a.dim,    \
+                       a.N, p.seg_len, p.segments, p.tiles_per_batch, p.tiles, a.fe)
     // general-A tiles (waves of structured-real tiles exit at once)
     if (p.segments > 1) SSCAN_SEG(false, false, seg_agg);
     SSCAN_SEG(true, false, seg_main);
     // structured-real tiles
     if (p.lockstep) {
-        hipLaunchKernelGGL((k_lockstep<IO, NT, kLockW, kLockT>), dim3(unsigned(p.tiles)),
-                           dim3(kLockW * kWave), 0, s, x, dl, a.A, bc, a.Dskip, a.h0, y, a.final_state,
-                           flags,
-                           a.L, a.dim, a.N, p.tiles_per_batch);
+        constexpr int LW = FE ? kLockWFe : kLockW;
+        hipLaunchKernelGGL((k_lockstep<IO, NT, LW, kLockT, FE>), dim3(unsigned(p.tiles)), dim3(LW * kWave),
+                           0, s, x, dl, a.A, bc, a.Dskip, a.h0, y, a.final_state, flags, a.L, a.dim, a.N,
+                           p.tiles_per_batch, a.fe);
     } else {
         if (p.segments > 1) SSCAN_SEG(false, true, seg_agg);
         SSCAN_SEG(true, true, seg_main);
     }
 #undef SSCAN_SEG
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && FE && a.conv_state_out)
+        e = launch_conv_tail(a.x, a.fe, a.conv_state_out, a.batch, a.L, a.dim, a.io, s);
+    return e;
 }
 
 template <class IO>
 hipError_t forward_io(const FwdArgs &a, const FwdPlan &p, void *ws, hipStream_t s) {
+    const bool fe = a.fe.K > 0;
     switch (p.nt) {
-        case 1: return forward_t<IO, 1>(a, p, ws, s);
-        case 2: return forward_t<IO, 2>(a, p, ws, s);
-        case 4: return forward_t<IO, 4>(a, p, ws, s);
-        case 8: return forward_t<IO, 8>(a, p, ws, s);
-        default: return forward_t<IO, 16>(a, p, ws, s);
+        case 1: return fe ? forward_t<IO, 1, true>(a, p, ws, s) : forward_t<IO, 1, false>(a, p, ws, s);
+        case 2: return fe ? forward_t<IO, 2, true>(a, p, ws, s) : forward_t<IO, 2, false>(a, p, ws, s);
+        case 4: return fe ? forward_t<IO, 4, true>(a, p, ws, s) : forward_t<IO, 4, false>(a, p, ws, s);
+        case 8: return fe ? forward_t<IO, 8, true>(a, p, ws, s) : forward_t<IO, 8, false>(a, p, ws, s);
+        default: return fe ? forward_t<IO, 16, true>(a, p, ws, s) : forward_t<IO, 16, false>(a, p, ws, s);
     }
 }
 
-template <class IO, int NT>
+template <class IO, int NT, bool FE>
 hipError_t step_t(const StepArgs &a, hipStream_t s) {
     using T = typename IO::T;
     constexpr int SPL = NT < 4 ? NT : 4;
@@ -640,27 +778,30 @@ hipError_t step_t(const StepArgs &a, hipStream_t s) {
                      (reinterpret_cast<uintptr_t>(a.A) % 16 == 0);
     if (vec) {
         if constexpr (SPL == 4)
-            hipLaunchKernelGGL((k_step<IO, NT, true>), grid, dim3(256), 0, s, a.state,
+            hipLaunchKernelGGL((k_step<IO, NT, true, FE>), grid, dim3(256), 0, s, a.state,
                                static_cast<const T *>(a.x), static_cast<const T *>(a.delta), a.A,
                                static_cast<const T *>(a.B), static_cast<const T *>(a.C), a.Dskip,
-                               static_cast<T *>(a.y), a.batch, a.dim, a.N);
+                               static_cast<T *>(a.y), a.batch, a.dim, a.N, a.fe,
+                               static_cast<T *>(a.conv_state));
     } else {
-        hipLaunchKernelGGL((k_step<IO, NT, false>), grid, dim3(256), 0, s, a.state,
+        hipLaunchKernelGGL((k_step<IO, NT, false, FE>), grid, dim3(256), 0, s, a.state,
                            static_cast<const T *>(a.x), static_cast<const T *>(a.delta), a.A,
                            static_cast<const T *>(a.B), static_cast<const T *>(a.C), a.Dskip,
-                           static_cast<T *>(a.y), a.batch, a.dim, a.N);
+                           static_cast<T *>(a.y), a.batch, a.dim, a.N, a.fe,
+                           static_cast<T *>(a.conv_state));
     }
     return hipGetLastError();
 }
 
 template <class IO>
 hipError_t step_io(const StepArgs &a, hipStream_t s) {
+    const bool fe = a.fe.K > 0;
     switch (round_nt(a.N)) {
-        case 1: return step_t<IO, 1>(a, s);
-        case 2: return step_t<IO, 2>(a, s);
-        case 4: return step_t<IO, 4>(a, s);
-        case 8: return step_t<IO, 8>(a, s);
-        default: return step_t<IO, 16>(a, s);
+        case 1: return fe ? step_t<IO, 1, true>(a, s) : step_t<IO, 1, false>(a, s);
+        case 2: return fe ? step_t<IO, 2, true>(a, s) : step_t<IO, 2, false>(a, s);
+        case 4: return fe ? step_t<IO, 4, true>(a, s) : step_t<IO, 4, false>(a, s);
+        case 8: return fe ? step_t<IO, 8, true>(a, s) : step_t<IO, 8, false>(a, s);
+        default: return fe ? step_t<IO, 16, true>(a, s) : step_t<IO, 16, false>(a, s);
     }
 }
 
@@ -706,6 +847,20 @@ hipError_t launch_prep(const void *B, const void *C, const float *A, float *bc, 
         prep_io<IoBF16>(B, C, A, bc, tile_fast, rows, dim, N, nt, s);
     else
         prep_io<IoF32>(B, C, A, bc, tile_fast, rows, dim, N, nt, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_conv_tail(const void *x, const FeArgs &fe, void *conv_state_out, int64_t batch,
+                            int64_t seqlen, int64_t dim, int io, hipStream_t s) {
+    const int64_t n = batch * (fe.K - 1) * dim;
+    if (n <= 0) return hipSuccess;
+    const dim3 grid(unsigned((n + 255) / 256));
+    if (io == 1)
+        hipLaunchKernelGGL((k_conv_tail<IoBF16>), grid, dim3(256), 0, s, static_cast<const uint16_t *>(x), fe,
+                           static_cast<uint16_t *>(conv_state_out), batch, seqlen, dim);
+    else
+        hipLaunchKernelGGL((k_conv_tail<IoF32>), grid, dim3(256), 0, s, static_cast<const float *>(x), fe,
+                           static_cast<float *>(conv_state_out), batch, seqlen, dim);
     return hipGetLastError();
 }
 

@@ -38,9 +38,8 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     assert _declared() == ["sscan_backward", "sscan_forward", "sscan_forward_from_state",
-                           "sscan_last_error",
-                           "sscan_status_string", "sscan_step",
-                           "sscan_version"]
+                           "sscan_forward_fused", "sscan_last_error", "sscan_status_string",
+                           "sscan_step", "sscan_step_fused", "sscan_version"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -134,6 +133,53 @@ def test_backward_validation(lib):
     # dB/dC are fp32 whatever io_dtype is: with bf16 inputs (B: 24 bytes) a dC 32
     # bytes after dB still overlaps it
     assert _bwd(lib, io=1, dC=0xB020) == -4
+
+
+def _fwd_fused(lib, **kw):
+    a = dict(x=0x1000, w=0x20000, cb=None, K=4, act=0, csi=None, dr=0x2000, db=None, A=0x3000,
+             B=0x4000, C=0x5000, D=None, h0=None, y=0x6000, hs=None, cso=None,
+             batch=1, L=4, dim=2, N=3, io=0)
+    a.update(kw)
+    return lib.sscan_forward_fused(a["x"], a["w"], a["cb"], a["K"], a["act"], a["csi"], a["dr"], a["db"],
+                                   a["A"], a["B"], a["C"], a["D"], a["h0"], a["y"], a["hs"], a["cso"],
+                                   a["batch"], a["L"], a["dim"], a["N"], a["io"], None)
+
+
+def test_forward_fused_validation(lib):
+    assert _fwd_fused(lib, K=0) == -3
+    assert _fwd_fused(lib, K=5) == -3
+    assert _fwd_fused(lib, act=2) == -3
+    assert _fwd_fused(lib, w=None) == -1
+    assert _fwd_fused(lib, dr=None) == -1
+    assert _fwd_fused(lib, batch=-1) == -2
+    assert _fwd_fused(lib, cso=0x1004) == -4                 # conv_state_out overlaps x
+    assert _fwd_fused(lib, csi=0x30000, cso=0x30008) == -4   # conv_state_out overlaps conv_state_in
+    assert b"conv_state_out" in lib.sscan_last_error()
+    assert _fwd_fused(lib, y=0x20004) == -4                  # y overlaps conv_weight (2 x 4 fp32)
+    assert _fwd_fused(lib, cso=0x20010) == -4                # conv_state_out overlaps conv_weight
+    # K = 1 has no carried inputs: conv_state pointers may then be anything disjoint
+    assert _fwd_fused(lib, K=1, y=None) == -1
+
+
+def _step_fused(lib, **kw):
+    a = dict(st=0x10000, cs=0x40000, x=0x1000, w=0x20000, cb=None, K=4, act=1, dr=0x2000, db=None,
+             A=0x3000, B=0x4000, C=0x5000, D=None, y=0x6000, batch=2, dim=3, N=4, io=1)
+    a.update(kw)
+    return lib.sscan_step_fused(a["st"], a["cs"], a["x"], a["w"], a["cb"], a["K"], a["act"], a["dr"],
+                                a["db"], a["A"], a["B"], a["C"], a["D"], a["y"], a["batch"], a["dim"],
+                                a["N"], a["io"], None)
+
+
+def test_step_fused_validation(lib):
+    assert _step_fused(lib, cs=None) == -1           # d_conv > 1 needs the carried inputs
+    assert _step_fused(lib, w=None) == -1
+    assert _step_fused(lib, K=0) == -3
+    assert _step_fused(lib, K=9) == -3
+    assert _step_fused(lib, act=-1) == -3
+    assert _step_fused(lib, cs=0x10010) == -4        # conv_state overlaps state
+    assert _step_fused(lib, cs=0x2002) == -4         # conv_state overlaps delta_raw_t
+    assert b"conv_state" in lib.sscan_last_error()
+    assert _step_fused(lib, batch=0, st=None, cs=None, x=None, dr=None, B=None, C=None, y=None) == 0
 
 
 def _step(lib, **kw):
