@@ -52,6 +52,8 @@ def _load():
         lib.oracle_frontend.argtypes = [dp, dp, dp, ctypes.c_int, ctypes.c_int, dp, dp, dp, dp, dp, dp,
                                         i64, i64, i64]
         lib.oracle_frontend.restype = ctypes.c_int
+        lib.oracle_ssd_forward.argtypes = [dp] * 9 + [i64] * 6
+        lib.oracle_ssd_forward.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -168,3 +170,29 @@ def forward_fused(xin, conv_w, delta_raw, A, B, C, Dskip=None, conv_bias=None, d
     u, delta, cs = frontend(xin, conv_w, delta_raw, conv_bias, delta_bias, act, conv_state)
     y, hs = forward(u, delta, A, B, C, Dskip, h0=h0, nthreads=nthreads)
     return y, hs, cs
+
+
+def ssd_forward(x, delta, A, B, C, D=None, h0=None, want_state: bool = True):
+    """fp64 scalar-A-per-head scan (Mamba-2's SSM).
+
+    x: (batch, L, H, P); delta: (batch, L, H); A: (H,); B, C: (batch, L, G, N) with G | H;
+    D: (H,) or None; h0: (batch, H, P, N) or None.  Returns (y (batch, L, H, P), final state
+    (batch, H, P, N) or None)."""
+    x, delta, A, B, C = map(_f64, (x, delta, A, B, C))
+    D, h0 = _f64(D), _f64(h0)
+    batch, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if delta.shape != (batch, L, H) or A.shape != (H,) or B.shape != (batch, L, G, N) \
+            or C.shape != B.shape or H % G:
+        raise ValueError("inconsistent shapes")
+    if D is not None and D.shape != (H,):
+        raise ValueError("D must have shape (H,)")
+    if h0 is not None and h0.shape != (batch, H, P, N):
+        raise ValueError("h0 must have shape (batch, H, P, N)")
+    y = np.empty_like(x)
+    hT = np.empty((batch, H, P, N)) if want_state else None
+    rc = _load().oracle_ssd_forward(_p(x), _p(delta), _p(A), _p(B), _p(C), _p(D), _p(h0), _p(y), _p(hT),
+                                    batch, L, H, P, G, N)
+    if rc != 0:
+        raise RuntimeError(f"oracle_ssd_forward failed ({rc})")
+    return y, hT

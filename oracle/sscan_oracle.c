@@ -58,7 +58,9 @@
  * consistency, linearity and causality; the backward pass by central finite
  * differences of oracle_forward and the transpose identity of the x -> y map;
  * the front end by numpy's correlate and logaddexp, impulse responses, the
- * SiLU reflection identity and streaming in pieces.
+ * SiLU reflection identity and streaming in pieces; the scalar-A-per-head
+ * variant by the per-channel forward with A[d,n] = A_h and by its dense
+ * lower-triangular (semiseparable) matrix form built in numpy.
  * Every function here is pinned.
  *
  * Threads: channels (b, d) are independent, so `nthreads` workers take
@@ -378,4 +380,60 @@ int oracle_frontend(const double *xin, const double *w, const double *conv_bias,
     return ORACLE_OK;
 }
 
-int oracle_version(void) { return 3; }
+/*
+ * Scalar-A-per-head variant (Mamba-2's state space model: "Mamba and State
+ * Space Models" and "Mamba matches the Transformer...", the section on the
+ * state space duality).  The same zero-order-hold recurrence as above with
+ * A[d,n] = A_h for every state n and every channel p of head h, delta
+ * per (b, t, h), and B, C per (b, t, group), shared by the heads of a group
+ * (head h reads group h / (H/G)):
+ *     abar = exp(delta[b,t,h] * A_h)
+ *     gain = expm1(delta * A_h) / A_h          (delta when A_h == 0)
+ *     h[p][n] = abar * h[p][n] + gain * B[b,t,g,n] * x[b,t,h,p]
+ *     y[b,t,h,p] = sum over n (ascending) of C[b,t,g,n] * h[p][n] + D[h] * x[b,t,h,p]
+ * Layouts (row-major): x, y (batch, L, H, P); delta (batch, L, H); A, D (H);
+ * B, C (batch, L, G, N); h0, hT (batch, H, P, N).  NULL D means 0, NULL h0
+ * zero, NULL hT not written.  Written as its own loop (not through token()),
+ * so that the two can be checked against each other.
+ */
+int oracle_ssd_forward(const double *x, const double *delta, const double *A, const double *B,
+                       const double *C, const double *D, const double *h0, double *y, double *hT,
+                       int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N) {
+    if (!x || !delta || !A || !B || !C || !y || batch < 0 || L < 0 || H < 1 || P < 1 || G < 1 ||
+        N < 1 || H % G != 0)
+        return ORACLE_ERR_ARG;
+    double *st = (double *)malloc((size_t)N * sizeof(double));
+    if (!st) return ORACLE_ERR_ARG;
+    const int64_t hpg = H / G;
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t h = 0; h < H; ++h) {
+            const int64_t g = h / hpg;
+            const double a = A[h];
+            const double dsk = D ? D[h] : 0.0;
+            for (int64_t p = 0; p < P; ++p) {
+                const int64_t so = ((b * H + h) * P + p) * N; /* state row of (b, h, p) */
+                for (int64_t n = 0; n < N; ++n) st[n] = h0 ? h0[so + n] : 0.0;
+                for (int64_t t = 0; t < L; ++t) {
+                    const double dt = delta[(b * L + t) * H + h];
+                    const double abar = exp(dt * a);
+                    const double gain = (a != 0.0) ? expm1(dt * a) / a : dt;
+                    const double xv = x[((b * L + t) * H + h) * P + p];
+                    const double *Bt = B + ((b * L + t) * G + g) * N;
+                    const double *Ct = C + ((b * L + t) * G + g) * N;
+                    double acc = 0.0;
+                    for (int64_t n = 0; n < N; ++n) {
+                        st[n] = abar * st[n] + gain * Bt[n] * xv;
+                        acc += Ct[n] * st[n];
+                    }
+                    y[((b * L + t) * H + h) * P + p] = acc + dsk * xv;
+                }
+                if (hT)
+                    for (int64_t n = 0; n < N; ++n) hT[so + n] = st[n];
+            }
+        }
+    }
+    free(st);
+    return ORACLE_OK;
+}
+
+int oracle_version(void) { return 4; }

@@ -527,3 +527,94 @@ def test_fused_forward_is_frontend_then_scan():
     y2, hs2 = oracle.forward(u, np.logaddexp(0.0, dr + db), A, B, C, D)
     np.testing.assert_allclose(y, y2, rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(hs, hs2, rtol=1e-11, atol=1e-12)
+
+
+# ---------------------------------------------------------------- scalar A per head (Mamba-2's SSM)
+# The state space duality ("Mamba and State Space Models"; "Mamba matches the Transformer...",
+# the duality section): with A a scalar per head the selective SSM is a lower-triangular,
+# structured (semiseparable) matrix applied to x -- a masked "attention" whose score for
+# (t, s) is C_t.B_s times the decay between s and t.
+
+def _ssd_inputs(rng, batch=2, L=23, H=4, P=3, G=2, N=5, A_zero_head=False):
+    x = rng.standard_normal((batch, L, H, P))
+    delta = np.exp(rng.standard_normal((batch, L, H)) - 1.0)
+    A = -np.exp(rng.standard_normal(H))
+    if A_zero_head:
+        A[1] = 0.0
+    B = rng.standard_normal((batch, L, G, N))
+    C = rng.standard_normal((batch, L, G, N))
+    D = rng.standard_normal(H)
+    return x, delta, A, B, C, D
+
+
+def _ssd_dense(x, delta, A, B, C, D, h0=None):
+    """y = M x + D x with M[t,s] = (C_t . B_s) exp(A (cum_t - cum_s)) gain_s for s <= t,
+    cum the inclusive running sum of delta, gain_s = expm1(delta_s A)/A (delta_s at A = 0);
+    plus, from an initial state, C_t . h0 exp(A cum_t)."""
+    batch, L, H, P = x.shape
+    G = B.shape[2]
+    y = np.empty_like(x)
+    for b in range(batch):
+        for h in range(H):
+            g = h // (H // G)
+            a = A[h]
+            cum = np.cumsum(delta[b, :, h])
+            gain = np.expm1(delta[b, :, h] * a) / a if a != 0 else delta[b, :, h]
+            score = C[b, :, g] @ B[b, :, g].T                       # (L, L): C_t . B_s
+            decay = np.exp(a * (cum[:, None] - cum[None, :]))
+            M = np.tril(score * decay) * gain[None, :]
+            y[b, :, h] = M @ x[b, :, h] + D[h] * x[b, :, h]
+            if h0 is not None:
+                y[b, :, h] += (C[b, :, g] @ h0[b, h].T) * np.exp(a * cum)[:, None]
+    return y
+
+
+@pytest.mark.parametrize("zero", [False, True])
+def test_ssd_is_the_dense_semiseparable_matrix(zero):
+    rng = np.random.default_rng(50 + zero)
+    x, delta, A, B, C, D = _ssd_inputs(rng, A_zero_head=zero)
+    y, _ = oracle.ssd_forward(x, delta, A, B, C, D)
+    np.testing.assert_allclose(y, _ssd_dense(x, delta, A, B, C, D), rtol=1e-9, atol=1e-10)
+    h0 = rng.standard_normal((2, 4, 3, 5))
+    y, _ = oracle.ssd_forward(x, delta, A, B, C, D, h0=h0)
+    np.testing.assert_allclose(y, _ssd_dense(x, delta, A, B, C, D, h0), rtol=1e-9, atol=1e-10)
+
+
+def test_ssd_is_the_per_channel_scan_with_a_repeated_A():
+    """One group: every (head, channel) is a channel of the per-channel scan whose A row is
+    A_h repeated over the states and whose delta is the head's."""
+    rng = np.random.default_rng(52)
+    x, delta, A, B, C, D = _ssd_inputs(rng, G=1)
+    batch, L, H, P = x.shape
+    N = B.shape[3]
+    h0 = rng.standard_normal((batch, H, P, N))
+    y, hT = oracle.ssd_forward(x, delta, A, B, C, D, h0=h0)
+    y2, hT2 = oracle.forward(x.reshape(batch, L, H * P), np.repeat(delta, P, axis=2),
+                             np.repeat(A, P)[:, None] * np.ones((1, N)), B[:, :, 0], C[:, :, 0],
+                             np.repeat(D, P), h0=h0.reshape(batch, H * P, N))
+    np.testing.assert_allclose(y.reshape(batch, L, H * P), y2, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(hT.reshape(batch, H * P, N), hT2, rtol=1e-12, atol=1e-13)
+
+
+def test_ssd_groups_share_B_and_C():
+    rng = np.random.default_rng(53)
+    x, delta, A, B, C, D = _ssd_inputs(rng, H=4, G=2)
+    y, _ = oracle.ssd_forward(x, delta, A, B, C, D)
+    # the same problem with one group per head, B/C replicated to each head of the group
+    y1, _ = oracle.ssd_forward(x, delta, A, np.repeat(B, 2, axis=2), np.repeat(C, 2, axis=2), D)
+    np.testing.assert_array_equal(y, y1)
+    # a head reads only its own group: changing group 1 leaves heads 0-1 unchanged
+    B2 = B.copy(); B2[:, :, 1] += 1.0
+    y2, _ = oracle.ssd_forward(x, delta, A, B2, C, D)
+    np.testing.assert_array_equal(y2[:, :, :2], y[:, :, :2])
+    assert np.abs(y2[:, :, 2:] - y[:, :, 2:]).max() > 1e-3
+
+
+def test_ssd_resumes_from_its_state():
+    rng = np.random.default_rng(54)
+    x, delta, A, B, C, D = _ssd_inputs(rng, L=30)
+    y, hT = oracle.ssd_forward(x, delta, A, B, C, D)
+    ya, ha = oracle.ssd_forward(x[:, :11], delta[:, :11], A, B[:, :11], C[:, :11], D)
+    yb, hb = oracle.ssd_forward(x[:, 11:], delta[:, 11:], A, B[:, 11:], C[:, 11:], D, h0=ha)
+    np.testing.assert_allclose(np.concatenate([ya, yb], axis=1), y, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(hb, hT, rtol=1e-12, atol=1e-13)
