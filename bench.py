@@ -48,6 +48,7 @@ FLOPS_PER_UPDATE_BWD = 8 + 19
 # multiply: 4), softplus of the biased raw step (add, exp, add, log, multiply, max: 6)
 FLOPS_PER_ELEMENT_FE = 18
 D_CONV = 4
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak, published
 
 
 CSRC = os.path.join(ROOT, "selective_state_space_77_amd", "csrc")
@@ -287,6 +288,59 @@ def bench_fused(wl, args, dev) -> int:
     return 0
 
 
+def bench_ssd(wl, args, dev) -> int:
+    """Scalar-A-per-head scan (Mamba-2 shape): one step = one sscan_ssd_forward over the whole
+    workload (chunked matrix form, products on the matrix cores), inputs resident in HBM."""
+    import torch
+
+    import datagen
+    import selective_state_space_77_amd as sscan
+
+    inp = datagen.ssd_inputs(wl)
+    to = (lambda a: torch.from_numpy(datagen.bf16_bits(a).view(np.int16)).to(dev).view(torch.bfloat16)) \
+        if wl.io == "bf16" else (lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev))
+    x, delta, B, C = (to(inp[k]) for k in ("x", "delta", "B", "C"))
+    A, D = torch.from_numpy(inp["A"]).to(dev), torch.from_numpy(inp["D"]).to(dev)
+    y = torch.empty_like(x)
+    hs = torch.empty(wl.batch, wl.nheads, wl.headdim, wl.dstate, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    print(f"[bench] ssd {wl.name}: batch={wl.batch} L={wl.seqlen} heads={wl.nheads} P={wl.headdim} "
+          f"groups={wl.ngroups} N={wl.dstate} io={wl.io}", file=sys.stderr, flush=True)
+    wall, ev_avg, ev_min = _time(
+        lambda: sscan.ssd_forward(x, delta, A, B, C, D, y=y, final_state=hs, stream=stream),
+        args.steps, args.warmup, stream)
+    if args.calib_copy:
+        _calib_copy(dev)
+    es = 2 if wl.io == "bf16" else 4
+    BL = wl.batch * wl.seqlen
+    nbytes = (2 * wl.elements * es + BL * wl.nheads * es + 2 * BL * wl.ngroups * wl.dstate * es
+              + 2 * wl.nheads * 4 + wl.batch * wl.nheads * wl.headdim * wl.dstate * 4)
+    # algorithmic matrix flops per (token, head) of the chunked form with 64-token chunks:
+    # scores C B^T over the causal half (incl. diagonal), scores x X, C S_in, B^T (w X)
+    Q = 64
+    per_tok = 2 * (Q + 1) / 2 * (wl.dstate + wl.headdim) + 2 * 2 * wl.dstate * wl.headdim
+    flops = per_tok * BL * wl.nheads
+    gbs = nbytes / ev_avg / 1e9
+    tflops = flops / ev_avg / 1e12
+    print(json.dumps({
+        "metric": "scalar-A-per-head scan (Mamba-2 SSM): B*L*H*P elements/s",
+        "value": wl.elements / wall, "unit": "elements/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if wl.io == "bf16" else "f32",
+        "data": "synthetic (seeded; x,B,C~N(0,1), delta=softplus(0.5N+bias), A=-exp(U(0,log16)))",
+        "config": {"workload": wl.name, "batch": wl.batch, "seqlen": wl.seqlen, "nheads": wl.nheads,
+                   "headdim": wl.headdim, "ngroups": wl.ngroups, "dstate": wl.dstate, "io_dtype": wl.io},
+        "roofline": {"kernel": "k_ssd", "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "per_launch": {"algorithmic_bytes": nbytes, "matrix_flops": flops,
+                                    "event_avg_us": round(ev_avg * 1e6, 2),
+                                    "event_min_us": round(ev_min * 1e6, 2)},
+                     "mfma": {"achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                              "frac": round(tflops / PEAK_BF16_TFLOPS, 4)}},
+        "cpu_baseline": None}), flush=True)
+    return 0
+
+
 def bench_step(wl, args, dev) -> int:
     """Decode workload: one step = one sscan_step over (batch, dim, N) fp32 state in HBM."""
     import torch
@@ -361,9 +415,11 @@ def main() -> int:
     import datagen
     import selective_state_space_77_amd as sscan
 
-    wl = datagen.workload(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload in datagen.SSD_WORKLOADS:
+        return bench_ssd(datagen.SSD_WORKLOADS[args.workload], args, dev)
+    wl = datagen.workload(args.workload)
     if wl.mode == "step":
         return bench_step(wl, args, dev)
     if args.which == "backward":

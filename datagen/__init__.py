@@ -273,3 +273,51 @@ def frontend_inputs(wl: Workload, d_conv: int, seed: int = 0, threads: int | Non
         "conv_state": _to_io(_rng(seed, wl, "conv_state").standard_normal((wl.batch, d_conv - 1, wl.dim)),
                              wl.io),
     }
+
+
+# ----------------------------------------------------------------------------- scalar A per head
+
+@dataclass(frozen=True)
+class SsdWorkload:
+    """A Mamba-2-shaped workload: heads of P channels, scalar A per head, B/C per group."""
+    name: str
+    key: int
+    batch: int
+    seqlen: int
+    nheads: int
+    headdim: int
+    ngroups: int
+    dstate: int
+    io: str
+
+    @property
+    def elements(self) -> int:
+        return self.batch * self.seqlen * self.nheads * self.headdim
+
+
+SSD_WORKLOADS = {
+    w.name: w for w in (
+        # inner width 4096 (64 heads x 64) as the benchmarked per-channel workload, N = 128
+        SsdWorkload("mamba2_bf16", 20, 4, 8192, 64, 64, 1, 128, "bf16"),
+        SsdWorkload("mamba2_small_f32", 21, 2, 1000, 8, 64, 2, 64, "f32"),
+    )
+}
+
+
+def ssd_inputs(wl: SsdWorkload, seed: int = 0) -> dict:
+    """x (batch, L, H, P), B, C (batch, L, G, N) ~ N(0,1); delta (batch, L, H) =
+    softplus(0.5 N(0,1) + per-head dt bias); A (H) = -exp(U(log 1, log 16)); D (H) ~ N(0,1).
+    Sequence tensors in the I/O dtype's values; A, D fp32."""
+    def rng(tensor):
+        return np.random.Generator(np.random.PCG64(np.random.SeedSequence(
+            [seed, wl.key, _TENSOR_IDS[tensor], 1000])))
+    b, L, H, P, G, N = wl.batch, wl.seqlen, wl.nheads, wl.headdim, wl.ngroups, wl.dstate
+    bias = np.log(np.expm1(rng("dt_bias").uniform(1e-3, 1e-1, H)))
+    return {
+        "x": _to_io(rng("x").standard_normal((b, L, H, P)), wl.io),
+        "delta": _to_io(np.logaddexp(0.0, 0.5 * rng("delta").standard_normal((b, L, H)) + bias), wl.io),
+        "A": (-np.exp(rng("A").uniform(0.0, np.log(16.0), H))).astype(np.float32),
+        "B": _to_io(rng("B").standard_normal((b, L, G, N)), wl.io),
+        "C": _to_io(rng("C").standard_normal((b, L, G, N)), wl.io),
+        "D": rng("Dskip").standard_normal(H).astype(np.float32),
+    }

@@ -220,6 +220,33 @@ int sscan_step_fused(float *state, void *conv_state, const void *x_t, const floa
                      const float *Dskip, void *y_t, int64_t batch, int64_t dim, int64_t dstate,
                      int io_dtype, void *stream);
 
+/*
+ * Scalar-A-per-head selective scan (Mamba-2's state space model), computed in its
+ * chunked matrix form.  The state space duality ("Mamba and State Space Models";
+ * "Mamba matches the Transformer...", the duality section): with A a scalar per
+ * head the scan is a lower-triangular structured (semiseparable) matrix applied to
+ * x, evaluated here chunk by chunk with dense block products.  Per batch row b,
+ * head h, channel p < headdim, state n < dstate, with group g = h / (nheads/ngroups):
+ *     Abar = exp(delta[b,t,h] * A[h]),  gain = (Abar - 1)/A[h]   (delta when A[h] = 0)
+ *     h[p][n] = Abar * h[p][n] + gain * B[b,t,g,n] * x[b,t,h,p]
+ *     y[b,t,h,p] = sum_n C[b,t,g,n] * h[p][n] + Dskip[h] * x[b,t,h,p]
+ * (the zero-order hold of sscan_forward, with A[d,n] = A[h] for every state).
+ *
+ *   x, y          (batch, seqlen, nheads, headdim), io_dtype.
+ *   delta         (batch, seqlen, nheads), io_dtype, after its softplus.
+ *   A             (nheads) fp32.   Dskip (nheads) fp32 or NULL.
+ *   B, C          (batch, seqlen, ngroups, dstate), io_dtype.
+ *   initial_state, final_state  (batch, nheads, headdim, dstate) fp32, or NULL.
+ *   headdim == 64; dstate 64 or 128; nheads a multiple of ngroups.
+ * Products run on the matrix cores in the precision of io_dtype (bf16 operands with
+ * fp32 accumulation for SSCAN_BF16; fp32 for SSCAN_F32); the carried state is fp32.
+ * Returns SSCAN_OK or a negative sscan_status.
+ */
+int sscan_ssd_forward(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                      const float *Dskip, const float *initial_state, void *y, float *final_state,
+                      int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t ngroups,
+                      int64_t dstate, int io_dtype, void *stream);
+
 /* Static text for a status code (never NULL). */
 const char *sscan_status_string(int status);
 

@@ -12,6 +12,8 @@ package raises.
                   conv_state_out=None, stream=None)
     backward(x, delta, A, B, C, dy, Dskip=None, initial_state=None, dfinal_state=None, ...)
     step(state, x_t, delta_t, A, B_t, C_t, Dskip=None, y_t=None, stream=None)
+    ssd_forward(x, delta, A, B, C, Dskip=None, initial_state=None, y=None, final_state=None,
+                stream=None)
     step_fused(state, conv_state, x_t, conv_weight, delta_raw_t, A, B_t, C_t, Dskip=None,
                conv_bias=None, delta_bias=None, activation=None, y_t=None, stream=None)
 
@@ -65,6 +67,9 @@ def _load() -> ctypes.CDLL:
     lib.sscan_step_fused.argtypes = [fp, vp, vp, fp, fp, ci, ci, vp, fp, fp, vp, vp, fp, vp,
                                      i64, i64, i64, ci, vp]
     lib.sscan_step_fused.restype = ctypes.c_int
+    lib.sscan_ssd_forward.argtypes = [vp, vp, fp, vp, vp, fp, fp, vp, fp, i64, i64, i64, i64, i64, i64,
+                                      ci, vp]
+    lib.sscan_ssd_forward.restype = ctypes.c_int
     lib.sscan_step.argtypes = [fp, vp, vp, fp, vp, vp, fp, vp, i64, i64, i64, ctypes.c_int, vp]
     lib.sscan_step.restype = ctypes.c_int
     lib.sscan_status_string.argtypes = [ctypes.c_int]
@@ -267,3 +272,31 @@ def step(state, x_t, delta_t, A, B_t, C_t, Dskip=None, y_t=None, stream=None):
 
 def version() -> int:
     return lib.sscan_version()
+
+
+def ssd_forward(x, delta, A, B, C, Dskip=None, initial_state=None, y=None, final_state=None,
+                stream=None):
+    """Scalar-A-per-head scan (Mamba-2's SSM) in its chunked matrix form; returns y.
+
+    x, y: (batch, L, H, P) with P = 64; delta: (batch, L, H); A: (H,) fp32; B, C:
+    (batch, L, G, N) with N in {64, 128} and G | H; Dskip: (H,) fp32; states:
+    (batch, H, P, N) fp32."""
+    batch, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if tuple(delta.shape) != (batch, L, H) or tuple(A.shape) != (H,) or B.shape != (batch, L, G, N) \
+            or C.shape != B.shape:
+        raise ValueError("inconsistent shapes")
+    for t, name, shape in ((Dskip, "Dskip", (H,)), (initial_state, "initial_state", (batch, H, P, N)),
+                           (final_state, "final_state", (batch, H, P, N))):
+        if t is not None and tuple(t.shape) != shape:
+            raise ValueError(f"{name} must have shape {shape}")
+    if y is None:
+        y = torch.empty_like(x)
+    io = _io_code(x, delta, B, C, y)
+    rc = lib.sscan_ssd_forward(_dev(x, "x"), _dev(delta, "delta"), _dev(A, "A", torch.float32),
+                               _dev(B, "B"), _dev(C, "C"), _dev(Dskip, "Dskip", torch.float32),
+                               _dev(initial_state, "initial_state", torch.float32), _dev(y, "y"),
+                               _dev(final_state, "final_state", torch.float32), batch, L, H, P, G, N, io,
+                               _stream(stream, x.device))
+    _check(rc)
+    return y

@@ -7,7 +7,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsscan.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("sscan_api.hip", "sscan_kernels.hip", "sscan_bwd.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("sscan_api.hip", "sscan_kernels.hip", "sscan_bwd.hip", "sscan_ssd.hip")]
 ARCH = "gfx950"
 
 # Packed-FP32 VALU forms are kept out of the generated code; the host pass warns

@@ -249,6 +249,46 @@ int sscan_forward_fused(const void *x, const float *conv_weight, const float *co
                         dstate, io_dtype, stream, fe);
 }
 
+int sscan_ssd_forward(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                      const float *Dskip, const float *initial_state, void *y, float *final_state,
+                      int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t ngroups,
+                      int64_t dstate, int io_dtype, void *stream) {
+    g_last_error[0] = '\0';
+    if (io_dtype != SSCAN_F32 && io_dtype != SSCAN_BF16)
+        return fail(SSCAN_ERR_UNSUPPORTED, "io_dtype must be SSCAN_F32 or SSCAN_BF16");
+    if (headdim != sscan::kSsdHeadDim) return fail(SSCAN_ERR_UNSUPPORTED, "headdim must be 64");
+    if (dstate != 64 && dstate != 128) return fail(SSCAN_ERR_UNSUPPORTED, "dstate must be 64 or 128");
+    if (nheads < 1 || ngroups < 1 || nheads % ngroups != 0)
+        return fail(SSCAN_ERR_SHAPE, "nheads and ngroups must be positive, nheads a multiple of ngroups");
+    const int64_t es = io_dtype == SSCAN_BF16 ? 2 : 4;
+    int64_t bx, bd, bbc, bh, bs, tmp;
+    if (!nbytes(&bx, es, batch, seqlen, nheads * headdim) || !nbytes(&bd, es, batch, seqlen, nheads) ||
+        !nbytes(&bbc, es, batch, seqlen, ngroups * dstate) || !nbytes(&bh, 4, nheads) ||
+        !nbytes(&bs, 4, batch, nheads, headdim * dstate) || !nbytes(&tmp, 1, batch, nheads))
+        return fail(SSCAN_ERR_SHAPE, "negative size or byte size overflows int64");
+    if (batch * nheads > 0x7FFFFFFF) return fail(SSCAN_ERR_SHAPE, "batch * nheads above 2^31 - 1");
+    const Span ins[] = {{x, bx, "x"}, {delta, bd, "delta"}, {A, bh, "A"}, {B, bbc, "B"}, {C, bbc, "C"},
+                        {Dskip, Dskip ? bh : 0, "Dskip"},
+                        {initial_state, initial_state ? bs : 0, "initial_state"}};
+    const Span outs[] = {{y, bx, "y"}, {final_state, final_state ? bs : 0, "final_state"}};
+    const Span req[] = {ins[0], ins[1], ins[2], ins[3], ins[4], outs[0]};
+    int rc = check_ptrs(req, 6);
+    if (rc) return rc;
+    rc = check_alias(outs, 2, ins, 7);
+    if (rc) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (batch == 0) return SSCAN_OK;
+    if (seqlen == 0) {
+        if (!final_state) return SSCAN_OK;
+        const hipError_t e = sscan::launch_copy_or_zero(final_state, initial_state, bs / 4, s);
+        return e == hipSuccess ? SSCAN_OK : fail_hip("state copy launch", e);
+    }
+    sscan::SsdArgs a{x, delta, A, B, C, Dskip, initial_state, y, final_state, batch, seqlen, nheads,
+                     headdim, ngroups, int(dstate), io_dtype};
+    const hipError_t e = sscan::launch_ssd(a, s);
+    return e == hipSuccess ? SSCAN_OK : fail_hip("ssd launch", e);
+}
+
 static int step_impl(float *state, const void *x_t, const void *delta_t, const float *A,
                      const void *B_t, const void *C_t, const float *Dskip, void *y_t, int64_t batch,
                      int64_t dim, int64_t dstate, int io_dtype, void *stream, const FrontEnd &fe,

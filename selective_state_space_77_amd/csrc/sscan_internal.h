@@ -120,6 +120,23 @@ hipError_t launch_backward(const BwdArgs &a, const BwdPlan &plan, void *ws, hipS
 hipError_t launch_conv_tail(const void *x, const FeArgs &fe, void *conv_state_out, int64_t batch,
                             int64_t seqlen, int64_t dim, int io, hipStream_t s);
 
+// Scalar-A-per-head scan (Mamba-2's SSM) in its chunked matrix form.
+struct SsdArgs {
+    const void *x, *delta;  // (batch, L, H, P), (batch, L, H)
+    const float *A;         // (H)
+    const void *B, *C;      // (batch, L, G, N)
+    const float *Dskip;     // (H) or NULL
+    const float *h0;        // (batch, H, P, N) or NULL
+    void *y;                // (batch, L, H, P)
+    float *final_state;     // (batch, H, P, N) or NULL
+    int64_t batch, L, H, P, G;
+    int N;
+    int io;
+};
+constexpr int kSsdHeadDim = 64;  // supported P
+
+hipError_t launch_ssd(const SsdArgs &a, hipStream_t s);
+
 // Enqueue dst[i] = src ? src[i] : 0 for `count` floats (final_state at seqlen 0).
 hipError_t launch_copy_or_zero(float *dst, const float *src, int64_t count, hipStream_t s);
 

@@ -38,8 +38,8 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     assert _declared() == ["sscan_backward", "sscan_forward", "sscan_forward_from_state",
-                           "sscan_forward_fused", "sscan_last_error", "sscan_status_string",
-                           "sscan_step", "sscan_step_fused", "sscan_version"]
+                           "sscan_forward_fused", "sscan_last_error", "sscan_ssd_forward",
+                           "sscan_status_string", "sscan_step", "sscan_step_fused", "sscan_version"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -180,6 +180,28 @@ def test_step_fused_validation(lib):
     assert _step_fused(lib, cs=0x2002) == -4         # conv_state overlaps delta_raw_t
     assert b"conv_state" in lib.sscan_last_error()
     assert _step_fused(lib, batch=0, st=None, cs=None, x=None, dr=None, B=None, C=None, y=None) == 0
+
+
+def _ssd(lib, **kw):
+    a = dict(x=0x100000, d=0x200000, A=0x300000, B=0x400000, C=0x500000, D=None, h0=None, y=0x600000,
+             hs=None, batch=1, L=8, H=4, P=64, G=2, N=64, io=1)
+    a.update(kw)
+    return lib.sscan_ssd_forward(a["x"], a["d"], a["A"], a["B"], a["C"], a["D"], a["h0"], a["y"], a["hs"],
+                                 a["batch"], a["L"], a["H"], a["P"], a["G"], a["N"], a["io"], None)
+
+
+def test_ssd_validation(lib):
+    assert _ssd(lib, P=32) == -3
+    assert _ssd(lib, N=16) == -3
+    assert _ssd(lib, io=3) == -3
+    assert _ssd(lib, G=3) == -2                 # heads not a multiple of groups
+    assert _ssd(lib, G=0) == -2
+    assert _ssd(lib, L=-1) == -2
+    assert _ssd(lib, x=None) == -1
+    assert _ssd(lib, C=None) == -1
+    assert _ssd(lib, y=0x100010) == -4          # y overlaps x
+    assert _ssd(lib, hs=0x300008) == -4         # final state overlaps A
+    assert _ssd(lib, batch=0, x=None, d=None, B=None, C=None, y=None) == 0
 
 
 def _step(lib, **kw):
