@@ -273,6 +273,279 @@ __global__ __launch_bounds__(SWV *kWave) void k_ssd(
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 kernel.  8 waves per (batch row, head); each chunk of x, B, C and delta
+// is fetched with 16-byte loads one chunk ahead (into registers, while the
+// current chunk computes) and staged in LDS as bf16, in the layouts the
+// matrix operands read with single 8- or 16-byte LDS reads: x and B transposed
+// ([channel][token], [state][token]), B and C row-major ([token][state]), the
+// entering state as a bf16 high part and remainder ([channel][state]).
+// Waves 2k and 2k+1 compute the outputs of tokens 16k..16k+15 (channel blocks
+// 0-1 and 2-3); for the state update wave v owns channel block v % 4 and half
+// of the state blocks.  The scores, C S_in and the update use the K = 32
+// matrix instruction (v_mfma_f32_16x16x32_bf16); (scores) X, whose K is a
+// 16-token block of the causal triangle, the K = 16 one.
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+constexpr int BWV = 8;            // waves per workgroup
+constexpr int BTH = BWV * kWave;  // threads per workgroup
+constexpr int XPB = SQ + 8;       // pitch (bf16) of the [channel][token] and [state][token] tiles
+
+__device__ __forceinline__ float bfv(uint16_t u) { return __uint_as_float(uint32_t(u) << 16); }
+
+__device__ __forceinline__ v4f mfma16(v4f acc, v4s a, v4s b) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
+}
+// K slab of 32: lane l holds a[j] = A[r][8q + j], b[j] = B[8q + j][r], j < 8
+__device__ __forceinline__ v4f mfma32(v4f acc, v8bf a, v8bf b) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ void split8(const float (&v)[8], v8bf &hi, v8bf &lo) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const __bf16 hb = static_cast<__bf16>(v[j]);
+        hi[j] = hb;
+        lo[j] = static_cast<__bf16>(v[j] - static_cast<float>(hb));
+    }
+}
+
+template <int NS>
+__global__ __launch_bounds__(BTH) void k_ssd_bf(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ delta, const float *__restrict__ A,
+    const uint16_t *__restrict__ Bm, const uint16_t *__restrict__ Cm, const float *__restrict__ Dskip,
+    const float *__restrict__ h0, uint16_t *__restrict__ y, float *__restrict__ hT, int64_t L,
+    int64_t H, int64_t G) {
+    constexpr int NB = NS / 16;        // 16-wide state blocks
+    constexpr int NK = NS / 32;        // 32-wide K steps over the states
+    constexpr int RP = NS + 8;         // pitch (bf16) of the [token][state] and [channel][state] tiles
+    constexpr int NBW = NB / 2;        // state tiles per wave in the update
+    constexpr int BE = NS * SQ / BTH;  // bf16 elements of B (and of C) staged per thread
+    static_assert(BE % 8 == 0 && SP * SQ / BTH == 8, "staging split");
+    __shared__ __align__(16) uint16_t sXt[SP][XPB];
+    __shared__ __align__(16) uint16_t sBt[NS][XPB];
+    __shared__ __align__(16) uint16_t sB[SQ][RP];
+    __shared__ __align__(16) uint16_t sC[SQ][RP];
+    __shared__ __align__(16) uint16_t sSh[SP][RP];
+    __shared__ __align__(16) uint16_t sSl[SP][RP];
+    __shared__ __align__(16) uint16_t sY[BWV][16][32];  // each wave's output tile, [token][channel]
+    __shared__ float sCum[SQ], sGain[SQ], sW[SQ], sE[SQ];
+    __shared__ float sDec;
+
+    const int tid = int(threadIdx.x);
+    const int v = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int lane = tid % kWave, r = lane % 16, q = lane / 16;
+    const int64_t b = int64_t(blockIdx.x) / H;
+    const int64_t h = int64_t(blockIdx.x) - b * H;
+    const int64_t g = h / (H / G);
+    const float a = A[h];
+    const float a2 = a * kLog2e;
+    const float dsk = Dskip ? Dskip[h] : 0.f;
+    // row t of this (batch row, head): x and y at xb/yb + t*rx, B/C at Bb/Cb + t*rbc,
+    // delta at db + t*H (elements).  Each chunk reads and writes through buffer
+    // descriptors over [t0, L): 32-bit offsets, and tokens past the end read 0
+    // and drop their stores in the hardware range check.
+    const int64_t rx = H * SP, rbc = G * NS;
+    const uint16_t *xb = x + (b * L * H + h) * SP;
+    uint16_t *yb = y + (b * L * H + h) * SP;
+    const uint16_t *Bb = Bm + (b * L * G + g) * NS;
+    const uint16_t *Cb = Cm + (b * L * G + g) * NS;
+    const uint16_t *db = delta + b * L * H + h;
+
+    // ---- chunk fetch (registers) and staging (LDS).  Thread roles: token
+    // st = lane, x channels 8v..8v+7, B and C states BE*v..BE*v+BE-1 (v = wave):
+    // the transposed LDS writes of a wave then fill consecutive tokens of one
+    // row (no bank conflicts); the 16-byte global reads of a wave hit 64 rows,
+    // whose other bytes the other waves read from the same cache lines.
+    const int st = lane, c8 = v;
+    const uint32_t ox = uint32_t(st * rx * 2 + 16 * c8);   // byte offsets of this thread
+    const uint32_t obc = uint32_t(st * rbc * 2 + 2 * BE * c8);
+    const uint32_t od = uint32_t(lane * H * 2);
+    v4u px, pb[BE / 8], pc[BE / 8];
+    uint16_t pd = 0;
+    auto fetch = [&](int64_t t0) {
+        const rsrc_t rxs = make_rsrc(xb + t0 * rx, (L - t0) * rx * 2);
+        const rsrc_t rbs = make_rsrc(Bb + t0 * rbc, (L - t0) * rbc * 2);
+        const rsrc_t rcs = make_rsrc(Cb + t0 * rbc, (L - t0) * rbc * 2);
+        px = __builtin_amdgcn_raw_buffer_load_b128(rxs, ox, 0, 0);
+#pragma unroll
+        for (int i = 0; i < BE / 8; ++i) {
+            pb[i] = __builtin_amdgcn_raw_buffer_load_b128(rbs, obc + 16 * i, 0, 0);
+            pc[i] = __builtin_amdgcn_raw_buffer_load_b128(rcs, obc + 16 * i, 0, 0);
+        }
+        if (v == 0) pd = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(db + t0 * H, (L - t0) * H * 2), od, 0, 0);
+    };
+    auto stage = [&]() {
+        const uint16_t *xv = reinterpret_cast<const uint16_t *>(&px);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sXt[8 * c8 + k][st] = xv[k];
+#pragma unroll
+        for (int i = 0; i < BE / 8; ++i) {
+            *reinterpret_cast<v4u *>(&sB[st][BE * c8 + 8 * i]) = pb[i];
+            *reinterpret_cast<v4u *>(&sC[st][BE * c8 + 8 * i]) = pc[i];
+            const uint16_t *bv = reinterpret_cast<const uint16_t *>(&pb[i]);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) sBt[BE * c8 + 8 * i + k][st] = bv[k];
+        }
+        // per-token scalars (wave 0, lane = token): running sum of delta
+        // (inclusive), gain, state weight, output decay; chunk decay.  Tokens
+        // past the end have delta = 0: gain 0, decay 1.
+        if (v == 0) {
+            const float dv = bfv(pd);
+            float cum = dv;
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) {
+                const float u = __shfl_up(cum, off);
+                if (lane >= off) cum += u;
+            }
+            const float total = __shfl(cum, kWave - 1);
+            const float gain = zoh_gain(dv, a, dv * a, exp2_hw(dv * a2));  // delta when A = 0
+            sCum[lane] = cum;
+            sGain[lane] = gain;
+            sW[lane] = exp2_hw(a2 * (total - cum)) * gain;
+            sE[lane] = exp2_hw(a2 * cum);
+            if (lane == 0) sDec = exp2_hw(a2 * total);
+        }
+    };
+
+    // ---- state tiles of this wave: channel block pbs, state blocks nb0..nb0+NBW-1;
+    // S[i][j] = S[n = 16(nb0 + i) + 4q + j][p = 16 pbs + r]
+    const int pbs = v % 4, nb0 = NBW * (v / 4);
+    v4f S[NBW];
+    const int64_t srow = ((b * H + h) * SP + 16 * pbs + r) * NS;
+#pragma unroll
+    for (int i = 0; i < NBW; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) S[i][j] = h0 ? h0[srow + 16 * (nb0 + i) + 4 * q + j] : 0.f;
+    auto publish_state = [&]() {
+#pragma unroll
+        for (int i = 0; i < NBW; ++i) {
+            v4s hi, lo;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint16_t hb = f32_to_bf16(S[i][j]);
+                hi[j] = short(hb);
+                lo[j] = short(f32_to_bf16(S[i][j] - bfv(hb)));
+            }
+            *reinterpret_cast<v4s *>(&sSh[16 * pbs + r][16 * (nb0 + i) + 4 * q]) = hi;
+            *reinterpret_cast<v4s *>(&sSl[16 * pbs + r][16 * (nb0 + i) + 4 * q]) = lo;
+        }
+    };
+    publish_state();
+    fetch(0);
+
+    const int tb = v >> 1, pp = v & 1;  // output tokens 16tb..16tb+15, channel blocks 2pp, 2pp+1
+    const int tl = 16 * tb + r;
+    const int64_t nchunks = (L + SQ - 1) / SQ;
+    for (int64_t c = 0; c < nchunks; ++c) {
+        const int64_t t0 = c * SQ;
+        stage();
+        __syncthreads();
+        if (c + 1 < nchunks) fetch(t0 + SQ);  // next chunk, in flight during this one
+
+        // ---- masked scores of tokens 16tb..: G^T tile (s-block sb, t-block tb) = B C^T,
+        // times exp(A (cum_t - cum_s)) gain_s where s <= t; split into bf16 parts
+        const float cum_t = sCum[tl];
+        // C fragments of this wave's tokens, K slabs of 32 states: the B operand
+        // (C^T) of the scores and the A operand of C S_in
+        v8bf ca[NK];
+#pragma unroll
+        for (int kb = 0; kb < NK; ++kb) ca[kb] = *reinterpret_cast<const v8bf *>(&sC[tl][32 * kb + 8 * q]);
+        v4s gh[SQ / 16], gl[SQ / 16];
+#pragma unroll
+        for (int sb = 0; sb < SQ / 16; ++sb) {
+            if (sb > tb) break;
+            v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < NK; ++kb) {
+                const v8bf bf = *reinterpret_cast<const v8bf *>(&sB[16 * sb + r][32 * kb + 8 * q]);
+                acc = mfma32(acc, bf, ca[kb]);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int sl = 16 * sb + 4 * q + j;
+                const float m = acc[j] * exp2_hw(a2 * (cum_t - sCum[sl])) * sGain[sl];
+                const float gv = sl <= tl ? m : 0.f;
+                const uint16_t hb = f32_to_bf16(gv);
+                gh[sb][j] = short(hb);
+                gl[sb][j] = short(f32_to_bf16(gv - bfv(hb)));
+            }
+        }
+        // ---- outputs: Y = scores X + diag(e) (C S_in) + D x
+        float et[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) et[j] = sE[16 * tb + 4 * q + j];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int pbk = 2 * pp + u;
+            v4f acc = {0.f, 0.f, 0.f, 0.f}, off = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int sb = 0; sb < SQ / 16; ++sb) {
+                if (sb > tb) break;
+                const v4s xf = *reinterpret_cast<const v4s *>(&sXt[16 * pbk + r][16 * sb + 4 * q]);
+                acc = mfma16(acc, gh[sb], xf);
+                acc = mfma16(acc, gl[sb], xf);
+            }
+#pragma unroll
+            for (int kb = 0; kb < NK; ++kb) {
+                const v8bf sh = *reinterpret_cast<const v8bf *>(&sSh[16 * pbk + r][32 * kb + 8 * q]);
+                const v8bf sl = *reinterpret_cast<const v8bf *>(&sSl[16 * pbk + r][32 * kb + 8 * q]);
+                off = mfma32(off, ca[kb], sh);
+                off = mfma32(off, ca[kb], sl);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int tj = 16 * tb + 4 * q + j;
+                const float val = fmaf(et[j], off[j], fmaf(dsk, bfv(sXt[16 * pbk + r][tj]), acc[j]));
+                sY[v][4 * q + j][16 * u + r] = f32_to_bf16(val);
+            }
+        }
+        // the wave's 16 x 32 output tile leaves as one 16-byte store per lane
+        // (token 16tb + lane/4, channels 32pp + 8(lane%4)..+7)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        {
+            const v4u yv = *reinterpret_cast<const v4u *>(&sY[v][lane / 4][8 * (lane % 4)]);
+            const rsrc_t rys = make_rsrc(yb + t0 * rx, (L - t0) * rx * 2);
+            __builtin_amdgcn_raw_buffer_store_b128(
+                yv, rys, uint32_t(((16 * tb + lane / 4) * rx + 32 * pp + 8 * (lane % 4)) * 2), 0, 0);
+        }
+        __syncthreads();  // every wave has read the entering state
+
+        // ---- state update: S = exp(A sum delta) S + B^T diag(w) X
+        const float dec = sDec;
+#pragma unroll
+        for (int i = 0; i < NBW; ++i) S[i] *= dec;
+#pragma unroll
+        for (int kb = 0; kb < SQ / 32; ++kb) {
+            float xw[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int sl = 32 * kb + 8 * q + j;
+                xw[j] = bfv(sXt[16 * pbs + r][sl]) * sW[sl];
+            }
+            v8bf xh, xl;
+            split8(xw, xh, xl);
+#pragma unroll
+            for (int i = 0; i < NBW; ++i) {
+                const v8bf bt = *reinterpret_cast<const v8bf *>(&sBt[16 * (nb0 + i) + r][32 * kb + 8 * q]);
+                S[i] = mfma32(S[i], bt, xh);
+                S[i] = mfma32(S[i], bt, xl);
+            }
+        }
+        publish_state();
+        __syncthreads();  // the next chunk restages and reads the new state
+    }
+    if (hT) {
+#pragma unroll
+        for (int i = 0; i < NBW; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) hT[srow + 16 * (nb0 + i) + 4 * q + j] = S[i][j];
+    }
+}
+
 template <class IO, int NS>
 hipError_t ssd_t(const SsdArgs &a, hipStream_t s) {
     using T = typename IO::T;
@@ -283,8 +556,25 @@ hipError_t ssd_t(const SsdArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int NS>
+hipError_t ssd_bf_t(const SsdArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL((k_ssd_bf<NS>), dim3(unsigned(a.batch * a.H)), dim3(BTH), 0, s,
+                       static_cast<const uint16_t *>(a.x), static_cast<const uint16_t *>(a.delta), a.A,
+                       static_cast<const uint16_t *>(a.B), static_cast<const uint16_t *>(a.C), a.Dskip, a.h0,
+                       static_cast<uint16_t *>(a.y), a.final_state, a.L, a.H, a.G);
+    return hipGetLastError();
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 template <class IO>
 hipError_t ssd_io(const SsdArgs &a, hipStream_t s) {
+    // the bf16 kernel's 16-byte loads need 16-byte aligned x, B and C; other
+    // bf16 arguments take the 4-wave kernel, which reads element by element
+    if constexpr (std::is_same<IO, IoBF16>::value) {
+        if (aligned16(a.x) && aligned16(a.B) && aligned16(a.C))
+            return a.N == 64 ? ssd_bf_t<64>(a, s) : ssd_bf_t<128>(a, s);
+    }
     return a.N == 64 ? ssd_t<IO, 64>(a, s) : ssd_t<IO, 128>(a, s);
 }
 

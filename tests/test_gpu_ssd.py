@@ -118,6 +118,29 @@ def test_ssd_resumes_from_its_final_state():
     assert e <= 1e-5 and rel_err(h2, hs.astype(np.float64)) <= 1e-5
 
 
+def test_ssd_unaligned_bf16_inputs_take_the_elementwise_kernel():
+    """x, B and C that are not 16-byte aligned (views one element in) give the same
+    result through the element-by-element kernel."""
+    wl = _wl("ssd_unal", 1, 200, 2, 1, 64, "bf16")
+    inp = datagen.ssd_inputs(wl)
+    announce("ssd unaligned bf16 inputs")
+    y_ref, h_ref = _run(wl, inp)
+    t = _up(inp, "bf16")
+    def shifted(z):
+        buf = torch.empty(z.numel() + 1, dtype=z.dtype, device="cuda")
+        v = buf[1:].view(z.shape)
+        v.copy_(z)
+        return v
+    x, B, C = shifted(t["x"]), shifted(t["B"]), shifted(t["C"])
+    assert x.data_ptr() % 16 != 0
+    hs = torch.empty(1, 2, 64, 64, device="cuda")
+    y = sscan.ssd_forward(x, t["delta"], t["A"], B, C, t["D"], final_state=hs)
+    torch.cuda.synchronize()
+    yr, hr = oracle.ssd_forward(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"])
+    assert rel_err(to_host(y), yr) <= TOL["bf16"] and rel_err(hs.cpu().numpy(), hr) <= TOL["bf16"]
+    assert rel_err(to_host(y), y_ref.astype(np.float64)) <= 1e-2
+
+
 def test_ssd_deterministic():
     wl = _wl("ssd_det", 2, 300, 4, 1, 128, "bf16")
     inp = datagen.ssd_inputs(wl)
