@@ -54,6 +54,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak, published
 CSRC = os.path.join(ROOT, "selective_state_space_77_amd", "csrc")
 FWD_SOURCES = ("sscan_kernels.hip", "sscan_device.h", "sscan_internal.h")
 BWD_SOURCES = ("sscan_bwd.hip", "sscan_device.h", "sscan_internal.h")
+SSD_SOURCES = ("sscan_ssd.hip", "sscan_device.h", "sscan_internal.h")
 
 
 def source_fingerprint(files) -> str:
@@ -330,8 +331,10 @@ def bench_ssd(wl, args, dev) -> int:
         "data": "synthetic (seeded; x,B,C~N(0,1), delta=softplus(0.5N+bias), A=-exp(U(0,log16)))",
         "config": {"workload": wl.name, "batch": wl.batch, "seqlen": wl.seqlen, "nheads": wl.nheads,
                    "headdim": wl.headdim, "ngroups": wl.ngroups, "dstate": wl.dstate, "io_dtype": wl.io},
-        "roofline": {"kernel": "k_ssd", "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+        "roofline": {"kernel": "k_ssd_bf" if wl.io == "bf16" else "k_ssd", "bound": "hbm",
+                     "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": recorded_traffic(f"k_ssd_{wl.name}_hbm_counters.md", SSD_SOURCES),
                      "per_launch": {"algorithmic_bytes": nbytes, "matrix_flops": flops,
                                     "event_avg_us": round(ev_avg * 1e6, 2),
                                     "event_min_us": round(ev_min * 1e6, 2)},
