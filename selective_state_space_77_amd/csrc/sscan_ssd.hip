@@ -280,9 +280,12 @@ __global__ __launch_bounds__(SWV *kWave) void k_ssd(
 // matrix operands read with single 8- or 16-byte LDS reads: x and B transposed
 // ([channel][token], [state][token]), B and C row-major ([token][state]), the
 // entering state as a bf16 high part and remainder ([channel][state]).
-// Waves 2k and 2k+1 compute the outputs of tokens 16k..16k+15 (channel blocks
-// 0-1 and 2-3); for the state update wave v owns channel block v % 4 and half
-// of the state blocks.  The scores, C S_in and the update use the K = 32
+// A chunk is three phases between barriers: staging (with the state
+// carried in from the previous chunk); the 10 causal 16x16 score tiles, spread
+// over the 8 waves and shared through LDS, beside the state update (wave v
+// owns channel block v % 4 and half of the state blocks: equal work); the
+// outputs, wave v taking channel block v % 4 of token blocks {0, 3} or {1, 2}
+// (equal causal work).  The scores, C S_in and the update use the K = 32
 // matrix instruction (v_mfma_f32_16x16x32_bf16); (scores) X, whose K is a
 // 16-token block of the causal triangle, the K = 16 one.
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
@@ -322,6 +325,7 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
     constexpr int RP = NS + 8;         // pitch (bf16) of the [token][state] and [channel][state] tiles
     constexpr int NBW = NB / 2;        // state tiles per wave in the update
     constexpr int BE = NS * SQ / BTH;  // bf16 elements of B (and of C) staged per thread
+    constexpr int NG = 10;             // causal 16x16 score tiles of a 64-token chunk
     static_assert(BE % 8 == 0 && SP * SQ / BTH == 8, "staging split");
     __shared__ __align__(16) uint16_t sXt[SP][XPB];
     __shared__ __align__(16) uint16_t sBt[NS][XPB];
@@ -329,7 +333,9 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
     __shared__ __align__(16) uint16_t sC[SQ][RP];
     __shared__ __align__(16) uint16_t sSh[SP][RP];
     __shared__ __align__(16) uint16_t sSl[SP][RP];
-    __shared__ __align__(16) uint16_t sY[BWV][16][32];  // each wave's output tile, [token][channel]
+    __shared__ __align__(16) uint16_t sGh[NG][16][16];  // masked scores, A-operand layout [tile][t][s]
+    __shared__ __align__(16) uint16_t sGl[NG][16][16];
+    __shared__ __align__(16) uint16_t sY[BWV][2][16][16];  // each wave's two output tiles
     __shared__ float sCum[SQ], sGain[SQ], sW[SQ], sE[SQ];
     __shared__ float sDec;
 
@@ -359,7 +365,7 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
     // row (no bank conflicts); the 16-byte global reads of a wave hit 64 rows,
     // whose other bytes the other waves read from the same cache lines.
     const int st = lane, c8 = v;
-    const uint32_t ox = uint32_t(st * rx * 2 + 16 * c8);   // byte offsets of this thread
+    const uint32_t ox = uint32_t(st * rx * 2 + 16 * c8);  // byte offsets of this thread
     const uint32_t obc = uint32_t(st * rbc * 2 + 2 * BE * c8);
     const uint32_t od = uint32_t(lane * H * 2);
     v4u px, pb[BE / 8], pc[BE / 8];
@@ -432,89 +438,55 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
             *reinterpret_cast<v4s *>(&sSl[16 * pbs + r][16 * (nb0 + i) + 4 * q]) = lo;
         }
     };
-    publish_state();
-    fetch(0);
 
-    const int tb = v >> 1, pp = v & 1;  // output tokens 16tb..16tb+15, channel blocks 2pp, 2pp+1
-    const int tl = 16 * tb + r;
+    // causal score tile k (0..9) = (token block tb, source block sb <= tb), row-major
+    // over the triangle; tile_of(tb, sb) = tb (tb + 1) / 2 + sb
+    // outputs of this wave: channel block pbo, token blocks tbo[0] + tbo[1] = 3 (equal work)
+    const int pbo = v % 4;
+    const int tbo0 = v < 4 ? 0 : 1, tbo1 = 3 - tbo0;
+
+    fetch(0);
     const int64_t nchunks = (L + SQ - 1) / SQ;
     for (int64_t c = 0; c < nchunks; ++c) {
         const int64_t t0 = c * SQ;
+        publish_state();  // the state entering this chunk
         stage();
         __syncthreads();
         if (c + 1 < nchunks) fetch(t0 + SQ);  // next chunk, in flight during this one
 
-        // ---- masked scores of tokens 16tb..: G^T tile (s-block sb, t-block tb) = B C^T,
-        // times exp(A (cum_t - cum_s)) gain_s where s <= t; split into bf16 parts
-        const float cum_t = sCum[tl];
-        // C fragments of this wave's tokens, K slabs of 32 states: the B operand
-        // (C^T) of the scores and the A operand of C S_in
-        v8bf ca[NK];
+        // ---- phase 2a: causal score tiles, spread over the waves (k = v, v + 8):
+        // G^T tile (s-block sb, t-block tb) = B C^T, times exp(A (cum_t - cum_s)) gain_s
+        // where s <= t, split into bf16 parts and stored in the A-operand layout
+        // of (scores) X: lane (t = r, k = s = 4q + j)
 #pragma unroll
-        for (int kb = 0; kb < NK; ++kb) ca[kb] = *reinterpret_cast<const v8bf *>(&sC[tl][32 * kb + 8 * q]);
-        v4s gh[SQ / 16], gl[SQ / 16];
-#pragma unroll
-        for (int sb = 0; sb < SQ / 16; ++sb) {
-            if (sb > tb) break;
+        for (int kk = 0; kk < 2; ++kk) {
+            const int k = v + 8 * kk;
+            if (k >= NG) break;
+            const int tb = k >= 6 ? 3 : k >= 3 ? 2 : k >= 1 ? 1 : 0;
+            const int sb = k - tb * (tb + 1) / 2;
+            const int tl = 16 * tb + r;
             v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < NK; ++kb) {
                 const v8bf bf = *reinterpret_cast<const v8bf *>(&sB[16 * sb + r][32 * kb + 8 * q]);
-                acc = mfma32(acc, bf, ca[kb]);
+                const v8bf cf = *reinterpret_cast<const v8bf *>(&sC[tl][32 * kb + 8 * q]);
+                acc = mfma32(acc, bf, cf);
             }
+            const float cum_t = sCum[tl];
+            v4s hi, lo;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int sl = 16 * sb + 4 * q + j;
                 const float m = acc[j] * exp2_hw(a2 * (cum_t - sCum[sl])) * sGain[sl];
                 const float gv = sl <= tl ? m : 0.f;
                 const uint16_t hb = f32_to_bf16(gv);
-                gh[sb][j] = short(hb);
-                gl[sb][j] = short(f32_to_bf16(gv - bfv(hb)));
+                hi[j] = short(hb);
+                lo[j] = short(f32_to_bf16(gv - bfv(hb)));
             }
+            *reinterpret_cast<v4s *>(&sGh[k][r][4 * q]) = hi;
+            *reinterpret_cast<v4s *>(&sGl[k][r][4 * q]) = lo;
         }
-        // ---- outputs: Y = scores X + diag(e) (C S_in) + D x
-        float et[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) et[j] = sE[16 * tb + 4 * q + j];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int pbk = 2 * pp + u;
-            v4f acc = {0.f, 0.f, 0.f, 0.f}, off = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int sb = 0; sb < SQ / 16; ++sb) {
-                if (sb > tb) break;
-                const v4s xf = *reinterpret_cast<const v4s *>(&sXt[16 * pbk + r][16 * sb + 4 * q]);
-                acc = mfma16(acc, gh[sb], xf);
-                acc = mfma16(acc, gl[sb], xf);
-            }
-#pragma unroll
-            for (int kb = 0; kb < NK; ++kb) {
-                const v8bf sh = *reinterpret_cast<const v8bf *>(&sSh[16 * pbk + r][32 * kb + 8 * q]);
-                const v8bf sl = *reinterpret_cast<const v8bf *>(&sSl[16 * pbk + r][32 * kb + 8 * q]);
-                off = mfma32(off, ca[kb], sh);
-                off = mfma32(off, ca[kb], sl);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int tj = 16 * tb + 4 * q + j;
-                const float val = fmaf(et[j], off[j], fmaf(dsk, bfv(sXt[16 * pbk + r][tj]), acc[j]));
-                sY[v][4 * q + j][16 * u + r] = f32_to_bf16(val);
-            }
-        }
-        // the wave's 16 x 32 output tile leaves as one 16-byte store per lane
-        // (token 16tb + lane/4, channels 32pp + 8(lane%4)..+7)
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        {
-            const v4u yv = *reinterpret_cast<const v4u *>(&sY[v][lane / 4][8 * (lane % 4)]);
-            const rsrc_t rys = make_rsrc(yb + t0 * rx, (L - t0) * rx * 2);
-            __builtin_amdgcn_raw_buffer_store_b128(
-                yv, rys, uint32_t(((16 * tb + lane / 4) * rx + 32 * pp + 8 * (lane % 4)) * 2), 0, 0);
-        }
-        __syncthreads();  // every wave has read the entering state
-
-        // ---- state update: S = exp(A sum delta) S + B^T diag(w) X
+        // ---- phase 2b: state update (registers): S = exp(A sum delta) S + B^T diag(w) X
         const float dec = sDec;
 #pragma unroll
         for (int i = 0; i < NBW; ++i) S[i] *= dec;
@@ -535,8 +507,55 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
                 S[i] = mfma32(S[i], bt, xl);
             }
         }
-        publish_state();
-        __syncthreads();  // the next chunk restages and reads the new state
+        __syncthreads();  // scores in LDS
+
+        // ---- phase 3: outputs Y = scores X + diag(e) (C S_in) + D x for
+        // (token block tbo[u], channel block pbo), u = 0, 1
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int tb = u == 0 ? tbo0 : tbo1;
+            const int tl = 16 * tb + r;
+            v4f acc = {0.f, 0.f, 0.f, 0.f}, off = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int sb = 0; sb < SQ / 16; ++sb) {
+                if (sb > tb) break;
+                const int k = tb * (tb + 1) / 2 + sb;
+                const v4s gh = *reinterpret_cast<const v4s *>(&sGh[k][r][4 * q]);
+                const v4s gl = *reinterpret_cast<const v4s *>(&sGl[k][r][4 * q]);
+                const v4s xf = *reinterpret_cast<const v4s *>(&sXt[16 * pbo + r][16 * sb + 4 * q]);
+                acc = mfma16(acc, gh, xf);
+                acc = mfma16(acc, gl, xf);
+            }
+#pragma unroll
+            for (int kb = 0; kb < NK; ++kb) {
+                const v8bf ca = *reinterpret_cast<const v8bf *>(&sC[tl][32 * kb + 8 * q]);
+                const v8bf sh = *reinterpret_cast<const v8bf *>(&sSh[16 * pbo + r][32 * kb + 8 * q]);
+                const v8bf sl = *reinterpret_cast<const v8bf *>(&sSl[16 * pbo + r][32 * kb + 8 * q]);
+                off = mfma32(off, ca, sh);
+                off = mfma32(off, ca, sl);
+            }
+            // acc[j], off[j] at [t = 16 tb + 4q + j][p = 16 pbo + r]
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int tj = 16 * tb + 4 * q + j;
+                const float val = fmaf(sE[tj], off[j], fmaf(dsk, bfv(sXt[16 * pbo + r][tj]), acc[j]));
+                sY[v][u][4 * q + j][r] = f32_to_bf16(val);
+            }
+        }
+        // the wave's two 16 x 16 output tiles leave as one 16-byte store per lane:
+        // lane -> tile u = lane / 32, token row (lane % 32) / 2, channels 8 (lane % 2)..+7
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        {
+            const int u = lane / 32, row = (lane % 32) / 2, seg = lane % 2;
+            const int tb = u == 0 ? tbo0 : tbo1;
+            const v4u yv = *reinterpret_cast<const v4u *>(&sY[v][u][row][8 * seg]);
+            const rsrc_t rys = make_rsrc(yb + t0 * rx, (L - t0) * rx * 2);
+            __builtin_amdgcn_raw_buffer_store_b128(
+                yv, rys, uint32_t(((16 * tb + row) * rx + 16 * pbo + 8 * seg) * 2), 0, 0);
+        }
+        __syncthreads();  // every wave is done with this chunk's staged data and state
     }
     if (hT) {
 #pragma unroll
