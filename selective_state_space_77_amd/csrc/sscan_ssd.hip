@@ -275,25 +275,35 @@ __global__ __launch_bounds__(SWV *kWave) void k_ssd(
 
 // ---------------------------------------------------------------------------
 // bf16 kernel.  8 waves per (batch row, head); each chunk of x, B, C and delta
-// is fetched with 16-byte loads one chunk ahead (into registers, while the
-// current chunk computes) and staged in LDS as bf16, in the layouts the
-// matrix operands read with single 8- or 16-byte LDS reads: x and B transposed
-// ([channel][token], [state][token]), B and C row-major ([token][state]), the
-// entering state as a bf16 high part and remainder ([channel][state]).
+// is fetched two chunks ahead (into registers, while the chunks before it
+// compute) with coalesced 16-byte loads, 8 or 16 lanes to a token's row, and
+// staged in LDS row-major ([token][channel], [token][state]) with 16-byte
+// writes.  Operands whose K runs over tokens (x and B, transposed) are read
+// with gfx950's transposing LDS read (ds_read_b64_tr_b16: each group of 16
+// lanes reads a 4 x 16 block and lane i receives its column i), from tiles
+// whose pitch keeps the four rows of a read in different banks; the state
+// entering the chunk is kept as a bf16 high part and remainder.
 // A chunk is three phases between barriers: staging (with the state
 // carried in from the previous chunk); the 10 causal 16x16 score tiles, spread
 // over the 8 waves and shared through LDS, beside the state update (wave v
 // owns channel block v % 4 and half of the state blocks: equal work); the
 // outputs, wave v taking channel block v % 4 of token blocks {0, 3} or {1, 2}
-// (equal causal work).  The scores, C S_in and the update use the K = 32
-// matrix instruction (v_mfma_f32_16x16x32_bf16); (scores) X, whose K is a
-// 16-token block of the causal triangle, the K = 16 one.
+// (equal causal work).  Every product uses the K = 32 matrix instruction
+// (v_mfma_f32_16x16x32_bf16); the outputs are formed transposed
+// (channels x tokens), so that each lane holds 4 adjacent channels of one
+// token and stores them directly.
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4bf lds_v4bf_t;
+
+__device__ __forceinline__ lds_v4bf_t *lds_v4bf(const uint16_t *p) {
+    return (lds_v4bf_t *)(p);
+}
 
 constexpr int BWV = 8;            // waves per workgroup
 constexpr int BTH = BWV * kWave;  // threads per workgroup
-constexpr int XPB = SQ + 8;       // pitch (bf16) of the [channel][token] and [state][token] tiles
 
 __device__ __forceinline__ float bfv(uint16_t u) { return __uint_as_float(uint32_t(u) << 16); }
 
@@ -314,6 +324,25 @@ __device__ __forceinline__ void split8(const float (&v)[8], v8bf &hi, v8bf &lo) 
     }
 }
 
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_or_zero(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, kRowMask, 0xF, false));
+}
+
+// inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4, 8 within each row
+// of 16 lanes (lanes without a source add 0), then the running total at the
+// end of row 0 added into row 1 and that of row 2 into row 3 (row_bcast:15),
+// then the one at lane 31 into rows 2 and 3 (row_bcast:31)
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+    v += dpp_or_zero<0x111, 0xF>(v);
+    v += dpp_or_zero<0x112, 0xF>(v);
+    v += dpp_or_zero<0x114, 0xF>(v);
+    v += dpp_or_zero<0x118, 0xF>(v);
+    v += dpp_or_zero<0x142, 0xA>(v);
+    v += dpp_or_zero<0x143, 0xC>(v);
+    return v;
+}
+
 template <int NS>
 __global__ __launch_bounds__(BTH) void k_ssd_bf(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ delta, const float *__restrict__ A,
@@ -322,20 +351,27 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
     int64_t H, int64_t G) {
     constexpr int NB = NS / 16;        // 16-wide state blocks
     constexpr int NK = NS / 32;        // 32-wide K steps over the states
-    constexpr int RP = NS + 8;         // pitch (bf16) of the [token][state] and [channel][state] tiles
+    constexpr int RP = NS + 8;         // pitch (bf16) of tiles read by rows: 16-byte reads of 8 rows
+    constexpr int TP = NS + 16;        // pitch (bf16) of B read transposed: 8-byte reads of 4 rows
+    constexpr int XP = SP + 16;        // pitch (bf16) of x, read transposed
     constexpr int NBW = NB / 2;        // state tiles per wave in the update
-    constexpr int BE = NS * SQ / BTH;  // bf16 elements of B (and of C) staged per thread
+    constexpr int LPR = NS / 8;        // lanes per row of B (or C) in a 16-byte load
+    constexpr int RPI = kWave / LPR;   // rows of B per load instruction
+    constexpr int NI = SQ / BWV / RPI; // B (and C) load instructions per wave and chunk
     constexpr int NG = 10;             // causal 16x16 score tiles of a 64-token chunk
-    static_assert(BE % 8 == 0 && SP * SQ / BTH == 8, "staging split");
-    __shared__ __align__(16) uint16_t sXt[SP][XPB];
-    __shared__ __align__(16) uint16_t sBt[NS][XPB];
-    __shared__ __align__(16) uint16_t sB[SQ][RP];
-    __shared__ __align__(16) uint16_t sC[SQ][RP];
-    __shared__ __align__(16) uint16_t sSh[SP][RP];
-    __shared__ __align__(16) uint16_t sSl[SP][RP];
-    __shared__ __align__(16) uint16_t sGh[NG][16][16];  // masked scores, A-operand layout [tile][t][s]
-    __shared__ __align__(16) uint16_t sGl[NG][16][16];
-    __shared__ __align__(16) uint16_t sY[BWV][2][16][16];  // each wave's two output tiles
+    constexpr int NM = 6;              // 16 x 32 tiles they are stored in
+    constexpr int GP = 40;             // row pitch (bf16) of the stored score tiles
+    static_assert(SQ == BWV * 8 && SP == 64 && NI * RPI * BWV == SQ, "staging split");
+    __shared__ __align__(16) uint16_t sX[SQ][XP];    // x of the chunk, [token][channel]
+    __shared__ __align__(16) uint16_t sBT[SQ][TP];   // B, [token][state], read transposed
+    __shared__ __align__(16) uint16_t sB[SQ][RP];    // B, [token][state], read by rows
+    __shared__ __align__(16) uint16_t sC[SQ][RP];    // C, [token][state]
+    __shared__ __align__(16) uint16_t sSh[SP][RP];   // entering state, [channel][state], bf16
+    __shared__ __align__(16) uint16_t sSl[SP][RP];   // and its remainder
+    // masked scores as 16 x 32 tiles [t][s] (B operand of the transposed causal product):
+    // tile m(tb, sp) holds tokens 16 tb.. and sources 32 sp..; rows padded to 40
+    __shared__ __align__(16) uint16_t sGh[NM][16][GP];
+    __shared__ __align__(16) uint16_t sGl[NM][16][GP];
     __shared__ float sCum[SQ], sGain[SQ], sW[SQ], sE[SQ];
     __shared__ float sDec;
 
@@ -359,53 +395,54 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
     const uint16_t *Cb = Cm + (b * L * G + g) * NS;
     const uint16_t *db = delta + b * L * H + h;
 
-    // ---- chunk fetch (registers) and staging (LDS).  Thread roles: token
-    // st = lane, x channels 8v..8v+7, B and C states BE*v..BE*v+BE-1 (v = wave):
-    // the transposed LDS writes of a wave then fill consecutive tokens of one
-    // row (no bank conflicts); the 16-byte global reads of a wave hit 64 rows,
-    // whose other bytes the other waves read from the same cache lines.
-    const int st = lane, c8 = v;
-    const uint32_t ox = uint32_t(st * rx * 2 + 16 * c8);  // byte offsets of this thread
-    const uint32_t obc = uint32_t(st * rbc * 2 + 2 * BE * c8);
+    // ---- chunk fetch (registers) and staging (LDS), coalesced: 8 lanes cover a
+    // token's 64 channels of x (wave v: tokens 8v..8v+7), LPR lanes a token's states
+    // of B and C (RPI tokens per instruction); staged row-major with 16-byte writes.
+    const int xs = 8 * v + lane / 8, xc = 8 * (lane % 8);
+    const uint32_t ox = uint32_t((xs * rx + xc) * 2);  // byte offsets of this thread
+    const int bc = 8 * (lane % LPR);
     const uint32_t od = uint32_t(lane * H * 2);
-    v4u px, pb[BE / 8], pc[BE / 8];
-    uint16_t pd = 0;
-    auto fetch = [&](int64_t t0) {
+    auto brow = [&](int i) { return 8 * v + RPI * i + lane / LPR; };
+    struct Chunk {  // one chunk's loads, in flight in registers
+        v4u px, pb[NI], pc[NI];
+        uint16_t pd;
+    };
+    auto fetch = [&](int64_t t0, Chunk &P) {
+        // the loads of one fetch stay together and in order (no scheduling across
+        // these points): the compiler's wait before a stage then counts only the
+        // operations issued after that chunk's loads
+        __builtin_amdgcn_sched_barrier(0);
         const rsrc_t rxs = make_rsrc(xb + t0 * rx, (L - t0) * rx * 2);
         const rsrc_t rbs = make_rsrc(Bb + t0 * rbc, (L - t0) * rbc * 2);
         const rsrc_t rcs = make_rsrc(Cb + t0 * rbc, (L - t0) * rbc * 2);
-        px = __builtin_amdgcn_raw_buffer_load_b128(rxs, ox, 0, 0);
+        P.px = __builtin_amdgcn_raw_buffer_load_b128(rxs, ox, 0, 0);
 #pragma unroll
-        for (int i = 0; i < BE / 8; ++i) {
-            pb[i] = __builtin_amdgcn_raw_buffer_load_b128(rbs, obc + 16 * i, 0, 0);
-            pc[i] = __builtin_amdgcn_raw_buffer_load_b128(rcs, obc + 16 * i, 0, 0);
+        for (int i = 0; i < NI; ++i) {
+            const uint32_t o = uint32_t((brow(i) * rbc + bc) * 2);
+            P.pb[i] = __builtin_amdgcn_raw_buffer_load_b128(rbs, o, 0, 0);
+            P.pc[i] = __builtin_amdgcn_raw_buffer_load_b128(rcs, o, 0, 0);
         }
-        if (v == 0) pd = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(db + t0 * H, (L - t0) * H * 2), od, 0, 0);
+        // delta: wave 0 only (the other waves' descriptor is empty, so their load
+        // reads 0 without a memory access and without a branch around it)
+        P.pd = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(db + t0 * H, v == 0 ? (L - t0) * H * 2 : 0), od, 0,
+                                                    0);
+        __builtin_amdgcn_sched_barrier(0);
     };
-    auto stage = [&]() {
-        const uint16_t *xv = reinterpret_cast<const uint16_t *>(&px);
+    auto stage = [&](const Chunk &P) {
+        *reinterpret_cast<v4u *>(&sX[xs][xc]) = P.px;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) sXt[8 * c8 + k][st] = xv[k];
-#pragma unroll
-        for (int i = 0; i < BE / 8; ++i) {
-            *reinterpret_cast<v4u *>(&sB[st][BE * c8 + 8 * i]) = pb[i];
-            *reinterpret_cast<v4u *>(&sC[st][BE * c8 + 8 * i]) = pc[i];
-            const uint16_t *bv = reinterpret_cast<const uint16_t *>(&pb[i]);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) sBt[BE * c8 + 8 * i + k][st] = bv[k];
+        for (int i = 0; i < NI; ++i) {
+            *reinterpret_cast<v4u *>(&sB[brow(i)][bc]) = P.pb[i];
+            *reinterpret_cast<v4u *>(&sBT[brow(i)][bc]) = P.pb[i];
+            *reinterpret_cast<v4u *>(&sC[brow(i)][bc]) = P.pc[i];
         }
         // per-token scalars (wave 0, lane = token): running sum of delta
         // (inclusive), gain, state weight, output decay; chunk decay.  Tokens
         // past the end have delta = 0: gain 0, decay 1.
         if (v == 0) {
-            const float dv = bfv(pd);
-            float cum = dv;
-#pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) {
-                const float u = __shfl_up(cum, off);
-                if (lane >= off) cum += u;
-            }
-            const float total = __shfl(cum, kWave - 1);
+            const float dv = bfv(P.pd);
+            const float cum = wave_prefix_sum(dv);
+            const float total = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cum), kWave - 1));
             const float gain = zoh_gain(dv, a, dv * a, exp2_hw(dv * a2));  // delta when A = 0
             sCum[lane] = cum;
             sGain[lane] = gain;
@@ -414,16 +451,31 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
             if (lane == 0) sDec = exp2_hw(a2 * total);
         }
     };
+    // K = 32 operand from a [k][column] tile: lane (r, q) gets rows k0 + 8q .. k0 + 8q + 7
+    // of column c0 + r, as two transposing 8-byte reads (each 16-lane group reads a
+    // 4 x 16 block, lane i of the group the 4 elements at row i / 4, column 4 (i % 4))
+    auto ld_t = [&](const uint16_t *tile, int pitch, int k0, int c0) {
+        const int row = k0 + 8 * q + r / 4, col = c0 + 4 * (r % 4);
+        const v4bf lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lds_v4bf(tile + row * pitch + col));
+        const v4bf hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lds_v4bf(tile + (row + 4) * pitch + col));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
 
     // ---- state tiles of this wave: channel block pbs, state blocks nb0..nb0+NBW-1;
     // S[i][j] = S[n = 16(nb0 + i) + 4q + j][p = 16 pbs + r]
     const int pbs = v % 4, nb0 = NBW * (v / 4);
     v4f S[NBW];
     const int64_t srow = ((b * H + h) * SP + 16 * pbs + r) * NS;
+    {
+        // the initial state through a descriptor of 0 bytes when there is none (reads
+        // 0): no branch around these loads, which would make the compiler wait for
+        // every outstanding load at the loop head
+        const rsrc_t rh = make_rsrc(h0 ? h0 + (b * H + h) * SP * NS : nullptr, h0 ? SP * NS * 4 : 0);
 #pragma unroll
-    for (int i = 0; i < NBW; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) S[i][j] = h0 ? h0[srow + 16 * (nb0 + i) + 4 * q + j] : 0.f;
+        for (int i = 0; i < NBW; ++i)
+            S[i] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                                               rh, uint32_t(((16 * pbs + r) * NS + 16 * (nb0 + i) + 4 * q) * 4), 0, 0));
+    }
     auto publish_state = [&]() {
 #pragma unroll
         for (int i = 0; i < NBW; ++i) {
@@ -440,24 +492,36 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
     };
 
     // causal score tile k (0..9) = (token block tb, source block sb <= tb), row-major
-    // over the triangle; tile_of(tb, sb) = tb (tb + 1) / 2 + sb
+    // over the triangle
     // outputs of this wave: channel block pbo, token blocks tbo[0] + tbo[1] = 3 (equal work)
     const int pbo = v % 4;
     const int tbo0 = v < 4 ? 0 : 1, tbo1 = 3 - tbo0;
 
-    fetch(0);
+    // the two 16 x 16 halves of the stored tiles above the diagonal blocks,
+    // (tb 0, sb 1) and (tb 2, sb 3), are never written and stay zero
+    auto tile32 = [](int tb, int sp) { return tb < 2 ? tb : 2 * tb - 2 + sp; };
+    if (v == 0) *reinterpret_cast<v4s *>(&sGh[tile32(0, 0)][r][16 + 4 * q]) = v4s{0, 0, 0, 0};
+    if (v == 1) *reinterpret_cast<v4s *>(&sGl[tile32(0, 0)][r][16 + 4 * q]) = v4s{0, 0, 0, 0};
+    if (v == 2) *reinterpret_cast<v4s *>(&sGh[tile32(2, 1)][r][16 + 4 * q]) = v4s{0, 0, 0, 0};
+    if (v == 3) *reinterpret_cast<v4s *>(&sGl[tile32(2, 1)][r][16 + 4 * q]) = v4s{0, 0, 0, 0};
+
+    // chunk c is fetched during chunks c - 2 and c - 1 (two register sets, taken in
+    // turn).  Chunks go in pairs, so an odd count ends with one past the end of the
+    // sequence: its loads read 0 (delta 0: decay 1, gain 0, the state unchanged) and
+    // its stores are dropped.  Fetches past the end are likewise unconditional: with
+    // no branch around them the compiler waits only for the loads a stage needs.
     const int64_t nchunks = (L + SQ - 1) / SQ;
-    for (int64_t c = 0; c < nchunks; ++c) {
+    auto chunk = [&](int64_t c, Chunk &P) {
         const int64_t t0 = c * SQ;
         publish_state();  // the state entering this chunk
-        stage();
+        stage(P);
         __syncthreads();
-        if (c + 1 < nchunks) fetch(t0 + SQ);  // next chunk, in flight during this one
+        fetch(t0 + 2 * SQ, P);
 
         // ---- phase 2a: causal score tiles, spread over the waves (k = v, v + 8):
         // G^T tile (s-block sb, t-block tb) = B C^T, times exp(A (cum_t - cum_s)) gain_s
-        // where s <= t, split into bf16 parts and stored in the A-operand layout
-        // of (scores) X: lane (t = r, k = s = 4q + j)
+        // where s <= t, plus the skip D on the diagonal (D x is then part of the
+        // causal product), split into bf16 parts and stored as rows t, columns s
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             const int k = v + 8 * kk;
@@ -478,13 +542,13 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
             for (int j = 0; j < 4; ++j) {
                 const int sl = 16 * sb + 4 * q + j;
                 const float m = acc[j] * exp2_hw(a2 * (cum_t - sCum[sl])) * sGain[sl];
-                const float gv = sl <= tl ? m : 0.f;
+                const float gv = sl < tl ? m : sl == tl ? m + dsk : 0.f;
                 const uint16_t hb = f32_to_bf16(gv);
                 hi[j] = short(hb);
                 lo[j] = short(f32_to_bf16(gv - bfv(hb)));
             }
-            *reinterpret_cast<v4s *>(&sGh[k][r][4 * q]) = hi;
-            *reinterpret_cast<v4s *>(&sGl[k][r][4 * q]) = lo;
+            *reinterpret_cast<v4s *>(&sGh[tile32(tb, sb / 2)][r][16 * (sb % 2) + 4 * q]) = hi;
+            *reinterpret_cast<v4s *>(&sGl[tile32(tb, sb / 2)][r][16 * (sb % 2) + 4 * q]) = lo;
         }
         // ---- phase 2b: state update (registers): S = exp(A sum delta) S + B^T diag(w) X
         const float dec = sDec;
@@ -492,70 +556,67 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
         for (int i = 0; i < NBW; ++i) S[i] *= dec;
 #pragma unroll
         for (int kb = 0; kb < SQ / 32; ++kb) {
+            const v8bf xt = ld_t(&sX[0][0], XP, 32 * kb, 16 * pbs);  // x[s = 32kb + 8q + j][16 pbs + r]
             float xw[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int sl = 32 * kb + 8 * q + j;
-                xw[j] = bfv(sXt[16 * pbs + r][sl]) * sW[sl];
-            }
+            for (int j = 0; j < 8; ++j) xw[j] = static_cast<float>(xt[j]) * sW[32 * kb + 8 * q + j];
             v8bf xh, xl;
             split8(xw, xh, xl);
 #pragma unroll
             for (int i = 0; i < NBW; ++i) {
-                const v8bf bt = *reinterpret_cast<const v8bf *>(&sBt[16 * (nb0 + i) + r][32 * kb + 8 * q]);
+                const v8bf bt = ld_t(&sBT[0][0], TP, 32 * kb, 16 * (nb0 + i));  // B[s][16(nb0 + i) + r]
                 S[i] = mfma32(S[i], bt, xh);
                 S[i] = mfma32(S[i], bt, xl);
             }
         }
         __syncthreads();  // scores in LDS
 
-        // ---- phase 3: outputs Y = scores X + diag(e) (C S_in) + D x for
-        // (token block tbo[u], channel block pbo), u = 0, 1
+        // ---- phase 3: outputs, transposed: Y^T = X^T G'^T + (S_in C^T) diag(e) for
+        // (channel block pbo, token block tbo[u]), u = 0, 1; lane (r, q) ends with
+        // channels 16 pbo + 4q .. + 3 of token 16 tb + r and stores them as 8 bytes
+        v8bf sh[NK], sl[NK];
+#pragma unroll
+        for (int kb = 0; kb < NK; ++kb) {
+            sh[kb] = *reinterpret_cast<const v8bf *>(&sSh[16 * pbo + r][32 * kb + 8 * q]);
+            sl[kb] = *reinterpret_cast<const v8bf *>(&sSl[16 * pbo + r][32 * kb + 8 * q]);
+        }
+        const rsrc_t rys = make_rsrc(yb + t0 * rx, (L - t0) * rx * 2);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int tb = u == 0 ? tbo0 : tbo1;
             const int tl = 16 * tb + r;
             v4f acc = {0.f, 0.f, 0.f, 0.f}, off = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int sb = 0; sb < SQ / 16; ++sb) {
-                if (sb > tb) break;
-                const int k = tb * (tb + 1) / 2 + sb;
-                const v4s gh = *reinterpret_cast<const v4s *>(&sGh[k][r][4 * q]);
-                const v4s gl = *reinterpret_cast<const v4s *>(&sGl[k][r][4 * q]);
-                const v4s xf = *reinterpret_cast<const v4s *>(&sXt[16 * pbo + r][16 * sb + 4 * q]);
-                acc = mfma16(acc, gh, xf);
-                acc = mfma16(acc, gl, xf);
+            for (int sp = 0; sp < 2; ++sp) {
+                if (32 * sp > 16 * tb + 15) break;
+                const int m = tile32(tb, sp);
+                const v8bf xa = ld_t(&sX[0][0], XP, 32 * sp, 16 * pbo);  // x[s = 32sp + 8q + j][16 pbo + r]
+                const v8bf gh = *reinterpret_cast<const v8bf *>(&sGh[m][r][8 * q]);
+                const v8bf gl = *reinterpret_cast<const v8bf *>(&sGl[m][r][8 * q]);
+                acc = mfma32(acc, xa, gh);
+                acc = mfma32(acc, xa, gl);
             }
 #pragma unroll
             for (int kb = 0; kb < NK; ++kb) {
-                const v8bf ca = *reinterpret_cast<const v8bf *>(&sC[tl][32 * kb + 8 * q]);
-                const v8bf sh = *reinterpret_cast<const v8bf *>(&sSh[16 * pbo + r][32 * kb + 8 * q]);
-                const v8bf sl = *reinterpret_cast<const v8bf *>(&sSl[16 * pbo + r][32 * kb + 8 * q]);
-                off = mfma32(off, ca, sh);
-                off = mfma32(off, ca, sl);
+                const v8bf cb = *reinterpret_cast<const v8bf *>(&sC[tl][32 * kb + 8 * q]);
+                off = mfma32(off, sh[kb], cb);
+                off = mfma32(off, sl[kb], cb);
             }
-            // acc[j], off[j] at [t = 16 tb + 4q + j][p = 16 pbo + r]
+            const float e = sE[tl];
+            v4s yv;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int tj = 16 * tb + 4 * q + j;
-                const float val = fmaf(sE[tj], off[j], fmaf(dsk, bfv(sXt[16 * pbo + r][tj]), acc[j]));
-                sY[v][u][4 * q + j][r] = f32_to_bf16(val);
-            }
-        }
-        // the wave's two 16 x 16 output tiles leave as one 16-byte store per lane:
-        // lane -> tile u = lane / 32, token row (lane % 32) / 2, channels 8 (lane % 2)..+7
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        {
-            const int u = lane / 32, row = (lane % 32) / 2, seg = lane % 2;
-            const int tb = u == 0 ? tbo0 : tbo1;
-            const v4u yv = *reinterpret_cast<const v4u *>(&sY[v][u][row][8 * seg]);
-            const rsrc_t rys = make_rsrc(yb + t0 * rx, (L - t0) * rx * 2);
-            __builtin_amdgcn_raw_buffer_store_b128(
-                yv, rys, uint32_t(((16 * tb + row) * rx + 16 * pbo + 8 * seg) * 2), 0, 0);
+            for (int j = 0; j < 4; ++j) yv[j] = short(f32_to_bf16(fmaf(e, off[j], acc[j])));
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, yv), rys,
+                                                  uint32_t((tl * rx + 16 * pbo + 4 * q) * 2), 0, 0);
         }
         __syncthreads();  // every wave is done with this chunk's staged data and state
+    };
+    Chunk P0, P1;
+    fetch(0, P0);
+    fetch(SQ, P1);
+    for (int64_t c = 0; c < nchunks; c += 2) {
+        chunk(c, P0);
+        chunk(c + 1, P1);
     }
     if (hT) {
 #pragma unroll
