@@ -363,6 +363,8 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
     constexpr int GP = 40;             // row pitch (bf16) of the stored score tiles
     static_assert(SQ == BWV * 8 && SP == 64 && NI * RPI * BWV == SQ, "staging split");
     __shared__ __align__(16) uint16_t sX[SQ][XP];    // x of the chunk, [token][channel]
+    __shared__ __align__(16) uint16_t sXWh[SQ][XP];  // w_s x, bf16 high part
+    __shared__ __align__(16) uint16_t sXWl[SQ][XP];  // and remainder
     __shared__ __align__(16) uint16_t sBT[SQ][TP];   // B, [token][state], read transposed
     __shared__ __align__(16) uint16_t sB[SQ][RP];    // B, [token][state], read by rows
     __shared__ __align__(16) uint16_t sC[SQ][RP];    // C, [token][state]
@@ -372,8 +374,10 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
     // tile m(tb, sp) holds tokens 16 tb.. and sources 32 sp..; rows padded to 40
     __shared__ __align__(16) uint16_t sGh[NM][16][GP];
     __shared__ __align__(16) uint16_t sGl[NM][16][GP];
-    __shared__ float sCum[SQ], sGain[SQ], sW[SQ], sE[SQ];
-    __shared__ float sDec;
+    // per-token scalars, two sets: those of chunk c + 1 are formed during chunk c
+    __shared__ float sCum[2][SQ], sGain[2][SQ], sW[2][SQ], sE[2][SQ];
+    __shared__ float sDec[2];
+    constexpr int kScalarWave = 3;  // a wave with one score tile
 
     const int tid = int(threadIdx.x);
     const int v = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -422,33 +426,46 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
             P.pb[i] = __builtin_amdgcn_raw_buffer_load_b128(rbs, o, 0, 0);
             P.pc[i] = __builtin_amdgcn_raw_buffer_load_b128(rcs, o, 0, 0);
         }
-        // delta: wave 0 only (the other waves' descriptor is empty, so their load
-        // reads 0 without a memory access and without a branch around it)
-        P.pd = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(db + t0 * H, v == 0 ? (L - t0) * H * 2 : 0), od, 0,
-                                                    0);
+        // delta: the scalar wave only (the other waves' descriptor is empty, so their
+        // load reads 0 without a memory access and without a branch around it)
+        P.pd = __builtin_amdgcn_raw_buffer_load_b16(
+            make_rsrc(db + t0 * H, v == kScalarWave ? (L - t0) * H * 2 : 0), od, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
-    auto stage = [&](const Chunk &P) {
+    // per-token scalars of a chunk (the scalar wave, lane = token): running sum of
+    // delta (inclusive), gain, state weight, output decay; chunk decay.  Tokens
+    // past the end have delta = 0: gain 0, decay 1.
+    auto scalars = [&](const Chunk &P, int par) {
+        const float dv = bfv(P.pd);
+        const float cum = wave_prefix_sum(dv);
+        const float total = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cum), kWave - 1));
+        const float gain = zoh_gain(dv, a, dv * a, exp2_hw(dv * a2));  // delta when A = 0
+        sCum[par][lane] = cum;
+        sGain[par][lane] = gain;
+        sW[par][lane] = exp2_hw(a2 * (total - cum)) * gain;
+        sE[par][lane] = exp2_hw(a2 * cum);
+        if (lane == 0) sDec[par] = exp2_hw(a2 * total);
+    };
+    // staging; x also as w_s x split into bf16 parts (the update's operand, formed
+    // once here rather than by both waves that share a channel block)
+    auto stage = [&](const Chunk &P, int par) {
         *reinterpret_cast<v4u *>(&sX[xs][xc]) = P.px;
+        {
+            const float w = sW[par][xs];
+            const uint16_t *xv = reinterpret_cast<const uint16_t *>(&P.px);
+            float xw[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) xw[j] = bfv(xv[j]) * w;
+            v8bf xh, xl;
+            split8(xw, xh, xl);
+            *reinterpret_cast<v8bf *>(&sXWh[xs][xc]) = xh;
+            *reinterpret_cast<v8bf *>(&sXWl[xs][xc]) = xl;
+        }
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             *reinterpret_cast<v4u *>(&sB[brow(i)][bc]) = P.pb[i];
             *reinterpret_cast<v4u *>(&sBT[brow(i)][bc]) = P.pb[i];
             *reinterpret_cast<v4u *>(&sC[brow(i)][bc]) = P.pc[i];
-        }
-        // per-token scalars (wave 0, lane = token): running sum of delta
-        // (inclusive), gain, state weight, output decay; chunk decay.  Tokens
-        // past the end have delta = 0: gain 0, decay 1.
-        if (v == 0) {
-            const float dv = bfv(P.pd);
-            const float cum = wave_prefix_sum(dv);
-            const float total = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cum), kWave - 1));
-            const float gain = zoh_gain(dv, a, dv * a, exp2_hw(dv * a2));  // delta when A = 0
-            sCum[lane] = cum;
-            sGain[lane] = gain;
-            sW[lane] = exp2_hw(a2 * (total - cum)) * gain;
-            sE[lane] = exp2_hw(a2 * cum);
-            if (lane == 0) sDec = exp2_hw(a2 * total);
         }
     };
     // K = 32 operand from a [k][column] tile: lane (r, q) gets rows k0 + 8q .. k0 + 8q + 7
@@ -511,12 +528,14 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
     // its stores are dropped.  Fetches past the end are likewise unconditional: with
     // no branch around them the compiler waits only for the loads a stage needs.
     const int64_t nchunks = (L + SQ - 1) / SQ;
-    auto chunk = [&](int64_t c, Chunk &P) {
+    auto chunk = [&](int64_t c, Chunk &P, const Chunk &Pn) {
         const int64_t t0 = c * SQ;
+        const int par = int(c & 1);  // which scalar set
         publish_state();  // the state entering this chunk
-        stage(P);
+        stage(P, par);
         __syncthreads();
         fetch(t0 + 2 * SQ, P);
+        if (v == kScalarWave) scalars(Pn, par ^ 1);  // for chunk c + 1
 
         // ---- phase 2a: causal score tiles, spread over the waves (k = v, v + 8):
         // G^T tile (s-block sb, t-block tb) = B C^T, times exp(A (cum_t - cum_s)) gain_s
@@ -536,12 +555,12 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
                 const v8bf cf = *reinterpret_cast<const v8bf *>(&sC[tl][32 * kb + 8 * q]);
                 acc = mfma32(acc, bf, cf);
             }
-            const float cum_t = sCum[tl];
+            const float cum_t = sCum[par][tl];
             v4s hi, lo;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int sl = 16 * sb + 4 * q + j;
-                const float m = acc[j] * exp2_hw(a2 * (cum_t - sCum[sl])) * sGain[sl];
+                const float m = acc[j] * exp2_hw(a2 * (cum_t - sCum[par][sl])) * sGain[par][sl];
                 const float gv = sl < tl ? m : sl == tl ? m + dsk : 0.f;
                 const uint16_t hb = f32_to_bf16(gv);
                 hi[j] = short(hb);
@@ -551,17 +570,14 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
             *reinterpret_cast<v4s *>(&sGl[tile32(tb, sb / 2)][r][16 * (sb % 2) + 4 * q]) = lo;
         }
         // ---- phase 2b: state update (registers): S = exp(A sum delta) S + B^T diag(w) X
-        const float dec = sDec;
+        const float dec = sDec[par];
 #pragma unroll
         for (int i = 0; i < NBW; ++i) S[i] *= dec;
 #pragma unroll
         for (int kb = 0; kb < SQ / 32; ++kb) {
-            const v8bf xt = ld_t(&sX[0][0], XP, 32 * kb, 16 * pbs);  // x[s = 32kb + 8q + j][16 pbs + r]
-            float xw[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) xw[j] = static_cast<float>(xt[j]) * sW[32 * kb + 8 * q + j];
-            v8bf xh, xl;
-            split8(xw, xh, xl);
+            // (w x)[s = 32kb + 8q + j][16 pbs + r], both parts
+            const v8bf xh = ld_t(&sXWh[0][0], XP, 32 * kb, 16 * pbs);
+            const v8bf xl = ld_t(&sXWl[0][0], XP, 32 * kb, 16 * pbs);
 #pragma unroll
             for (int i = 0; i < NBW; ++i) {
                 const v8bf bt = ld_t(&sBT[0][0], TP, 32 * kb, 16 * (nb0 + i));  // B[s][16(nb0 + i) + r]
@@ -602,7 +618,7 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
                 off = mfma32(off, sh[kb], cb);
                 off = mfma32(off, sl[kb], cb);
             }
-            const float e = sE[tl];
+            const float e = sE[par][tl];
             v4s yv;
 #pragma unroll
             for (int j = 0; j < 4; ++j) yv[j] = short(f32_to_bf16(fmaf(e, off[j], acc[j])));
@@ -614,9 +630,11 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
     Chunk P0, P1;
     fetch(0, P0);
     fetch(SQ, P1);
+    if (v == kScalarWave) scalars(P0, 0);
+    __syncthreads();
     for (int64_t c = 0; c < nchunks; c += 2) {
-        chunk(c, P0);
-        chunk(c + 1, P1);
+        chunk(c, P0, P1);
+        chunk(c + 1, P1, P0);
     }
     if (hT) {
 #pragma unroll
