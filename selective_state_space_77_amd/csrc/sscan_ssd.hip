@@ -298,11 +298,16 @@ typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4bf lds_v4bf_t;
 
+// raw buffer descriptor over `bytes` (< 2^31) bytes from `base`
+__device__ __forceinline__ rsrc_t make_rsrc32(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), short(0), int(bytes), 0x00020000);
+}
+
 __device__ __forceinline__ lds_v4bf_t *lds_v4bf(const uint16_t *p) {
     return (lds_v4bf_t *)(p);
 }
 
-constexpr int BWV = 8;            // waves per workgroup
+constexpr int BWV = 16;           // waves per workgroup
 constexpr int BTH = BWV * kWave;  // threads per workgroup
 
 __device__ __forceinline__ float bfv(uint16_t u) { return __uint_as_float(uint32_t(u) << 16); }
@@ -349,19 +354,18 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
     const uint16_t *__restrict__ Bm, const uint16_t *__restrict__ Cm, const float *__restrict__ Dskip,
     const float *__restrict__ h0, uint16_t *__restrict__ y, float *__restrict__ hT, int64_t L,
     int64_t H, int64_t G) {
-    constexpr int NB = NS / 16;        // 16-wide state blocks
     constexpr int NK = NS / 32;        // 32-wide K steps over the states
     constexpr int RP = NS + 8;         // pitch (bf16) of tiles read by rows: 16-byte reads of 8 rows
     constexpr int TP = NS + 16;        // pitch (bf16) of B read transposed: 8-byte reads of 4 rows
     constexpr int XP = SP + 16;        // pitch (bf16) of x, read transposed
-    constexpr int NBW = NB / 2;        // state tiles per wave in the update
-    constexpr int LPR = NS / 8;        // lanes per row of B (or C) in a 16-byte load
-    constexpr int RPI = kWave / LPR;   // rows of B per load instruction
-    constexpr int NI = SQ / BWV / RPI; // B (and C) load instructions per wave and chunk
+    constexpr int NBW = NS / 64;       // 16x16 state tiles per wave (4 channel blocks x NS/16 state blocks)
+    constexpr int BPL = NS / 16;       // bf16 of a B (or C) row per lane: 16 lanes to a row
     constexpr int NG = 10;             // causal 16x16 score tiles of a 64-token chunk
     constexpr int NM = 6;              // 16 x 32 tiles they are stored in
     constexpr int GP = 40;             // row pitch (bf16) of the stored score tiles
-    static_assert(SQ == BWV * 8 && SP == 64 && NI * RPI * BWV == SQ, "staging split");
+    constexpr int kScalarWave = 11;    // a wave without a score tile, on a SIMD with two of them
+    static_assert(BWV == 16 && SQ == 64 && SP == 64, "work split");
+    using VB = typename std::conditional<BPL == 8, v4u, v2u>::type;
     __shared__ __align__(16) uint16_t sX[SQ][XP];    // x of the chunk, [token][channel]
     __shared__ __align__(16) uint16_t sXWh[SQ][XP];  // w_s x, bf16 high part
     __shared__ __align__(16) uint16_t sXWl[SQ][XP];  // and remainder
@@ -377,7 +381,6 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
     // per-token scalars, two sets: those of chunk c + 1 are formed during chunk c
     __shared__ float sCum[2][SQ], sGain[2][SQ], sW[2][SQ], sE[2][SQ];
     __shared__ float sDec[2];
-    constexpr int kScalarWave = 3;  // a wave with one score tile
 
     const int tid = int(threadIdx.x);
     const int v = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -390,8 +393,8 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
     const float dsk = Dskip ? Dskip[h] : 0.f;
     // row t of this (batch row, head): x and y at xb/yb + t*rx, B/C at Bb/Cb + t*rbc,
     // delta at db + t*H (elements).  Each chunk reads and writes through buffer
-    // descriptors over [t0, L): 32-bit offsets, and tokens past the end read 0
-    // and drop their stores in the hardware range check.
+    // descriptors over its tokens inside the sequence: 32-bit offsets, and tokens
+    // past the end read 0 and drop their stores in the hardware range check.
     const int64_t rx = H * SP, rbc = G * NS;
     const uint16_t *xb = x + (b * L * H + h) * SP;
     uint16_t *yb = y + (b * L * H + h) * SP;
@@ -399,37 +402,40 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
     const uint16_t *Cb = Cm + (b * L * G + g) * NS;
     const uint16_t *db = delta + b * L * H + h;
 
-    // ---- chunk fetch (registers) and staging (LDS), coalesced: 8 lanes cover a
-    // token's 64 channels of x (wave v: tokens 8v..8v+7), LPR lanes a token's states
-    // of B and C (RPI tokens per instruction); staged row-major with 16-byte writes.
-    const int xs = 8 * v + lane / 8, xc = 8 * (lane % 8);
-    const uint32_t ox = uint32_t((xs * rx + xc) * 2);  // byte offsets of this thread
-    const int bc = 8 * (lane % LPR);
+    // ---- chunk fetch (registers) and staging (LDS), coalesced: 16 lanes to a
+    // token's row (8 bytes of x, BPL states of B and C each), wave v taking tokens
+    // 4v..4v+3; staged row-major.
+    const int srow = 4 * v + lane / 16;
+    const int xc = 4 * (lane % 16), bc = BPL * (lane % 16);
+    const uint32_t ox = uint32_t((srow * rx + xc) * 2), ob = uint32_t((srow * rbc + bc) * 2);
     const uint32_t od = uint32_t(lane * H * 2);
-    auto brow = [&](int i) { return 8 * v + RPI * i + lane / LPR; };
     struct Chunk {  // one chunk's loads, in flight in registers
-        v4u px, pb[NI], pc[NI];
+        v2u px;
+        VB pb, pc;
         uint16_t pd;
     };
-    auto fetch = [&](int64_t t0, Chunk &P) {
+    // tokens of chunk c inside the sequence (64, the tail, or 0 past the end); a
+    // chunk's bytes fit in 32 bits and the chunk count in 31 (checked at launch)
+    const int nfull = int(L / SQ), tail = int(L % SQ);
+    auto toks = [&](int c) { return uint32_t(c < nfull ? SQ : c == nfull ? tail : 0); };
+    auto ldb = [&](rsrc_t rs, uint32_t o) {
+        if constexpr (BPL == 8) return __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, 0);
+        else return __builtin_amdgcn_raw_buffer_load_b64(rs, o, 0, 0);
+    };
+    auto fetch = [&](int c, Chunk &P) {
         // the loads of one fetch stay together and in order (no scheduling across
         // these points): the compiler's wait before a stage then counts only the
         // operations issued after that chunk's loads
         __builtin_amdgcn_sched_barrier(0);
-        const rsrc_t rxs = make_rsrc(xb + t0 * rx, (L - t0) * rx * 2);
-        const rsrc_t rbs = make_rsrc(Bb + t0 * rbc, (L - t0) * rbc * 2);
-        const rsrc_t rcs = make_rsrc(Cb + t0 * rbc, (L - t0) * rbc * 2);
-        P.px = __builtin_amdgcn_raw_buffer_load_b128(rxs, ox, 0, 0);
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const uint32_t o = uint32_t((brow(i) * rbc + bc) * 2);
-            P.pb[i] = __builtin_amdgcn_raw_buffer_load_b128(rbs, o, 0, 0);
-            P.pc[i] = __builtin_amdgcn_raw_buffer_load_b128(rcs, o, 0, 0);
-        }
+        const int64_t t0 = int64_t(c) * SQ;
+        const uint32_t n = toks(c);
+        P.px = __builtin_amdgcn_raw_buffer_load_b64(make_rsrc32(xb + t0 * rx, n * uint32_t(rx) * 2), ox, 0, 0);
+        P.pb = ldb(make_rsrc32(Bb + t0 * rbc, n * uint32_t(rbc) * 2), ob);
+        P.pc = ldb(make_rsrc32(Cb + t0 * rbc, n * uint32_t(rbc) * 2), ob);
         // delta: the scalar wave only (the other waves' descriptor is empty, so their
         // load reads 0 without a memory access and without a branch around it)
         P.pd = __builtin_amdgcn_raw_buffer_load_b16(
-            make_rsrc(db + t0 * H, v == kScalarWave ? (L - t0) * H * 2 : 0), od, 0, 0);
+            make_rsrc32(db + t0 * H, v == kScalarWave ? n * uint32_t(H) * 2 : 0), od, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
     // per-token scalars of a chunk (the scalar wave, lane = token): running sum of
@@ -447,26 +453,26 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
         if (lane == 0) sDec[par] = exp2_hw(a2 * total);
     };
     // staging; x also as w_s x split into bf16 parts (the update's operand, formed
-    // once here rather than by both waves that share a channel block)
+    // once here rather than by the waves that share a channel block)
     auto stage = [&](const Chunk &P, int par) {
-        *reinterpret_cast<v4u *>(&sX[xs][xc]) = P.px;
+        *reinterpret_cast<v2u *>(&sX[srow][xc]) = P.px;
         {
-            const float w = sW[par][xs];
+            const float w = sW[par][srow];
             const uint16_t *xv = reinterpret_cast<const uint16_t *>(&P.px);
-            float xw[8];
+            v4s hi, lo;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) xw[j] = bfv(xv[j]) * w;
-            v8bf xh, xl;
-            split8(xw, xh, xl);
-            *reinterpret_cast<v8bf *>(&sXWh[xs][xc]) = xh;
-            *reinterpret_cast<v8bf *>(&sXWl[xs][xc]) = xl;
+            for (int j = 0; j < 4; ++j) {
+                const float xw = bfv(xv[j]) * w;
+                const uint16_t hb = f32_to_bf16(xw);
+                hi[j] = short(hb);
+                lo[j] = short(f32_to_bf16(xw - bfv(hb)));
+            }
+            *reinterpret_cast<v4s *>(&sXWh[srow][xc]) = hi;
+            *reinterpret_cast<v4s *>(&sXWl[srow][xc]) = lo;
         }
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            *reinterpret_cast<v4u *>(&sB[brow(i)][bc]) = P.pb[i];
-            *reinterpret_cast<v4u *>(&sBT[brow(i)][bc]) = P.pb[i];
-            *reinterpret_cast<v4u *>(&sC[brow(i)][bc]) = P.pc[i];
-        }
+        *reinterpret_cast<VB *>(&sB[srow][bc]) = P.pb;
+        *reinterpret_cast<VB *>(&sBT[srow][bc]) = P.pb;
+        *reinterpret_cast<VB *>(&sC[srow][bc]) = P.pc;
     };
     // K = 32 operand from a [k][column] tile: lane (r, q) gets rows k0 + 8q .. k0 + 8q + 7
     // of column c0 + r, as two transposing 8-byte reads (each 16-lane group reads a
@@ -482,12 +488,12 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
     // S[i][j] = S[n = 16(nb0 + i) + 4q + j][p = 16 pbs + r]
     const int pbs = v % 4, nb0 = NBW * (v / 4);
     v4f S[NBW];
-    const int64_t srow = ((b * H + h) * SP + 16 * pbs + r) * NS;
+    const int64_t hrow = ((b * H + h) * SP + 16 * pbs + r) * NS;
     {
         // the initial state through a descriptor of 0 bytes when there is none (reads
         // 0): no branch around these loads, which would make the compiler wait for
         // every outstanding load at the loop head
-        const rsrc_t rh = make_rsrc(h0 ? h0 + (b * H + h) * SP * NS : nullptr, h0 ? SP * NS * 4 : 0);
+        const rsrc_t rh = make_rsrc32(h0 ? h0 + (b * H + h) * SP * NS : nullptr, h0 ? SP * NS * 4 : 0);
 #pragma unroll
         for (int i = 0; i < NBW; ++i)
             S[i] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
@@ -508,43 +514,39 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
         }
     };
 
-    // causal score tile k (0..9) = (token block tb, source block sb <= tb), row-major
-    // over the triangle
-    // outputs of this wave: channel block pbo, token blocks tbo[0] + tbo[1] = 3 (equal work)
-    const int pbo = v % 4;
-    const int tbo0 = v < 4 ? 0 : 1, tbo1 = 3 - tbo0;
+    // output tile of this wave: channel block pbo, token block tbo
+    const int pbo = v % 4, tbo = v / 4;
 
     // the two 16 x 16 halves of the stored tiles above the diagonal blocks,
     // (tb 0, sb 1) and (tb 2, sb 3), are never written and stay zero
     auto tile32 = [](int tb, int sp) { return tb < 2 ? tb : 2 * tb - 2 + sp; };
-    if (v == 0) *reinterpret_cast<v4s *>(&sGh[tile32(0, 0)][r][16 + 4 * q]) = v4s{0, 0, 0, 0};
-    if (v == 1) *reinterpret_cast<v4s *>(&sGl[tile32(0, 0)][r][16 + 4 * q]) = v4s{0, 0, 0, 0};
-    if (v == 2) *reinterpret_cast<v4s *>(&sGh[tile32(2, 1)][r][16 + 4 * q]) = v4s{0, 0, 0, 0};
-    if (v == 3) *reinterpret_cast<v4s *>(&sGl[tile32(2, 1)][r][16 + 4 * q]) = v4s{0, 0, 0, 0};
+    if (v == 12) *reinterpret_cast<v4s *>(&sGh[tile32(0, 0)][r][16 + 4 * q]) = v4s{0, 0, 0, 0};
+    if (v == 13) *reinterpret_cast<v4s *>(&sGl[tile32(0, 0)][r][16 + 4 * q]) = v4s{0, 0, 0, 0};
+    if (v == 14) *reinterpret_cast<v4s *>(&sGh[tile32(2, 1)][r][16 + 4 * q]) = v4s{0, 0, 0, 0};
+    if (v == 15) *reinterpret_cast<v4s *>(&sGl[tile32(2, 1)][r][16 + 4 * q]) = v4s{0, 0, 0, 0};
 
     // chunk c is fetched during chunks c - 2 and c - 1 (two register sets, taken in
     // turn).  Chunks go in pairs, so an odd count ends with one past the end of the
     // sequence: its loads read 0 (delta 0: decay 1, gain 0, the state unchanged) and
     // its stores are dropped.  Fetches past the end are likewise unconditional: with
     // no branch around them the compiler waits only for the loads a stage needs.
-    const int64_t nchunks = (L + SQ - 1) / SQ;
-    auto chunk = [&](int64_t c, Chunk &P, const Chunk &Pn) {
-        const int64_t t0 = c * SQ;
+    const int nchunks = nfull + (tail > 0);
+    auto chunk = [&](int c, Chunk &P, const Chunk &Pn) {
+        const int64_t t0 = int64_t(c) * SQ;
         const int par = int(c & 1);  // which scalar set
         publish_state();  // the state entering this chunk
         stage(P, par);
         __syncthreads();
-        fetch(t0 + 2 * SQ, P);
+        fetch(c + 2, P);
         if (v == kScalarWave) scalars(Pn, par ^ 1);  // for chunk c + 1
 
-        // ---- phase 2a: causal score tiles, spread over the waves (k = v, v + 8):
+        // ---- phase 2a: causal score tile k = v (waves 0..9), (token block tb, source
+        // block sb <= tb), row-major over the triangle:
         // G^T tile (s-block sb, t-block tb) = B C^T, times exp(A (cum_t - cum_s)) gain_s
         // where s <= t, plus the skip D on the diagonal (D x is then part of the
         // causal product), split into bf16 parts and stored as rows t, columns s
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int k = v + 8 * kk;
-            if (k >= NG) break;
+        if (v < NG) {
+            const int k = v;
             const int tb = k >= 6 ? 3 : k >= 3 ? 2 : k >= 1 ? 1 : 0;
             const int sb = k - tb * (tb + 1) / 2;
             const int tl = 16 * tb + r;
@@ -588,24 +590,15 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
         __syncthreads();  // scores in LDS
 
         // ---- phase 3: outputs, transposed: Y^T = X^T G'^T + (S_in C^T) diag(e) for
-        // (channel block pbo, token block tbo[u]), u = 0, 1; lane (r, q) ends with
-        // channels 16 pbo + 4q .. + 3 of token 16 tb + r and stores them as 8 bytes
-        v8bf sh[NK], sl[NK];
-#pragma unroll
-        for (int kb = 0; kb < NK; ++kb) {
-            sh[kb] = *reinterpret_cast<const v8bf *>(&sSh[16 * pbo + r][32 * kb + 8 * q]);
-            sl[kb] = *reinterpret_cast<const v8bf *>(&sSl[16 * pbo + r][32 * kb + 8 * q]);
-        }
-        const rsrc_t rys = make_rsrc(yb + t0 * rx, (L - t0) * rx * 2);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int tb = u == 0 ? tbo0 : tbo1;
-            const int tl = 16 * tb + r;
+        // (channel block pbo, token block tbo); lane (r, q) ends with channels
+        // 16 pbo + 4q .. + 3 of token 16 tbo + r and stores them as 8 bytes
+        {
+            const int tl = 16 * tbo + r;
             v4f acc = {0.f, 0.f, 0.f, 0.f}, off = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int sp = 0; sp < 2; ++sp) {
-                if (32 * sp > 16 * tb + 15) break;
-                const int m = tile32(tb, sp);
+                if (32 * sp > 16 * tbo + 15) break;
+                const int m = tile32(tbo, sp);
                 const v8bf xa = ld_t(&sX[0][0], XP, 32 * sp, 16 * pbo);  // x[s = 32sp + 8q + j][16 pbo + r]
                 const v8bf gh = *reinterpret_cast<const v8bf *>(&sGh[m][r][8 * q]);
                 const v8bf gl = *reinterpret_cast<const v8bf *>(&sGl[m][r][8 * q]);
@@ -614,25 +607,28 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
             }
 #pragma unroll
             for (int kb = 0; kb < NK; ++kb) {
+                const v8bf sh = *reinterpret_cast<const v8bf *>(&sSh[16 * pbo + r][32 * kb + 8 * q]);
+                const v8bf sl = *reinterpret_cast<const v8bf *>(&sSl[16 * pbo + r][32 * kb + 8 * q]);
                 const v8bf cb = *reinterpret_cast<const v8bf *>(&sC[tl][32 * kb + 8 * q]);
-                off = mfma32(off, sh[kb], cb);
-                off = mfma32(off, sl[kb], cb);
+                off = mfma32(off, sh, cb);
+                off = mfma32(off, sl, cb);
             }
             const float e = sE[par][tl];
             v4s yv;
 #pragma unroll
             for (int j = 0; j < 4; ++j) yv[j] = short(f32_to_bf16(fmaf(e, off[j], acc[j])));
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, yv), rys,
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, yv),
+                                                  make_rsrc32(yb + t0 * rx, toks(c) * uint32_t(rx) * 2),
                                                   uint32_t((tl * rx + 16 * pbo + 4 * q) * 2), 0, 0);
         }
         __syncthreads();  // every wave is done with this chunk's staged data and state
     };
     Chunk P0, P1;
     fetch(0, P0);
-    fetch(SQ, P1);
+    fetch(1, P1);
     if (v == kScalarWave) scalars(P0, 0);
     __syncthreads();
-    for (int64_t c = 0; c < nchunks; c += 2) {
+    for (int c = 0; c < nchunks; c += 2) {
         chunk(c, P0, P1);
         chunk(c + 1, P1, P0);
     }
@@ -640,7 +636,7 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
 #pragma unroll
         for (int i = 0; i < NBW; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) hT[srow + 16 * (nb0 + i) + 4 * q + j] = S[i][j];
+            for (int j = 0; j < 4; ++j) hT[hrow + 16 * (nb0 + i) + 4 * q + j] = S[i][j];
     }
 }
 
@@ -670,7 +666,11 @@ hipError_t ssd_io(const SsdArgs &a, hipStream_t s) {
     // the bf16 kernel's 16-byte loads need 16-byte aligned x, B and C; other
     // bf16 arguments take the 4-wave kernel, which reads element by element
     if constexpr (std::is_same<IO, IoBF16>::value) {
-        if (aligned16(a.x) && aligned16(a.B) && aligned16(a.C))
+        // its chunk offsets are 32-bit: a 64-token chunk of x, B, C or delta below
+        // 2^31 bytes, and the chunk count (plus the two fetched ahead) below 2^31
+        const bool fits = a.H < (int64_t(1) << 18) && a.G * a.N < (int64_t(1) << 23) &&
+                          a.L / SQ < (int64_t(1) << 31) - 4;
+        if (fits && aligned16(a.x) && aligned16(a.B) && aligned16(a.C))
             return a.N == 64 ? ssd_bf_t<64>(a, s) : ssd_bf_t<128>(a, s);
     }
     return a.N == 64 ? ssd_t<IO, 64>(a, s) : ssd_t<IO, 128>(a, s);
