@@ -514,8 +514,9 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
         }
     };
 
-    // output tile of this wave: channel block pbo, token block tbo
-    const int pbo = v % 4, tbo = v / 4;
+    // outputs (waves 0..7): channel block pbo, token blocks tbo0 and 3 - tbo0, whose
+    // causal work sums to the same for every wave; the two tiles share the state operand
+    const int pbo = v % 4, tbo0 = (v / 4) % 2;
 
     // the two 16 x 16 halves of the stored tiles above the diagonal blocks,
     // (tb 0, sb 1) and (tb 2, sb 3), are never written and stay zero
@@ -590,36 +591,50 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
         __syncthreads();  // scores in LDS
 
         // ---- phase 3: outputs, transposed: Y^T = X^T G'^T + (S_in C^T) diag(e) for
-        // (channel block pbo, token block tbo); lane (r, q) ends with channels
-        // 16 pbo + 4q .. + 3 of token 16 tbo + r and stores them as 8 bytes
-        {
-            const int tl = 16 * tbo + r;
-            v4f acc = {0.f, 0.f, 0.f, 0.f}, off = {0.f, 0.f, 0.f, 0.f};
+        // (channel block pbo, token block tb); lane (r, q) ends with channels
+        // 16 pbo + 4q .. + 3 of token 16 tb + r and stores them as 8 bytes
+        if (v < 8) {
+            v4f acc[2], off[2];
 #pragma unroll
-            for (int sp = 0; sp < 2; ++sp) {
-                if (32 * sp > 16 * tbo + 15) break;
-                const int m = tile32(tbo, sp);
-                const v8bf xa = ld_t(&sX[0][0], XP, 32 * sp, 16 * pbo);  // x[s = 32sp + 8q + j][16 pbo + r]
-                const v8bf gh = *reinterpret_cast<const v8bf *>(&sGh[m][r][8 * q]);
-                const v8bf gl = *reinterpret_cast<const v8bf *>(&sGl[m][r][8 * q]);
-                acc = mfma32(acc, xa, gh);
-                acc = mfma32(acc, xa, gl);
+            for (int u = 0; u < 2; ++u) {
+                const int tb = u == 0 ? tbo0 : 3 - tbo0;
+                acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
+                off[u] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int sp = 0; sp < 2; ++sp) {
+                    if (32 * sp > 16 * tb + 15) break;
+                    const int m = tile32(tb, sp);
+                    const v8bf xa = ld_t(&sX[0][0], XP, 32 * sp, 16 * pbo);  // x[s = 32sp + 8q + j][16 pbo + r]
+                    const v8bf gh = *reinterpret_cast<const v8bf *>(&sGh[m][r][8 * q]);
+                    const v8bf gl = *reinterpret_cast<const v8bf *>(&sGl[m][r][8 * q]);
+                    acc[u] = mfma32(acc[u], xa, gh);
+                    acc[u] = mfma32(acc[u], xa, gl);
+                }
             }
+            // S_in C^T: each K step of the state operand serves both tiles
 #pragma unroll
             for (int kb = 0; kb < NK; ++kb) {
                 const v8bf sh = *reinterpret_cast<const v8bf *>(&sSh[16 * pbo + r][32 * kb + 8 * q]);
                 const v8bf sl = *reinterpret_cast<const v8bf *>(&sSl[16 * pbo + r][32 * kb + 8 * q]);
-                const v8bf cb = *reinterpret_cast<const v8bf *>(&sC[tl][32 * kb + 8 * q]);
-                off = mfma32(off, sh, cb);
-                off = mfma32(off, sl, cb);
-            }
-            const float e = sE[par][tl];
-            v4s yv;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) yv[j] = short(f32_to_bf16(fmaf(e, off[j], acc[j])));
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, yv),
-                                                  make_rsrc32(yb + t0 * rx, toks(c) * uint32_t(rx) * 2),
-                                                  uint32_t((tl * rx + 16 * pbo + 4 * q) * 2), 0, 0);
+                for (int u = 0; u < 2; ++u) {
+                    const int tb = u == 0 ? tbo0 : 3 - tbo0;
+                    const v8bf cb = *reinterpret_cast<const v8bf *>(&sC[16 * tb + r][32 * kb + 8 * q]);
+                    off[u] = mfma32(off[u], sh, cb);
+                    off[u] = mfma32(off[u], sl, cb);
+                }
+            }
+            const rsrc_t rys = make_rsrc32(yb + t0 * rx, toks(c) * uint32_t(rx) * 2);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int tl = 16 * (u == 0 ? tbo0 : 3 - tbo0) + r;
+                const float e = sE[par][tl];
+                v4s yv;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) yv[j] = short(f32_to_bf16(fmaf(e, off[u][j], acc[u][j])));
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, yv), rys,
+                                                      uint32_t((tl * rx + 16 * pbo + 4 * q) * 2), 0, 0);
+            }
         }
         __syncthreads();  // every wave is done with this chunk's staged data and state
     };
