@@ -355,15 +355,19 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
     const float *__restrict__ h0, uint16_t *__restrict__ y, float *__restrict__ hT, int64_t L,
     int64_t H, int64_t G) {
     constexpr int NK = NS / 32;        // 32-wide K steps over the states
-    constexpr int RP = NS + 8;         // pitch (bf16) of tiles read by rows: 16-byte reads of 8 rows
-    constexpr int TP = NS + 16;        // pitch (bf16) of B read transposed: 8-byte reads of 4 rows
-    constexpr int XP = SP + 16;        // pitch (bf16) of x, read transposed
-    constexpr int NBW = NS / 64;       // 16x16 state tiles per wave (4 channel blocks x NS/16 state blocks)
+    // LDS pitches (bf16).  A 16-byte read of rows r = 0..15 at one column is
+    // conflict-free on gfx950's 64 banks when the pitch is 8 (mod 16) dwords, so
+    // tiles read by rows take NS + 16 (72 or 40 dwords); transposing reads run at
+    // one 4 x 16 block per group for any of these pitches.
+    constexpr int RP = NS + 16;        // tiles read by rows
+    constexpr int TP = NS + 16;        // B read transposed
+    constexpr int XP = SP + 16;        // x read transposed
+    constexpr int NBW = NS / 32;       // 16x16 state tiles per state wave (8 waves: 4 channel blocks x 2 halves)
     constexpr int BPL = NS / 16;       // bf16 of a B (or C) row per lane: 16 lanes to a row
     constexpr int NG = 10;             // causal 16x16 score tiles of a 64-token chunk
     constexpr int NM = 6;              // 16 x 32 tiles they are stored in
-    constexpr int GP = 40;             // row pitch (bf16) of the stored score tiles
-    constexpr int kScalarWave = 11;    // a wave without a score tile, on a SIMD with two of them
+    constexpr int GP = 48;             // row pitch (bf16) of the stored score tiles (24 dwords)
+    constexpr int kScalarWave = 15;    // a state wave: it forms the next chunk's scalars after the scores
     static_assert(BWV == 16 && SQ == 64 && SP == 64, "work split");
     using VB = typename std::conditional<BPL == 8, v4u, v2u>::type;
     __shared__ __align__(16) uint16_t sX[SQ][XP];    // x of the chunk, [token][channel]
@@ -375,7 +379,7 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
     __shared__ __align__(16) uint16_t sSh[SP][RP];   // entering state, [channel][state], bf16
     __shared__ __align__(16) uint16_t sSl[SP][RP];   // and its remainder
     // masked scores as 16 x 32 tiles [t][s] (B operand of the transposed causal product):
-    // tile m(tb, sp) holds tokens 16 tb.. and sources 32 sp..; rows padded to 40
+    // tile m(tb, sp) holds tokens 16 tb.. and sources 32 sp..; rows padded to 48
     __shared__ __align__(16) uint16_t sGh[NM][16][GP];
     __shared__ __align__(16) uint16_t sGl[NM][16][GP];
     // per-token scalars, two sets: those of chunk c + 1 are formed during chunk c
@@ -484,16 +488,21 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     };
 
-    // ---- state tiles of this wave: channel block pbs, state blocks nb0..nb0+NBW-1;
+    // ---- wave roles.  Output waves (v < 8) form C S_in for two output tiles and one
+    // score tile before the scores are all ready, and (scores) X after; state waves
+    // (v >= 8) update a quarter of the state before (waves 8 and 9 also take a score
+    // tile) and publish it after.
+    // State tiles of state wave v: channel block pbs, state blocks nb0..nb0+NBW-1;
     // S[i][j] = S[n = 16(nb0 + i) + 4q + j][p = 16 pbs + r]
-    const int pbs = v % 4, nb0 = NBW * (v / 4);
+    const bool outw = v < 8;
+    const int pbs = v % 4, nb0 = NBW * ((v / 4) % 2);
     v4f S[NBW];
     const int64_t hrow = ((b * H + h) * SP + 16 * pbs + r) * NS;
     {
         // the initial state through a descriptor of 0 bytes when there is none (reads
         // 0): no branch around these loads, which would make the compiler wait for
         // every outstanding load at the loop head
-        const rsrc_t rh = make_rsrc32(h0 ? h0 + (b * H + h) * SP * NS : nullptr, h0 ? SP * NS * 4 : 0);
+        const rsrc_t rh = make_rsrc32(h0 && !outw ? h0 + (b * H + h) * SP * NS : nullptr, h0 && !outw ? SP * NS * 4 : 0);
 #pragma unroll
         for (int i = 0; i < NBW; ++i)
             S[i] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
@@ -514,9 +523,11 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
         }
     };
 
-    // outputs (waves 0..7): channel block pbo, token blocks tbo0 and 3 - tbo0, whose
-    // causal work sums to the same for every wave; the two tiles share the state operand
+    // output wave v: channel block pbo, token blocks tbo0 and 3 - tbo0, whose causal
+    // work sums to the same for every output wave; the two tiles share the state operand
     const int pbo = v % 4, tbo0 = (v / 4) % 2;
+    // score tiles: k = v on output waves 0..7 and state waves 8, 9
+    const int ktile = v < 10 ? v : -1;
 
     // the two 16 x 16 halves of the stored tiles above the diagonal blocks,
     // (tb 0, sb 1) and (tb 2, sb 3), are never written and stay zero
@@ -535,19 +546,36 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
     auto chunk = [&](int c, Chunk &P, const Chunk &Pn) {
         const int64_t t0 = int64_t(c) * SQ;
         const int par = int(c & 1);  // which scalar set
-        publish_state();  // the state entering this chunk
         stage(P, par);
-        __syncthreads();
+        __syncthreads();  // chunk staged; the state entering it published
         fetch(c + 2, P);
-        if (v == kScalarWave) scalars(Pn, par ^ 1);  // for chunk c + 1
 
-        // ---- phase 2a: causal score tile k = v (waves 0..9), (token block tb, source
-        // block sb <= tb), row-major over the triangle:
+        // ---- phase A, output waves: S_in C^T for both tiles (the state operand's K
+        // steps serve both), kept in registers across the barrier
+        v4f off[2];
+        if (outw) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) off[u] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < NK; ++kb) {
+                const v8bf sh = *reinterpret_cast<const v8bf *>(&sSh[16 * pbo + r][32 * kb + 8 * q]);
+                const v8bf sl = *reinterpret_cast<const v8bf *>(&sSl[16 * pbo + r][32 * kb + 8 * q]);
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int tb = u == 0 ? tbo0 : 3 - tbo0;
+                    const v8bf cb = *reinterpret_cast<const v8bf *>(&sC[16 * tb + r][32 * kb + 8 * q]);
+                    off[u] = mfma32(off[u], sh, cb);
+                    off[u] = mfma32(off[u], sl, cb);
+                }
+            }
+        }
+        // ---- phase A: causal score tile k (token block tb, source block sb <= tb,
+        // row-major over the triangle):
         // G^T tile (s-block sb, t-block tb) = B C^T, times exp(A (cum_t - cum_s)) gain_s
         // where s <= t, plus the skip D on the diagonal (D x is then part of the
         // causal product), split into bf16 parts and stored as rows t, columns s
-        if (v < NG) {
-            const int k = v;
+        if (ktile >= 0) {
+            const int k = ktile;
             const int tb = k >= 6 ? 3 : k >= 3 ? 2 : k >= 1 ? 1 : 0;
             const int sb = k - tb * (tb + 1) / 2;
             const int tl = 16 * tb + r;
@@ -572,34 +600,36 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
             *reinterpret_cast<v4s *>(&sGh[tile32(tb, sb / 2)][r][16 * (sb % 2) + 4 * q]) = hi;
             *reinterpret_cast<v4s *>(&sGl[tile32(tb, sb / 2)][r][16 * (sb % 2) + 4 * q]) = lo;
         }
-        // ---- phase 2b: state update (registers): S = exp(A sum delta) S + B^T diag(w) X
-        const float dec = sDec[par];
+        // ---- phase A, state waves: S = exp(A sum delta) S + B^T diag(w) X
+        if (!outw) {
+            const float dec = sDec[par];
 #pragma unroll
-        for (int i = 0; i < NBW; ++i) S[i] *= dec;
+            for (int i = 0; i < NBW; ++i) S[i] *= dec;
 #pragma unroll
-        for (int kb = 0; kb < SQ / 32; ++kb) {
-            // (w x)[s = 32kb + 8q + j][16 pbs + r], both parts
-            const v8bf xh = ld_t(&sXWh[0][0], XP, 32 * kb, 16 * pbs);
-            const v8bf xl = ld_t(&sXWl[0][0], XP, 32 * kb, 16 * pbs);
+            for (int kb = 0; kb < SQ / 32; ++kb) {
+                // (w x)[s = 32kb + 8q + j][16 pbs + r], both parts
+                const v8bf xh = ld_t(&sXWh[0][0], XP, 32 * kb, 16 * pbs);
+                const v8bf xl = ld_t(&sXWl[0][0], XP, 32 * kb, 16 * pbs);
 #pragma unroll
-            for (int i = 0; i < NBW; ++i) {
-                const v8bf bt = ld_t(&sBT[0][0], TP, 32 * kb, 16 * (nb0 + i));  // B[s][16(nb0 + i) + r]
-                S[i] = mfma32(S[i], bt, xh);
-                S[i] = mfma32(S[i], bt, xl);
+                for (int i = 0; i < NBW; ++i) {
+                    const v8bf bt = ld_t(&sBT[0][0], TP, 32 * kb, 16 * (nb0 + i));  // B[s][16(nb0 + i) + r]
+                    S[i] = mfma32(S[i], bt, xh);
+                    S[i] = mfma32(S[i], bt, xl);
+                }
             }
         }
-        __syncthreads();  // scores in LDS
+        __syncthreads();  // scores in LDS; every read of the entering state done
 
-        // ---- phase 3: outputs, transposed: Y^T = X^T G'^T + (S_in C^T) diag(e) for
-        // (channel block pbo, token block tb); lane (r, q) ends with channels
-        // 16 pbo + 4q .. + 3 of token 16 tb + r and stores them as 8 bytes
-        if (v < 8) {
-            v4f acc[2], off[2];
+        // ---- phase B, output waves: Y^T = X^T G'^T + (S_in C^T) diag(e), transposed:
+        // lane (r, q) ends with channels 16 pbo + 4q .. + 3 of token 16 tb + r and
+        // stores them as 8 bytes
+        if (outw) {
+            const rsrc_t rys = make_rsrc32(yb + t0 * rx, toks(c) * uint32_t(rx) * 2);
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int tb = u == 0 ? tbo0 : 3 - tbo0;
-                acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
-                off[u] = v4f{0.f, 0.f, 0.f, 0.f};
+                const int tl = 16 * tb + r;
+                v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int sp = 0; sp < 2; ++sp) {
                     if (32 * sp > 16 * tb + 15) break;
@@ -607,47 +637,35 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
                     const v8bf xa = ld_t(&sX[0][0], XP, 32 * sp, 16 * pbo);  // x[s = 32sp + 8q + j][16 pbo + r]
                     const v8bf gh = *reinterpret_cast<const v8bf *>(&sGh[m][r][8 * q]);
                     const v8bf gl = *reinterpret_cast<const v8bf *>(&sGl[m][r][8 * q]);
-                    acc[u] = mfma32(acc[u], xa, gh);
-                    acc[u] = mfma32(acc[u], xa, gl);
+                    acc = mfma32(acc, xa, gh);
+                    acc = mfma32(acc, xa, gl);
                 }
-            }
-            // S_in C^T: each K step of the state operand serves both tiles
-#pragma unroll
-            for (int kb = 0; kb < NK; ++kb) {
-                const v8bf sh = *reinterpret_cast<const v8bf *>(&sSh[16 * pbo + r][32 * kb + 8 * q]);
-                const v8bf sl = *reinterpret_cast<const v8bf *>(&sSl[16 * pbo + r][32 * kb + 8 * q]);
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int tb = u == 0 ? tbo0 : 3 - tbo0;
-                    const v8bf cb = *reinterpret_cast<const v8bf *>(&sC[16 * tb + r][32 * kb + 8 * q]);
-                    off[u] = mfma32(off[u], sh, cb);
-                    off[u] = mfma32(off[u], sl, cb);
-                }
-            }
-            const rsrc_t rys = make_rsrc32(yb + t0 * rx, toks(c) * uint32_t(rx) * 2);
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int tl = 16 * (u == 0 ? tbo0 : 3 - tbo0) + r;
                 const float e = sE[par][tl];
                 v4s yv;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) yv[j] = short(f32_to_bf16(fmaf(e, off[u][j], acc[u][j])));
+                for (int j = 0; j < 4; ++j) yv[j] = short(f32_to_bf16(fmaf(e, off[u][j], acc[j])));
                 __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, yv), rys,
                                                       uint32_t((tl * rx + 16 * pbo + 4 * q) * 2), 0, 0);
             }
+        } else {
+            // ---- phase B, state waves: publish the state entering the next chunk; the
+            // scalar wave also forms the next chunk's scalars
+            publish_state();
+            if (v == kScalarWave) scalars(Pn, par ^ 1);
         }
-        __syncthreads();  // every wave is done with this chunk's staged data and state
+        __syncthreads();  // every wave is done with this chunk's staged data
     };
     Chunk P0, P1;
     fetch(0, P0);
     fetch(1, P1);
     if (v == kScalarWave) scalars(P0, 0);
+    if (!outw) publish_state();  // the initial state
     __syncthreads();
     for (int c = 0; c < nchunks; c += 2) {
         chunk(c, P0, P1);
         chunk(c + 1, P1, P0);
     }
-    if (hT) {
+    if (hT && !outw) {
 #pragma unroll
         for (int i = 0; i < NBW; ++i)
 #pragma unroll
