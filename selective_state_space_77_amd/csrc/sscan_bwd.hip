@@ -330,6 +330,13 @@ __global__ __launch_bounds__(BW *kWave) void k_bwd(
     auto rsrc_at = [&](const T *base, int64_t t0) {
         return make_rsrc(base + (b * L + t0) * dim, (L - t0) * dim * ES);
     };
+    // inputs of chunk c (c < 0: an empty descriptor, whose loads read 0): the next
+    // chunk's loads are issued unconditionally and stay in flight while the current
+    // chunk computes
+    auto rsrc_chunk = [&](const T *base, int64_t c) {
+        const int64_t t0 = (c < 0 ? 0 : c) * BCH + int64_t(w) * BT;
+        return make_rsrc(base + (b * L + t0) * dim, c < 0 ? 0 : (L - t0) * dim * ES);
+    };
     auto ck = [&](int64_t c, int n) -> float & { return ckpt[((c * batch + b) * NT + n) * dim + d]; };
     const RedRow red{&s_red[w][0][lane]};
 
@@ -338,9 +345,20 @@ __global__ __launch_bounds__(BW *kWave) void k_bwd(
 #pragma unroll
     for (int n = 0; n < NT; ++n)
         k[n] = (w == 0 && h0 && n < N) ? m.to_state(h0[(b * dim + d) * N + n]) : 0.f;
+    T cx[BT], cd[BT];  // raw x and delta of the chunk, loaded one chunk ahead
+    auto load1 = [&](int64_t c, T *xr, T *dr) {
+        const rsrc_t rx = rsrc_chunk(x, c), rd = rsrc_chunk(delta, c);
+#pragma unroll
+        for (int tau = 0; tau < BT; ++tau) {
+            xr[tau] = IO::bld(rx, voff, uint32_t(tau) * rowb);
+            dr[tau] = IO::bld(rd, voff, uint32_t(tau) * rowb);
+        }
+    };
+    load1(0, cx, cd);
     for (int64_t c = 0; c < nchunks; ++c) {
         const int64_t t0 = c * BCH + int64_t(w) * BT;
-        const rsrc_t rx = rsrc_at(x, t0), rd = rsrc_at(delta, t0);
+        T nx[BT], nd[BT];
+        load1(c + 1, nx, nd);
         const float *bc0 = bcrow + min(t0, L - 1) * (2 * NT);
         const int last = int(max<int64_t>(0, min<int64_t>(BT, L - t0) - 1));
         if (w == 0) {
@@ -359,8 +377,8 @@ __global__ __launch_bounds__(BW *kWave) void k_bwd(
         float dsum = 0.f;
 #pragma unroll
         for (int tau = 0; tau < BT; ++tau) {
-            const float xv = amask * IO::cvt(IO::bld(rx, voff, uint32_t(tau) * rowb));
-            const float dv = IO::cvt(IO::bld(rd, voff, uint32_t(tau) * rowb));
+            const float xv = amask * IO::cvt(cx[tau]);
+            const float dv = IO::cvt(cd[tau]);
             m.fwd(dv, xv, bc0 + min(tau, last) * (2 * NT), k);
             dsum += dv;
         }
@@ -378,6 +396,11 @@ __global__ __launch_bounds__(BW *kWave) void k_bwd(
             }
         }
         __syncthreads();
+#pragma unroll
+        for (int tau = 0; tau < BT; ++tau) {
+            cx[tau] = nx[tau];
+            cd[tau] = nd[tau];
+        }
     }
 
     // ---------------- pass 2: chunks in reverse
@@ -392,9 +415,35 @@ __global__ __launch_bounds__(BW *kWave) void k_bwd(
     for (int n = 0; n < NT; ++n) dA_acc[n] = 0.f;
     float dD_acc = 0.f;
 
+    // raw x, delta, dy and (wave 0) the entering-state checkpoint of the chunk,
+    // loaded one chunk ahead (chunk c - 1 while chunk c computes); the general-A
+    // path, short of registers, loads them at the top of its chunk
+    T cg[BT];
+    float cck[NT];
+    auto load_ck = [&](int64_t c, float *kr) {
+        const int64_t cc = c < 0 ? 0 : c;
+        const rsrc_t rk = make_rsrc(ckpt + (cc * batch + b) * NT * dim, (c < 0 || w != 0) ? 0 : NT * dim * 4);
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+            kr[n] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rk, uint32_t((n * dim + d) * 4), 0, 0));
+    };
+    auto load2 = [&](int64_t c, T *xr, T *dr, T *gr, float *kr) {
+        const rsrc_t rx = rsrc_chunk(x, c), rd = rsrc_chunk(delta, c), rg = rsrc_chunk(dy, c);
+#pragma unroll
+        for (int tau = 0; tau < BT; ++tau) {
+            xr[tau] = IO::bld(rx, voff, uint32_t(tau) * rowb);
+            dr[tau] = IO::bld(rd, voff, uint32_t(tau) * rowb);
+            gr[tau] = IO::bld(rg, voff, uint32_t(tau) * rowb);
+        }
+        if constexpr (kFast) load_ck(c, kr);
+    };
+    if constexpr (kFast) load2(nchunks - 1, cx, cd, cg, cck);
     for (int64_t c = nchunks - 1; c >= 0; --c) {
         const int64_t t0 = c * BCH + int64_t(w) * BT;
-        const rsrc_t rx = rsrc_at(x, t0), rd = rsrc_at(delta, t0), rg = rsrc_at(dy, t0);
+        T nx[BT], nd[BT], ng[BT];
+        float nck[NT];
+        if constexpr (kFast) load2(c - 1, nx, nd, ng, nck);
+        else load2(c, cx, cd, cg, cck);
         const rsrc_t rdx = rsrc_at(dx, t0), rdd = rsrc_at(ddelta, t0);
         const float *bc0 = bcrow + min(t0, L - 1) * (2 * NT);
         const int last = int(max<int64_t>(0, min<int64_t>(BT, L - t0) - 1));
@@ -403,17 +452,18 @@ __global__ __launch_bounds__(BW *kWave) void k_bwd(
         float xs[BT], ds[BT], gs[BT];
 #pragma unroll
         for (int tau = 0; tau < BT; ++tau) {
-            xs[tau] = amask * IO::cvt(IO::bld(rx, voff, uint32_t(tau) * rowb));
-            ds[tau] = IO::cvt(IO::bld(rd, voff, uint32_t(tau) * rowb));
-            gs[tau] = amask * IO::cvt(IO::bld(rg, voff, uint32_t(tau) * rowb));
+            xs[tau] = amask * IO::cvt(cx[tau]);
+            ds[tau] = IO::cvt(cd[tau]);
+            gs[tau] = amask * IO::cvt(cg[tau]);
         }
 
         // phase A: the run's states from its entering state (run 0: the chunk's,
         // exact; other runs: zero, corrected below) and its adjoint from zero
         float hist[BT + 1][NT];  // hist[0]: entering state, hist[tau+1]: after token tau
         float dcum[BT];          // delta summed from the run start through token tau
+        if constexpr (!kFast) load_ck(c, cck);  // (load2 leaves it to this point)
 #pragma unroll
-        for (int n = 0; n < NT; ++n) hist[0][n] = (w == 0) ? ck(c, n) : 0.f;
+        for (int n = 0; n < NT; ++n) hist[0][n] = cck[n];  // 0 for waves other than 0
         float dsum = 0.f;
 #pragma unroll
         for (int tau = 0; tau < BT; ++tau) {
@@ -493,6 +543,16 @@ __global__ __launch_bounds__(BW *kWave) void k_bwd(
                 part_bc[((dt_ * batch + b) * L + t0 + tau) * (2 * NT) + lane] =
                     lane < NT ? acc * Math::b_scale(lane) : acc;
             wave_sync_lds();
+        }
+        if constexpr (kFast) {
+#pragma unroll
+            for (int tau = 0; tau < BT; ++tau) {
+                cx[tau] = nx[tau];
+                cd[tau] = nd[tau];
+                cg[tau] = ng[tau];
+            }
+#pragma unroll
+            for (int n = 0; n < NT; ++n) cck[n] = nck[n];
         }
     }
     // adjoint leaving chunk 0 = dLoss/d(initial state)
