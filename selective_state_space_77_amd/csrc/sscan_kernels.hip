@@ -38,6 +38,7 @@
 // general path (exp2 and the ZOH gain per state).
 
 #include <math.h>
+#include <type_traits>
 
 #include "sscan_device.h"
 
@@ -582,15 +583,105 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
     }
 }
 
+// 1/(n+1) for state n = q SPL + j of a lane (q < LPC): constants for one or two
+// lanes per channel
+template <int SPL, int LPC>
+__device__ __forceinline__ float inv_np1(int q, int j) {
+    if constexpr (LPC == 1) return 1.f / float(j + 1);
+    else if constexpr (LPC == 2) return q == 0 ? 1.f / float(j + 1) : 1.f / float(SPL + j + 1);
+    else return 1.f / float(q * SPL + j + 1);
+}
+
+// S consecutive elements (S a multiple of 4, aligned to 4 elements) as floats,
+// in 16-byte loads
+template <int S>
+__device__ __forceinline__ void ldrow(const float *p, float *o) {
+#pragma unroll
+    for (int j = 0; j < S; j += 4) {
+        const float4 v = *reinterpret_cast<const float4 *>(p + j);
+        o[j] = v.x; o[j + 1] = v.y; o[j + 2] = v.z; o[j + 3] = v.w;
+    }
+}
+template <int S>
+__device__ __forceinline__ void ldrow(const uint16_t *p, float *o) {
+    if constexpr (S % 8 == 0) {
+#pragma unroll
+        for (int j = 0; j < S; j += 8) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(p + j);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                o[j + 2 * u] = __uint_as_float(w[u] << 16);
+                o[j + 2 * u + 1] = __uint_as_float(w[u] & 0xFFFF0000u);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < S; j += 4) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(p + j);
+            o[j] = __uint_as_float(v.x << 16);
+            o[j + 1] = __uint_as_float(v.x & 0xFFFF0000u);
+            o[j + 2] = __uint_as_float(v.y << 16);
+            o[j + 3] = __uint_as_float(v.y & 0xFFFF0000u);
+        }
+    }
+}
+
+// One lane's SPL states of one channel (states n = q SPL + j, those >= N padded
+// with zeros): the state update, and the lane's part of the readout C.h.
+template <int SPL, int LPC>
+__device__ __forceinline__ float step_lane(int q, int N, float dt, float xv, float a0, const float *av,
+                                           const float *bv, const float *cv, float *h) {
+    // structured-real states (A[d,n] = (n+1) A[d,0], A[d,0] < 0, the form the scan
+    // kernels classify): one exp per lane, and with r = exp(delta A[d,0]) and
+    // q_n = 1 - r^(n+1) = r q_(n-1) + q_0,
+    //     h_n <- h_n + q_n (B_n x / ((n+1) alpha) - h_n),  alpha = -A[d,0],
+    // the update of the scan kernels on the unscaled state; other states take
+    // the general form (an exp and the ZOH gain per state)
+    bool sr = (a0 < 0.f) && (a0 > -INFINITY);
+#pragma unroll
+    for (int j = 0; j < SPL; ++j)
+        if (q * SPL + j < N) sr = sr && (av[j] == a0 * float(q * SPL + j + 1));
+    float yacc = 0.f;
+    if (sr) {
+        const float z = dt * a0;
+        const float r = exp2_hw(z * kLog2e);
+        const float q0 = one_minus_exp(z, r);
+        // q_(n0-1) = 1 - r^n0 for this lane's first state n0
+        const float zn = z * float(q * SPL);
+        float qn = q == 0 ? 0.f : one_minus_exp(zn, exp2_hw(zn * kLog2e));
+        const float xa = xv / -a0;
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) {
+            qn = fmaf(qn, r, q0);
+            const float e = fmaf(bv[j] * inv_np1<SPL, LPC>(q, j), xa, -h[j]);
+            h[j] = fmaf(qn, e, h[j]);
+            yacc = fmaf(cv[j], h[j], yacc);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) {
+            const float z = dt * av[j];
+            const float abar = exp2_hw(dt * (av[j] * kLog2e));
+            const float g = zoh_gain(dt, av[j], z, abar);
+            h[j] = fmaf(abar, h[j], g * (bv[j] * xv));
+            yacc = fmaf(cv[j], h[j], yacc);
+        }
+    }
+    return yacc;
+}
+
 // ----------------------------------------------------------------------------
-// Decode step: LPC lanes share one channel, each owning SPL consecutive states
-// (16 B for N = 16), so a wave reads and writes one contiguous 1 KB span of
-// the (batch, dim, N) state.  The partial readouts are summed across the LPC
-// lanes.  Memory bound; per state one hardware exp2 and the gain above.
+// Decode step: LPC lanes share one channel, each owning SPL consecutive states,
+// so a wave reads and writes one contiguous span of the (batch, dim, N) state
+// (SPL x 256 B).  The partial readouts are summed across the LPC lanes.  Memory
+// bound: what limits it is the state bytes each CU keeps in flight, hence
+// several 16-byte state loads per lane.  Per state one hardware exp2 and the
+// gain above.
 // With the front end (FE), x and delta are the raw token inputs: the step
 // reads the K-1 carried raw inputs of its channel from conv_state, forms the
 // convolution and softplus, and shifts conv_state by one token in place.
-template <class IO, int NT, bool kVec, bool FE>
+template <class IO, int NT, int SPL, bool kVec, bool FE>
 __global__ __launch_bounds__(256) void k_step(float *__restrict__ state,
                                               const typename IO::T *__restrict__ x,
                                               const typename IO::T *__restrict__ delta,
@@ -602,7 +693,6 @@ __global__ __launch_bounds__(256) void k_step(float *__restrict__ state,
                                               int64_t dim, int N, FeArgs fe,
                                               typename IO::T *__restrict__ conv_state) {
     using T = typename IO::T;
-    constexpr int SPL = NT < 4 ? NT : 4;
     constexpr int LPC = NT / SPL;
     const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t chans = batch * dim;
@@ -614,6 +704,9 @@ __global__ __launch_bounds__(256) void k_step(float *__restrict__ state,
     const int64_t d = c - b * dim;
     float xv = IO::ld(x, c);
     float dt = IO::ld(delta, c);
+    // every load goes out at the start (a load issued after the readout would add a
+    // second memory round trip to each wave's lifetime)
+    const float dsk = Dskip ? Dskip[d] : 0.f;
     if constexpr (FE) {
         // carried raw inputs of this channel: row r of conv_state is the token
         // K-1-r before this one
@@ -640,16 +733,20 @@ __global__ __launch_bounds__(256) void k_step(float *__restrict__ state,
     float h[SPL], av[SPL], bv[SPL], cv[SPL];
     float *sp = state + c * N + q * SPL;
     if constexpr (kVec) {
-        // N == NT (a multiple of 4) and 16-byte aligned state: vector accesses
-        const float4 v = *reinterpret_cast<const float4 *>(sp);
-        h[0] = v.x; h[1] = v.y; h[2] = v.z; h[3] = v.w;
-        const float4 va = *reinterpret_cast<const float4 *>(A + d * N + q * SPL);
-        av[0] = va.x; av[1] = va.y; av[2] = va.z; av[3] = va.w;
+        // N == NT (a multiple of 4), 16-byte aligned state and A, B and C rows
+        // aligned to 4 elements: vector accesses
 #pragma unroll
-        for (int j = 0; j < SPL; ++j) {
-            bv[j] = IO::ld(B, b * N + q * SPL + j);
-            cv[j] = IO::ld(C, b * N + q * SPL + j);
+        for (int j = 0; j < SPL; j += 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(sp + j);
+            h[j] = v.x; h[j + 1] = v.y; h[j + 2] = v.z; h[j + 3] = v.w;
         }
+#pragma unroll
+        for (int j = 0; j < SPL; j += 4) {
+            const float4 va = *reinterpret_cast<const float4 *>(A + d * N + q * SPL + j);
+            av[j] = va.x; av[j + 1] = va.y; av[j + 2] = va.z; av[j + 3] = va.w;
+        }
+        ldrow<SPL>(B + b * N + q * SPL, bv);
+        ldrow<SPL>(C + b * N + q * SPL, cv);
     } else {
 #pragma unroll
         for (int j = 0; j < SPL; ++j) {
@@ -661,30 +758,26 @@ __global__ __launch_bounds__(256) void k_step(float *__restrict__ state,
             cv[j] = ok ? IO::ld(C, b * N + n) : 0.f;
         }
     }
-    float yacc = 0.f;
-#pragma unroll
-    for (int j = 0; j < SPL; ++j) {
-        const float z = dt * av[j];
-        const float abar = exp2_hw(dt * (av[j] * kLog2e));
-        const float g = zoh_gain(dt, av[j], z, abar);
-        h[j] = fmaf(abar, h[j], g * (bv[j] * xv));
-        yacc = fmaf(cv[j], h[j], yacc);
-    }
+    const float a0 = A[d * N];
+    float yacc = step_lane<SPL, LPC>(q, N, dt, xv, a0, av, bv, cv, h);
 #pragma unroll
     for (int off = LPC / 2; off >= 1; off /= 2) yacc += __shfl_xor(yacc, off, LPC);
     if (!active) return;
     if constexpr (kVec) {
-        *reinterpret_cast<float4 *>(sp) = make_float4(h[0], h[1], h[2], h[3]);
+#pragma unroll
+        for (int j = 0; j < SPL; j += 4)
+            *reinterpret_cast<float4 *>(sp + j) = make_float4(h[j], h[j + 1], h[j + 2], h[j + 3]);
     } else {
 #pragma unroll
         for (int j = 0; j < SPL; ++j)
             if (q * SPL + j < N) sp[j] = h[j];
     }
-    if (q == 0) {
-        const float dsk = Dskip ? Dskip[d] : 0.f;
-        y[c] = IO::enc(fmaf(dsk, xv, yacc));
-    }
+    if (q == 0) y[c] = IO::enc(fmaf(dsk, xv, yacc));
 }
+
+
+// states per lane of the decode step (N above it: several lanes per channel)
+constexpr int kStepSpl = 8;
 
 int round_nt(int64_t N) { return N <= 1 ? 1 : N <= 2 ? 2 : N <= 4 ? 4 : N <= 8 ? 8 : 16; }
 
@@ -770,21 +863,23 @@ hipError_t forward_io(const FwdArgs &a, const FwdPlan &p, void *ws, hipStream_t 
 template <class IO, int NT, bool FE>
 hipError_t step_t(const StepArgs &a, hipStream_t s) {
     using T = typename IO::T;
-    constexpr int SPL = NT < 4 ? NT : 4;
+    constexpr int SPL = NT < kStepSpl ? NT : kStepSpl;
     constexpr int LPC = NT / SPL;
     const int64_t threads = a.batch * a.dim * LPC;
     const dim3 grid(unsigned((threads + 255) / 256));
-    const bool vec = (SPL == 4) && (a.N == NT) && (reinterpret_cast<uintptr_t>(a.state) % 16 == 0) &&
-                     (reinterpret_cast<uintptr_t>(a.A) % 16 == 0);
+    const uintptr_t rb = (sizeof(T) == 2 && SPL % 8 == 0 ? 8 : 4) * sizeof(T);  // one B or C load
+    const bool vec = (SPL % 4 == 0) && (a.N == NT) && (reinterpret_cast<uintptr_t>(a.state) % 16 == 0) &&
+                     (reinterpret_cast<uintptr_t>(a.A) % 16 == 0) && (reinterpret_cast<uintptr_t>(a.B) % rb == 0) &&
+                     (reinterpret_cast<uintptr_t>(a.C) % rb == 0);
     if (vec) {
-        if constexpr (SPL == 4)
-            hipLaunchKernelGGL((k_step<IO, NT, true, FE>), grid, dim3(256), 0, s, a.state,
+        if constexpr (SPL % 4 == 0)
+            hipLaunchKernelGGL((k_step<IO, NT, SPL, true, FE>), grid, dim3(256), 0, s, a.state,
                                static_cast<const T *>(a.x), static_cast<const T *>(a.delta), a.A,
                                static_cast<const T *>(a.B), static_cast<const T *>(a.C), a.Dskip,
                                static_cast<T *>(a.y), a.batch, a.dim, a.N, a.fe,
                                static_cast<T *>(a.conv_state));
     } else {
-        hipLaunchKernelGGL((k_step<IO, NT, false, FE>), grid, dim3(256), 0, s, a.state,
+        hipLaunchKernelGGL((k_step<IO, NT, SPL, false, FE>), grid, dim3(256), 0, s, a.state,
                            static_cast<const T *>(a.x), static_cast<const T *>(a.delta), a.A,
                            static_cast<const T *>(a.B), static_cast<const T *>(a.C), a.Dskip,
                            static_cast<T *>(a.y), a.batch, a.dim, a.N, a.fe,

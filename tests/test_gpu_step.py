@@ -93,10 +93,8 @@ def test_decode_1000_steps_bf16():
     assert e3 <= 1e-4 and e4 <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("N,io", [(16, "f32"), (16, "bf16"), (8, "f32"), (5, "bf16"), (1, "f32"), (2, "f32")])
-def test_steps_match_the_oracle_small(N, io):
-    wl = datagen.custom(f"stepsmall{N}{io}", 3, 40, 70, N, io, "loguniform", key=20 + N, mode="step")
-    A = datagen.gen_A(wl)
+def _steps_vs_oracle(wl, N, io, A=None):
+    A = datagen.gen_A(wl) if A is None else A
     D = datagen.gen_Dskip(wl)
     bias = datagen.gen_dt_bias(wl)
     At, Dt = torch.from_numpy(A).cuda(), torch.from_numpy(D).cuda()
@@ -110,6 +108,36 @@ def test_steps_match_the_oracle_small(N, io):
         yr, ref = oracle.step(ref, s["x"], s["delta"], A, s["B"], s["C"], D)
         assert rel_err(to_host(yt), yr) <= TOL[io], k
     assert rel_err(state.cpu().numpy(), ref) <= TOL[io]
+
+
+@pytest.mark.parametrize("N,io", [(16, "f32"), (16, "bf16"), (8, "f32"), (5, "bf16"), (1, "f32"), (2, "f32")])
+def test_steps_match_the_oracle_small(N, io):
+    """General A (an exp and the ZOH gain per state)."""
+    announce(f"step small general A N={N} io={io}")
+    _steps_vs_oracle(datagen.custom(f"stepsmall{N}{io}", 3, 40, 70, N, io, "loguniform", key=20 + N,
+                                    mode="step"), N, io)
+
+
+@pytest.mark.parametrize("N,io", [(16, "f32"), (16, "bf16"), (8, "f32"), (5, "f32"), (4, "f32"), (1, "f32")])
+def test_steps_structured_A(N, io):
+    """A = -(n+1): the structured-real update (one exp per lane, 1 - r^(n+1) by recurrence)."""
+    announce(f"step small structured A N={N} io={io}")
+    _steps_vs_oracle(datagen.custom(f"stepsr{N}{io}", 3, 40, 70, N, io, "s4d_real", key=50 + N,
+                                    mode="step"), N, io)
+
+
+def test_steps_mixed_A_rows():
+    """Structured rows beside general ones, a row structured only in its first eight
+    states (its lanes take different updates), A = 0, A > 0 and a tiny A row."""
+    announce("step mixed A rows")
+    wl = datagen.custom("stepmixed", 2, 30, 70, 16, "f32", "s4d_real", key=60, mode="step")
+    A = datagen.gen_A(wl).copy()
+    A[3] = -np.linspace(0.3, 3.0, 16, dtype=np.float32)          # unstructured
+    A[4, 8:] = A[4, 8:] * np.float32(1.5)                        # structured in states 0..7 only
+    A[5] = 0.0                                                    # A = 0: gain = delta
+    A[6] = np.float32(0.01) * np.arange(1, 17, dtype=np.float32)  # A > 0 (grows)
+    A[7] = A[0] * np.float32(1e-4)                                # tiny: the series branches
+    _steps_vs_oracle(wl, 16, "f32", A=A)
 
 
 def test_misaligned_state_uses_the_scalar_path():
