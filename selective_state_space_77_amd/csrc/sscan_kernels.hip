@@ -907,7 +907,7 @@ FwdPlan plan_forward(int64_t batch, int64_t L, int64_t dim, int64_t N) {
     p.nt = round_nt(N);
     p.tiles_per_batch = (dim + kWave - 1) / kWave;
     p.tiles = batch * p.tiles_per_batch;
-    // Segment kernels: enough segments for ~2 waves per SIMD (1024 SIMDs) with
+    // Segment kernels: enough segments for ~4 waves per SIMD (1024 SIMDs) with
     // segments of >= 64 tokens.
     const int64_t target_waves = kTargetWaves;
     int64_t S = p.tiles > 0 ? (target_waves + p.tiles - 1) / p.tiles : 1;
