@@ -390,8 +390,15 @@ __global__ __launch_bounds__(BW *kWave) void k_bwd(
         for (int i = 0; i < NPW; ++i) {
             const int n = w * NPW + i;
             if (n < NT) {
-                float P = s_k[0][n][lane];
-                for (int j = 1; j < BW; ++j) P = fmaf(m.run_decay(n, s_sum[j][lane]), P, s_k[j][n][lane]);
+                float dec[BW], kv[BW];
+#pragma unroll
+                for (int j = 0; j < BW; ++j) {
+                    dec[j] = m.run_decay(n, s_sum[j][lane]);
+                    kv[j] = s_k[j][n][lane];
+                }
+                float P = kv[0];
+#pragma unroll
+                for (int j = 1; j < BW; ++j) P = fmaf(dec[j], P, kv[j]);
                 s_pre[0][n][lane] = P;
             }
         }
@@ -486,22 +493,33 @@ __global__ __launch_bounds__(BW *kWave) void k_bwd(
         __syncthreads();
         // folds: states entering each run (left to right), adjoints entering each
         // run from the right (right to left), and the adjoint leaving the chunk
+        // (the runs' values and decays are read and formed first, independently, so
+        // that only the short fma chains are serial)
 #pragma unroll
         for (int i = 0; i < NPW; ++i) {
             const int n = w * NPW + i;
             if (n < NT) {
-                float P = s_k[0][n][lane];  // run 0 started from the chunk's entering state
+                float dec[BW], kv[BW], qv[BW];
+#pragma unroll
+                for (int j = 0; j < BW; ++j) {
+                    dec[j] = m.run_decay(n, s_sum[j][lane]);
+                    kv[j] = s_k[j][n][lane];
+                    qv[j] = s_q[j][n][lane];
+                }
+                float P = kv[0];  // run 0 started from the chunk's entering state
+#pragma unroll
                 for (int j = 1; j < BW; ++j) {
                     s_pre[j][n][lane] = P;
-                    P = fmaf(m.run_decay(n, s_sum[j][lane]), P, s_k[j][n][lane]);
+                    P = fmaf(dec[j], P, kv[j]);
                 }
                 float M = mu[i];
+#pragma unroll
                 for (int j = BW - 1; j >= 1; --j) {
                     s_mu[j][n][lane] = M;
-                    M = fmaf(m.run_decay(n, s_sum[j][lane]), M, s_q[j][n][lane]);
+                    M = fmaf(dec[j], M, qv[j]);
                 }
                 s_mu[0][n][lane] = M;
-                mu[i] = fmaf(m.run_decay(n, s_sum[0][lane]), M, s_q[0][n][lane]);
+                mu[i] = fmaf(dec[0], M, qv[0]);
             }
         }
         __syncthreads();
