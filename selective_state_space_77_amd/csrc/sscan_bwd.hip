@@ -196,19 +196,24 @@ struct FastMath {
         const float d0 = small ? (dv * z0) * p : g0 - dv;                       // g0 - delta
         const float ngq = -g0 * (g0 * alpha);                                  // -g0 (1 - r)
         const float qx = g0 * xv, gva = gv * inv_alpha;
-        float pw = r, s = 1.f, sprev = 0.f, E = 0.f, dxa = 0.f, dda = 0.f;
+        // Ep = E_n - (n+1) d0 = g0 sum_{j<=n} (r^j - 1), one-signed like E_n, so that
+        // u = E_n/(n+1) = Ep/(n+1) + d0 = gain_n - delta is one fma; then
+        //     alpha dh_n/dA_n = u w_n + delta k_n = u (w_n - k_n) + (u + delta) k_n,
+        // which reuses w_n - k_n from the delta gradient
+        float pw = r, s = 1.f, sprev = 0.f, Ep = 0.f, dxa = 0.f, dda = 0.f;
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-            E = fmaf(ngq, sprev, E + d0);
+            Ep = fmaf(ngq, sprev, Ep);
             const float l = fmaf(row[NT + n], gv, lc[n]);
             lc[n] = pw * l;
             const float ls = l * s;
             dxa = fmaf(ls, row[n], dxa);
             red.put(n, ls * qx);
             red.put(NT + n, gva * kt[n]);
-            const float w = row[n] * xv;
-            dda = fmaf(l * (w - kt[n]), float(n + 1), dda);
-            dA[n] = fmaf(l, fmaf(E * w, 1.f / float(n + 1), dv * kt[n]), dA[n]);
+            const float wk = fmaf(row[n], xv, -kt[n]);  // w_n - k_n
+            dda = fmaf(l * wk, float(n + 1), dda);
+            const float u = fmaf(Ep, 1.f / float(n + 1), d0);
+            dA[n] = fmaf(l, fmaf(u, wk, (u + dv) * kt[n]), dA[n]);
             sprev = s;
             s += pw;
             pw *= r;
