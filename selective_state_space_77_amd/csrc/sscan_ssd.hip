@@ -537,23 +537,61 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
     if (v == 14) *reinterpret_cast<v4s *>(&sGh[tile32(2, 1)][r][16 + 4 * q]) = v4s{0, 0, 0, 0};
     if (v == 15) *reinterpret_cast<v4s *>(&sGl[tile32(2, 1)][r][16 + 4 * q]) = v4s{0, 0, 0, 0};
 
+    // causal score tile k (token block tb, source block sb <= tb, row-major over the
+    // triangle): G^T tile (s-block sb, t-block tb) = B C^T, times exp(A (cum_t - cum_s))
+    // gain_s where s <= t, plus the skip D on the diagonal (D x is then part of the
+    // causal product), split into bf16 parts and stored as rows t, columns s
+    auto score_tile = [&](int k, int par) {
+        const int tb = k >= 6 ? 3 : k >= 3 ? 2 : k >= 1 ? 1 : 0;
+        const int sb = k - tb * (tb + 1) / 2;
+        const int tl = 16 * tb + r;
+        v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < NK; ++kb) {
+            const v8bf bf = *reinterpret_cast<const v8bf *>(&sB[16 * sb + r][32 * kb + 8 * q]);
+            const v8bf cf = *reinterpret_cast<const v8bf *>(&sC[tl][32 * kb + 8 * q]);
+            acc = mfma32(acc, bf, cf);
+        }
+        const float cum_t = sCum[par][tl];
+        v4s hi, lo;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int sl = 16 * sb + 4 * q + j;
+            const float m = acc[j] * exp2_hw(a2 * (cum_t - sCum[par][sl])) * sGain[par][sl];
+            const float gv = sl < tl ? m : sl == tl ? m + dsk : 0.f;
+            const uint16_t hb = f32_to_bf16(gv);
+            hi[j] = short(hb);
+            lo[j] = short(f32_to_bf16(gv - bfv(hb)));
+        }
+        *reinterpret_cast<v4s *>(&sGh[tile32(tb, sb / 2)][r][16 * (sb % 2) + 4 * q]) = hi;
+        *reinterpret_cast<v4s *>(&sGl[tile32(tb, sb / 2)][r][16 * (sb % 2) + 4 * q]) = lo;
+    };
+
     // chunk c is fetched during chunks c - 2 and c - 1 (two register sets, taken in
     // turn).  Chunks go in pairs, so an odd count ends with one past the end of the
     // sequence: its loads read 0 (delta 0: decay 1, gain 0, the state unchanged) and
     // its stores are dropped.  Fetches past the end are likewise unconditional: with
     // no branch around them the compiler waits only for the loads a stage needs.
+    // The two roles run loops of their own with the same three barriers per chunk, so
+    // that each loop issues one fixed sequence of loads.
     const int nchunks = nfull + (tail > 0);
-    auto chunk = [&](int c, Chunk &P, const Chunk &Pn) {
-        const int64_t t0 = int64_t(c) * SQ;
-        const int par = int(c & 1);  // which scalar set
-        stage(P, par);
-        __syncthreads();  // chunk staged; the state entering it published
-        fetch(c + 2, P);
+    Chunk P0, P1;
+    fetch(0, P0);
+    fetch(1, P1);
+    if (v == kScalarWave) scalars(P0, 0);
+    if (!outw) publish_state();  // the initial state
+    __syncthreads();
+    if (outw) {
+        auto chunk = [&](int c, Chunk &P) {
+            const int64_t t0 = int64_t(c) * SQ;
+            const int par = int(c & 1);  // which scalar set
+            stage(P, par);
+            __syncthreads();  // chunk staged; the state entering it published
+            fetch(c + 2, P);
 
-        // ---- phase A, output waves: S_in C^T for both tiles (the state operand's K
-        // steps serve both), kept in registers across the barrier
-        v4f off[2];
-        if (outw) {
+            // ---- phase A: S_in C^T for both tiles (the state operand's K steps serve
+            // both), kept in registers across the barrier, and score tile v
+            v4f off[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u) off[u] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -568,62 +606,12 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
                     off[u] = mfma32(off[u], sl, cb);
                 }
             }
-        }
-        // ---- phase A: causal score tile k (token block tb, source block sb <= tb,
-        // row-major over the triangle):
-        // G^T tile (s-block sb, t-block tb) = B C^T, times exp(A (cum_t - cum_s)) gain_s
-        // where s <= t, plus the skip D on the diagonal (D x is then part of the
-        // causal product), split into bf16 parts and stored as rows t, columns s
-        if (ktile >= 0) {
-            const int k = ktile;
-            const int tb = k >= 6 ? 3 : k >= 3 ? 2 : k >= 1 ? 1 : 0;
-            const int sb = k - tb * (tb + 1) / 2;
-            const int tl = 16 * tb + r;
-            v4f acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < NK; ++kb) {
-                const v8bf bf = *reinterpret_cast<const v8bf *>(&sB[16 * sb + r][32 * kb + 8 * q]);
-                const v8bf cf = *reinterpret_cast<const v8bf *>(&sC[tl][32 * kb + 8 * q]);
-                acc = mfma32(acc, bf, cf);
-            }
-            const float cum_t = sCum[par][tl];
-            v4s hi, lo;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int sl = 16 * sb + 4 * q + j;
-                const float m = acc[j] * exp2_hw(a2 * (cum_t - sCum[par][sl])) * sGain[par][sl];
-                const float gv = sl < tl ? m : sl == tl ? m + dsk : 0.f;
-                const uint16_t hb = f32_to_bf16(gv);
-                hi[j] = short(hb);
-                lo[j] = short(f32_to_bf16(gv - bfv(hb)));
-            }
-            *reinterpret_cast<v4s *>(&sGh[tile32(tb, sb / 2)][r][16 * (sb % 2) + 4 * q]) = hi;
-            *reinterpret_cast<v4s *>(&sGl[tile32(tb, sb / 2)][r][16 * (sb % 2) + 4 * q]) = lo;
-        }
-        // ---- phase A, state waves: S = exp(A sum delta) S + B^T diag(w) X
-        if (!outw) {
-            const float dec = sDec[par];
-#pragma unroll
-            for (int i = 0; i < NBW; ++i) S[i] *= dec;
-#pragma unroll
-            for (int kb = 0; kb < SQ / 32; ++kb) {
-                // (w x)[s = 32kb + 8q + j][16 pbs + r], both parts
-                const v8bf xh = ld_t(&sXWh[0][0], XP, 32 * kb, 16 * pbs);
-                const v8bf xl = ld_t(&sXWl[0][0], XP, 32 * kb, 16 * pbs);
-#pragma unroll
-                for (int i = 0; i < NBW; ++i) {
-                    const v8bf bt = ld_t(&sBT[0][0], TP, 32 * kb, 16 * (nb0 + i));  // B[s][16(nb0 + i) + r]
-                    S[i] = mfma32(S[i], bt, xh);
-                    S[i] = mfma32(S[i], bt, xl);
-                }
-            }
-        }
-        __syncthreads();  // scores in LDS; every read of the entering state done
+            score_tile(v, par);
+            __syncthreads();  // scores in LDS; every read of the entering state done
 
-        // ---- phase B, output waves: Y^T = X^T G'^T + (S_in C^T) diag(e), transposed:
-        // lane (r, q) ends with channels 16 pbo + 4q .. + 3 of token 16 tb + r and
-        // stores them as 8 bytes
-        if (outw) {
+            // ---- phase B: Y^T = X^T G'^T + (S_in C^T) diag(e), transposed: lane (r, q)
+            // ends with channels 16 pbo + 4q .. + 3 of token 16 tb + r and stores them
+            // as 8 bytes
             const rsrc_t rys = make_rsrc32(yb + t0 * rx, toks(c) * uint32_t(rx) * 2);
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
@@ -647,29 +635,55 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
                 __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, yv), rys,
                                                       uint32_t((tl * rx + 16 * pbo + 4 * q) * 2), 0, 0);
             }
-        } else {
-            // ---- phase B, state waves: publish the state entering the next chunk; the
-            // scalar wave also forms the next chunk's scalars
+            __syncthreads();  // every wave is done with this chunk's staged data
+        };
+        for (int c = 0; c < nchunks; c += 2) {
+            chunk(c, P0);
+            chunk(c + 1, P1);
+        }
+    } else {
+        auto chunk = [&](int c, Chunk &P, const Chunk &Pn) {
+            const int par = int(c & 1);
+            stage(P, par);
+            __syncthreads();  // chunk staged; the state entering it published
+            fetch(c + 2, P);
+
+            // ---- phase A: waves 8 and 9 a score tile, then S = exp(A sum delta) S +
+            // B^T diag(w) X
+            if (ktile >= 0) score_tile(ktile, par);
+            const float dec = sDec[par];
+#pragma unroll
+            for (int i = 0; i < NBW; ++i) S[i] *= dec;
+#pragma unroll
+            for (int kb = 0; kb < SQ / 32; ++kb) {
+                // (w x)[s = 32kb + 8q + j][16 pbs + r], both parts
+                const v8bf xh = ld_t(&sXWh[0][0], XP, 32 * kb, 16 * pbs);
+                const v8bf xl = ld_t(&sXWl[0][0], XP, 32 * kb, 16 * pbs);
+#pragma unroll
+                for (int i = 0; i < NBW; ++i) {
+                    const v8bf bt = ld_t(&sBT[0][0], TP, 32 * kb, 16 * (nb0 + i));  // B[s][16(nb0 + i) + r]
+                    S[i] = mfma32(S[i], bt, xh);
+                    S[i] = mfma32(S[i], bt, xl);
+                }
+            }
+            __syncthreads();  // scores in LDS; every read of the entering state done
+
+            // ---- phase B: the state entering the next chunk; the scalar wave also
+            // forms the next chunk's scalars
             publish_state();
             if (v == kScalarWave) scalars(Pn, par ^ 1);
+            __syncthreads();  // every wave is done with this chunk's staged data
+        };
+        for (int c = 0; c < nchunks; c += 2) {
+            chunk(c, P0, P1);
+            chunk(c + 1, P1, P0);
         }
-        __syncthreads();  // every wave is done with this chunk's staged data
-    };
-    Chunk P0, P1;
-    fetch(0, P0);
-    fetch(1, P1);
-    if (v == kScalarWave) scalars(P0, 0);
-    if (!outw) publish_state();  // the initial state
-    __syncthreads();
-    for (int c = 0; c < nchunks; c += 2) {
-        chunk(c, P0, P1);
-        chunk(c + 1, P1, P0);
-    }
-    if (hT && !outw) {
+        if (hT) {
 #pragma unroll
-        for (int i = 0; i < NBW; ++i)
+            for (int i = 0; i < NBW; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) hT[hrow + 16 * (nb0 + i) + 4 * q + j] = S[i][j];
+                for (int j = 0; j < 4; ++j) hT[hrow + 16 * (nb0 + i) + 4 * q + j] = S[i][j];
+        }
     }
 }
 
