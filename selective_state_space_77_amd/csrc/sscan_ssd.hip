@@ -358,24 +358,24 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
     // LDS pitches (bf16).  A 16-byte read of rows r = 0..15 at one column is
     // conflict-free on gfx950's 64 banks when the pitch is 8 (mod 16) dwords, so
     // tiles read by rows take NS + 16 (72 or 40 dwords); transposing reads run at
-    // one 4 x 16 block per group for any of these pitches.
-    constexpr int RP = NS + 16;        // tiles read by rows
-    constexpr int TP = NS + 16;        // B read transposed
+    // one 4 x 16 block per group for any of these pitches, so B serves both ways.
+    constexpr int RP = NS + 16;        // [token or channel][state] tiles
     constexpr int XP = SP + 16;        // x read transposed
     constexpr int NBW = NS / 32;       // 16x16 state tiles per state wave (8 waves: 4 channel blocks x 2 halves)
     constexpr int BPL = NS / 16;       // bf16 of a B (or C) row per lane: 16 lanes to a row
     constexpr int NG = 10;             // causal 16x16 score tiles of a 64-token chunk
     constexpr int NM = 6;              // 16 x 32 tiles they are stored in
     constexpr int GP = 48;             // row pitch (bf16) of the stored score tiles (24 dwords)
-    constexpr int kScalarWave = 15;    // a state wave: it forms the next chunk's scalars after the scores
+    constexpr int kScalarWave = 7;    // an output wave: it forms the next chunk's scalars after its score tile
     static_assert(BWV == 16 && SQ == 64 && SP == 64, "work split");
     using VB = typename std::conditional<BPL == 8, v4u, v2u>::type;
-    __shared__ __align__(16) uint16_t sX[SQ][XP];    // x of the chunk, [token][channel]
-    __shared__ __align__(16) uint16_t sXWh[SQ][XP];  // w_s x, bf16 high part
-    __shared__ __align__(16) uint16_t sXWl[SQ][XP];  // and remainder
-    __shared__ __align__(16) uint16_t sBT[SQ][TP];   // B, [token][state], read transposed
-    __shared__ __align__(16) uint16_t sB[SQ][RP];    // B, [token][state], read by rows
-    __shared__ __align__(16) uint16_t sC[SQ][RP];    // C, [token][state]
+    // a chunk's x (two sets: chunk c in set c % 2, as the outputs of chunk c read it
+    // while chunk c + 1 is staged), w x, B and C (read before the scores barrier only)
+    __shared__ __align__(16) uint16_t sX[2][SQ][XP];  // x, [token][channel]
+    __shared__ __align__(16) uint16_t sXWh[SQ][XP];   // w_s x, bf16 high part
+    __shared__ __align__(16) uint16_t sXWl[SQ][XP];   // and remainder
+    __shared__ __align__(16) uint16_t sB[SQ][RP];     // B, [token][state], read by rows and transposed
+    __shared__ __align__(16) uint16_t sC[SQ][RP];     // C, [token][state]
     __shared__ __align__(16) uint16_t sSh[SP][RP];   // entering state, [channel][state], bf16
     __shared__ __align__(16) uint16_t sSl[SP][RP];   // and its remainder
     // masked scores as 16 x 32 tiles [t][s] (B operand of the transposed causal product):
@@ -383,7 +383,7 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
     __shared__ __align__(16) uint16_t sGh[NM][16][GP];
     __shared__ __align__(16) uint16_t sGl[NM][16][GP];
     // per-token scalars, two sets: those of chunk c + 1 are formed during chunk c
-    __shared__ float sCum[2][SQ], sGain[2][SQ], sW[2][SQ], sE[2][SQ];
+    __shared__ __align__(16) float sCum[2][SQ], sGain[2][SQ], sW[2][SQ], sE[2][SQ];
     __shared__ float sDec[2];
 
     const int tid = int(threadIdx.x);
@@ -456,10 +456,11 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
         sE[par][lane] = exp2_hw(a2 * cum);
         if (lane == 0) sDec[par] = exp2_hw(a2 * total);
     };
-    // staging; x also as w_s x split into bf16 parts (the update's operand, formed
-    // once here rather than by the waves that share a channel block)
+    // staging of the chunk with scalar set par; x also as w_s x split into bf16 parts
+    // (the update's operand, formed once here rather than by the waves that share a
+    // channel block)
     auto stage = [&](const Chunk &P, int par) {
-        *reinterpret_cast<v2u *>(&sX[srow][xc]) = P.px;
+        *reinterpret_cast<v2u *>(&sX[par][srow][xc]) = P.px;
         {
             const float w = sW[par][srow];
             const uint16_t *xv = reinterpret_cast<const uint16_t *>(&P.px);
@@ -475,7 +476,6 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
             *reinterpret_cast<v4s *>(&sXWl[srow][xc]) = lo;
         }
         *reinterpret_cast<VB *>(&sB[srow][bc]) = P.pb;
-        *reinterpret_cast<VB *>(&sBT[srow][bc]) = P.pb;
         *reinterpret_cast<VB *>(&sC[srow][bc]) = P.pc;
     };
     // K = 32 operand from a [k][column] tile: lane (r, q) gets rows k0 + 8q .. k0 + 8q + 7
@@ -488,26 +488,17 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     };
 
-    // ---- wave roles.  Output waves (v < 8) form C S_in for two output tiles and one
-    // score tile before the scores are all ready, and (scores) X after; state waves
-    // (v >= 8) update a quarter of the state before (waves 8 and 9 also take a score
-    // tile) and publish it after.
+    // ---- wave roles.  Output waves (v < 8) form C S_in for two output tiles and a
+    // score tile before the scores barrier, and (scores) X after; state waves (v >= 8)
+    // update a quarter of the state before (waves 8 and 9 also take a score tile) and
+    // publish it after.  (The older waves of a SIMD get its issue slots first: with
+    // the state waves first the output products after the barrier ran last.)
     // State tiles of state wave v: channel block pbs, state blocks nb0..nb0+NBW-1;
     // S[i][j] = S[n = 16(nb0 + i) + 4q + j][p = 16 pbs + r]
     const bool outw = v < 8;
     const int pbs = v % 4, nb0 = NBW * ((v / 4) % 2);
     v4f S[NBW];
     const int64_t hrow = ((b * H + h) * SP + 16 * pbs + r) * NS;
-    {
-        // the initial state through a descriptor of 0 bytes when there is none (reads
-        // 0): no branch around these loads, which would make the compiler wait for
-        // every outstanding load at the loop head
-        const rsrc_t rh = make_rsrc32(h0 && !outw ? h0 + (b * H + h) * SP * NS : nullptr, h0 && !outw ? SP * NS * 4 : 0);
-#pragma unroll
-        for (int i = 0; i < NBW; ++i)
-            S[i] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
-                                               rh, uint32_t(((16 * pbs + r) * NS + 16 * (nb0 + i) + 4 * q) * 4), 0, 0));
-    }
     auto publish_state = [&]() {
 #pragma unroll
         for (int i = 0; i < NBW; ++i) {
@@ -567,30 +558,34 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
         *reinterpret_cast<v4s *>(&sGl[tile32(tb, sb / 2)][r][16 * (sb % 2) + 4 * q]) = lo;
     };
 
-    // chunk c is fetched during chunks c - 2 and c - 1 (two register sets, taken in
-    // turn).  Chunks go in pairs, so an odd count ends with one past the end of the
-    // sequence: its loads read 0 (delta 0: decay 1, gain 0, the state unchanged) and
-    // its stores are dropped.  Fetches past the end are likewise unconditional: with
-    // no branch around them the compiler waits only for the loads a stage needs.
-    // The two roles run loops of their own with the same three barriers per chunk, so
-    // that each loop issues one fixed sequence of loads.
+    // Chunk c is fetched into registers during chunk c - 2 and staged into LDS during
+    // chunk c - 1, after the scores barrier (its scalars are formed before it), so a
+    // chunk has two barriers: scores ready, and chunk done.  Chunks go in pairs, so an
+    // odd count ends with one past the end of the sequence: its loads read 0 (delta
+    // 0: decay 1, gain 0, the state unchanged) and its stores are dropped.  Fetches
+    // past the end are likewise unconditional: with no branch around them the
+    // compiler waits only for the loads a stage needs.  The two roles run loops of
+    // their own with the same barriers, so that each loop issues one fixed sequence of
+    // loads, and prologues of their own: a load issued before the split whose result
+    // one role never uses would leave its registers pending into that role's loop,
+    // where the compiler then waits for every load at the loop head.
     const int nchunks = nfull + (tail > 0);
     Chunk P0, P1;
-    fetch(0, P0);
-    fetch(1, P1);
-    if (v == kScalarWave) scalars(P0, 0);
-    if (!outw) publish_state();  // the initial state
-    __syncthreads();
     if (outw) {
-        auto chunk = [&](int c, Chunk &P) {
+        fetch(0, P0);
+        fetch(1, P1);
+        if (v == kScalarWave) scalars(P0, 0);
+        __syncthreads();  // scalars of chunk 0
+        stage(P0, 0);
+        fetch(2, P0);
+        __syncthreads();  // chunk 0 staged
+        // chunk c with its x in LDS set par; Pn holds chunk c + 1 in registers
+        auto chunk = [&](int c, int par, Chunk &Pn) {
             const int64_t t0 = int64_t(c) * SQ;
-            const int par = int(c & 1);  // which scalar set
-            stage(P, par);
-            __syncthreads();  // chunk staged; the state entering it published
-            fetch(c + 2, P);
 
             // ---- phase A: S_in C^T for both tiles (the state operand's K steps serve
-            // both), kept in registers across the barrier, and score tile v
+            // both), kept in registers across the barrier, score tile v, and on the
+            // scalar wave chunk c + 1's scalars
             v4f off[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u) off[u] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -606,12 +601,13 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
                     off[u] = mfma32(off[u], sl, cb);
                 }
             }
-            score_tile(v, par);
-            __syncthreads();  // scores in LDS; every read of the entering state done
+            score_tile(ktile, par);
+            if (v == kScalarWave) scalars(Pn, par ^ 1);
+            __syncthreads();  // scores and scalars in LDS; every read of S_in, B, C, w x done
 
             // ---- phase B: Y^T = X^T G'^T + (S_in C^T) diag(e), transposed: lane (r, q)
             // ends with channels 16 pbo + 4q .. + 3 of token 16 tb + r and stores them
-            // as 8 bytes
+            // as 8 bytes; then chunk c + 1 staged and chunk c + 3 fetched
             const rsrc_t rys = make_rsrc32(yb + t0 * rx, toks(c) * uint32_t(rx) * 2);
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
@@ -622,7 +618,7 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
                 for (int sp = 0; sp < 2; ++sp) {
                     if (32 * sp > 16 * tb + 15) break;
                     const int m = tile32(tb, sp);
-                    const v8bf xa = ld_t(&sX[0][0], XP, 32 * sp, 16 * pbo);  // x[s = 32sp + 8q + j][16 pbo + r]
+                    const v8bf xa = ld_t(&sX[par][0][0], XP, 32 * sp, 16 * pbo);  // x[s = 32sp + 8q + j][16 pbo + r]
                     const v8bf gh = *reinterpret_cast<const v8bf *>(&sGh[m][r][8 * q]);
                     const v8bf gl = *reinterpret_cast<const v8bf *>(&sGl[m][r][8 * q]);
                     acc = mfma32(acc, xa, gh);
@@ -635,19 +631,32 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
                 __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, yv), rys,
                                                       uint32_t((tl * rx + 16 * pbo + 4 * q) * 2), 0, 0);
             }
-            __syncthreads();  // every wave is done with this chunk's staged data
+            stage(Pn, par ^ 1);
+            fetch(c + 3, Pn);
+            __syncthreads();  // chunk c done; chunk c + 1 staged
         };
         for (int c = 0; c < nchunks; c += 2) {
-            chunk(c, P0);
-            chunk(c + 1, P1);
+            chunk(c, 0, P1);
+            chunk(c + 1, 1, P0);
         }
     } else {
-        auto chunk = [&](int c, Chunk &P, const Chunk &Pn) {
-            const int par = int(c & 1);
-            stage(P, par);
-            __syncthreads();  // chunk staged; the state entering it published
-            fetch(c + 2, P);
-
+        {
+            // the initial state through a descriptor of 0 bytes when there is none
+            // (reads 0), with no branch around these loads
+            const rsrc_t rh = make_rsrc32(h0 ? h0 + (b * H + h) * SP * NS : nullptr, h0 ? SP * NS * 4 : 0);
+#pragma unroll
+            for (int i = 0; i < NBW; ++i)
+                S[i] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   rh, uint32_t(((16 * pbs + r) * NS + 16 * (nb0 + i) + 4 * q) * 4), 0, 0));
+        }
+        fetch(0, P0);
+        fetch(1, P1);
+        __syncthreads();  // scalars of chunk 0
+        stage(P0, 0);
+        fetch(2, P0);
+        publish_state();  // the initial state
+        __syncthreads();  // chunk 0 staged
+        auto chunk = [&](int c, int par, Chunk &Pn) {
             // ---- phase A: waves 8 and 9 a score tile, then S = exp(A sum delta) S +
             // B^T diag(w) X
             if (ktile >= 0) score_tile(ktile, par);
@@ -661,22 +670,23 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
                 const v8bf xl = ld_t(&sXWl[0][0], XP, 32 * kb, 16 * pbs);
 #pragma unroll
                 for (int i = 0; i < NBW; ++i) {
-                    const v8bf bt = ld_t(&sBT[0][0], TP, 32 * kb, 16 * (nb0 + i));  // B[s][16(nb0 + i) + r]
+                    const v8bf bt = ld_t(&sB[0][0], RP, 32 * kb, 16 * (nb0 + i));  // B[s][16(nb0 + i) + r]
                     S[i] = mfma32(S[i], bt, xh);
                     S[i] = mfma32(S[i], bt, xl);
                 }
             }
-            __syncthreads();  // scores in LDS; every read of the entering state done
+            __syncthreads();  // scores and scalars in LDS; every read of S_in, B, C, w x done
 
-            // ---- phase B: the state entering the next chunk; the scalar wave also
-            // forms the next chunk's scalars
+            // ---- phase B: the state entering chunk c + 1, then chunk c + 1 staged and
+            // chunk c + 3 fetched
             publish_state();
-            if (v == kScalarWave) scalars(Pn, par ^ 1);
-            __syncthreads();  // every wave is done with this chunk's staged data
+            stage(Pn, par ^ 1);
+            fetch(c + 3, Pn);
+            __syncthreads();  // chunk c done; chunk c + 1 staged
         };
         for (int c = 0; c < nchunks; c += 2) {
-            chunk(c, P0, P1);
-            chunk(c + 1, P1, P0);
+            chunk(c, 0, P1);
+            chunk(c + 1, 1, P0);
         }
         if (hT) {
 #pragma unroll
