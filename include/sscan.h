@@ -238,8 +238,10 @@ int sscan_step_fused(float *state, void *conv_state, const void *x_t, const floa
  *   B, C          (batch, seqlen, ngroups, dstate), io_dtype.
  *   initial_state, final_state  (batch, nheads, headdim, dstate) fp32, or NULL.
  *   headdim == 64; dstate 64 or 128; nheads a multiple of ngroups.
- * Products run on the matrix cores in the precision of io_dtype (bf16 operands with
- * fp32 accumulation for SSCAN_BF16; fp32 for SSCAN_F32); the carried state is fp32.
+ * Products run on the matrix cores with fp32 accumulation: for SSCAN_BF16 on bf16
+ * operands, where the operands computed in fp32 (the masked scores, w x and the
+ * state) enter as two bf16 parts each (high part + remainder); for SSCAN_F32 on
+ * fp32 operands.  The carried state is fp32.
  * Returns SSCAN_OK or a negative sscan_status.
  */
 int sscan_ssd_forward(const void *x, const void *delta, const float *A, const void *B, const void *C,

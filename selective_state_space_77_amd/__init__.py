@@ -113,6 +113,19 @@ def _dev(t: torch.Tensor | None, name: str, dtype=None):
     return t.data_ptr()
 
 
+def _shape(t: torch.Tensor | None, name: str, shape) -> None:
+    """An output buffer given by the caller must have the output's shape: the kernels
+    write every element of it."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+
+
+def _one_device(*ts: torch.Tensor | None) -> None:
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"all tensors must be on one device, got {sorted(map(str, devs))}")
+
+
 def _stream(stream, device) -> int:
     s = torch.cuda.current_stream(device) if stream is None else stream
     return s.cuda_stream if isinstance(s, torch.cuda.Stream) else int(s)
@@ -129,7 +142,9 @@ def forward(x, delta, A, B, C, Dskip=None, y=None, final_state=None, stream=None
         raise ValueError("inconsistent shapes")
     if y is None:
         y = torch.empty_like(x)
+    _shape(y, "y", x.shape)
     io = _io_code(x, delta, B, C, y)
+    _one_device(x, delta, A, B, C, Dskip, y, final_state, initial_state)
     if Dskip is not None and tuple(Dskip.shape) != (dim,):
         raise ValueError("Dskip must have shape (dim,)")
     if final_state is not None and tuple(final_state.shape) != (batch, dim, N):
@@ -177,7 +192,10 @@ def forward_fused(x, conv_weight, delta_raw, A, B, C, Dskip=None, conv_bias=None
             raise ValueError(f"{name} must have shape {shape}")
     if y is None:
         y = torch.empty_like(x)
+    _shape(y, "y", x.shape)
     io = _io_code(x, delta_raw, B, C, y, *(t for t in (conv_state, conv_state_out) if t is not None))
+    _one_device(x, conv_weight, delta_raw, A, B, C, Dskip, conv_bias, delta_bias, conv_state,
+                initial_state, y, final_state, conv_state_out)
     rc = lib.sscan_forward_fused(
         _dev(x, "x"), _dev(conv_weight, "conv_weight", torch.float32),
         _dev(conv_bias, "conv_bias", torch.float32), K, _act_code(activation),
@@ -204,7 +222,15 @@ def step_fused(state, conv_state, x_t, conv_weight, delta_raw_t, A, B_t, C_t, Ds
         raise ValueError("conv_state must have shape (batch, d_conv-1, dim)")
     if y_t is None:
         y_t = torch.empty_like(x_t)
+    _shape(y_t, "y_t", x_t.shape)
+    if Dskip is not None and tuple(Dskip.shape) != (dim,):
+        raise ValueError("Dskip must have shape (dim,)")
+    for t, name in ((conv_bias, "conv_bias"), (delta_bias, "delta_bias")):
+        if t is not None and tuple(t.shape) != (dim,):
+            raise ValueError(f"{name} must have shape (dim,)")
     io = _io_code(x_t, delta_raw_t, B_t, C_t, y_t, *(() if conv_state is None else (conv_state,)))
+    _one_device(state, conv_state, x_t, conv_weight, delta_raw_t, A, B_t, C_t, Dskip, conv_bias,
+                delta_bias, y_t)
     rc = lib.sscan_step_fused(
         _dev(state, "state", torch.float32), _dev(conv_state, "conv_state"), _dev(x_t, "x_t"),
         _dev(conv_weight, "conv_weight", torch.float32), _dev(conv_bias, "conv_bias", torch.float32),
@@ -229,6 +255,7 @@ def backward(x, delta, A, B, C, dy, Dskip=None, initial_state=None, dfinal_state
             or B.shape != (batch, L, N) or C.shape != B.shape:
         raise ValueError("inconsistent shapes")
     io = _io_code(x, delta, B, C, dy)
+    _one_device(x, delta, A, B, C, dy, Dskip, initial_state, dfinal_state)
     for t, name, shape in ((Dskip, "Dskip", (dim,)), (initial_state, "initial_state", (batch, dim, N)),
                            (dfinal_state, "dfinal_state", (batch, dim, N))):
         if t is not None and tuple(t.shape) != shape:
@@ -259,7 +286,9 @@ def step(state, x_t, delta_t, A, B_t, C_t, Dskip=None, y_t=None, stream=None):
         raise ValueError("inconsistent shapes")
     if y_t is None:
         y_t = torch.empty_like(x_t)
+    _shape(y_t, "y_t", x_t.shape)
     io = _io_code(x_t, delta_t, B_t, C_t, y_t)
+    _one_device(state, x_t, delta_t, A, B_t, C_t, Dskip, y_t)
     if Dskip is not None and tuple(Dskip.shape) != (dim,):
         raise ValueError("Dskip must have shape (dim,)")
     rc = lib.sscan_step(_dev(state, "state", torch.float32), _dev(x_t, "x_t"), _dev(delta_t, "delta_t"),
@@ -292,7 +321,9 @@ def ssd_forward(x, delta, A, B, C, Dskip=None, initial_state=None, y=None, final
             raise ValueError(f"{name} must have shape {shape}")
     if y is None:
         y = torch.empty_like(x)
+    _shape(y, "y", x.shape)
     io = _io_code(x, delta, B, C, y)
+    _one_device(x, delta, A, B, C, Dskip, initial_state, y, final_state)
     rc = lib.sscan_ssd_forward(_dev(x, "x"), _dev(delta, "delta"), _dev(A, "A", torch.float32),
                                _dev(B, "B"), _dev(C, "C"), _dev(Dskip, "Dskip", torch.float32),
                                _dev(initial_state, "initial_state", torch.float32), _dev(y, "y"),

@@ -235,6 +235,27 @@ def test_python_binding_rejects_host_tensors():
                   torch.zeros(1, 4, 3).double())
 
 
+def test_python_binding_checks_output_shapes_before_any_device_work():
+    """An output buffer of the wrong shape would be written past its end by the
+    kernels; the binding refuses it (host tensors reach the shape check first)."""
+    import torch
+    import selective_state_space_77_amd as s
+    x = torch.zeros(1, 4, 2)
+    A, B = torch.zeros(2, 3), torch.zeros(1, 4, 3)
+    with pytest.raises(ValueError, match="y must have shape"):
+        s.forward(x, x.clone(), A, B, B.clone(), y=torch.zeros(1, 3, 2))
+    with pytest.raises(ValueError, match="y_t must have shape"):
+        s.step(torch.zeros(1, 2, 3), torch.zeros(1, 2), torch.zeros(1, 2), A, torch.zeros(1, 3),
+               torch.zeros(1, 3), y_t=torch.zeros(1, 1))
+    with pytest.raises(ValueError, match="y must have shape"):
+        xs = torch.zeros(1, 4, 2, 64)
+        Bs = torch.zeros(1, 4, 1, 64)
+        s.ssd_forward(xs, torch.zeros(1, 4, 2), torch.zeros(2), Bs, Bs.clone(), y=torch.zeros(1, 4, 2, 32))
+    with pytest.raises(ValueError, match="Dskip must have shape"):
+        s.step_fused(torch.zeros(1, 2, 3), torch.zeros(1, 3, 2), torch.zeros(1, 2), torch.zeros(2, 4),
+                     torch.zeros(1, 2), A, torch.zeros(1, 3), torch.zeros(1, 3), Dskip=torch.zeros(5))
+
+
 def test_product_package_does_not_reference_the_oracle():
     pkg = os.path.join(ROOT, "selective_state_space_77_amd")
     for dirpath, _, files in os.walk(pkg):
