@@ -17,6 +17,8 @@ sample on the host cores.
 workload, dy and dfinal_state seeded like x); --pass fused times
 sscan_forward_fused (d_conv = 4, SiLU, carried inputs and biases) on the same
 workload, x being the convolution's raw input and delta the raw step size.
+--workload decode_bf16 times sscan_step, --workload mamba2_bf16 sscan_ssd_forward and
+--workload mamba2_decode_bf16 sscan_ssd_step (the scalar-A-per-head scan and its step).
 """
 from __future__ import annotations
 
@@ -397,6 +399,62 @@ def bench_step(wl, args, dev) -> int:
     return 0
 
 
+def bench_ssd_step(wl, args, dev) -> int:
+    """Scalar-A-per-head decode: one step = one sscan_ssd_step over the (batch, heads, 64, N)
+    fp32 state in HBM, token inputs cycled through wl.seqlen pre-staged ones."""
+    import torch
+
+    import datagen
+    import selective_state_space_77_amd as sscan
+
+    inp = datagen.ssd_inputs(wl)
+    to = (lambda a: torch.from_numpy(datagen.bf16_bits(a).view(np.int16)).to(dev).view(torch.bfloat16)) \
+        if wl.io == "bf16" else (lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev))
+    # token-major staging: step k reads row k of each
+    X, Dl, Bs, Cs = (to(np.ascontiguousarray(np.moveaxis(inp[k], 1, 0))) for k in ("x", "delta", "B", "C"))
+    A, D = torch.from_numpy(inp["A"]).to(dev), torch.from_numpy(inp["D"]).to(dev)
+    state = torch.zeros(wl.batch, wl.nheads, wl.headdim, wl.dstate, device=dev)
+    Y = torch.empty_like(X)
+    nstage = wl.seqlen
+    stream = torch.cuda.current_stream(dev)
+    print(f"[bench] ssd decode {wl.name}: batch={wl.batch} heads={wl.nheads} P={wl.headdim} "
+          f"groups={wl.ngroups} N={wl.dstate} io={wl.io}", file=sys.stderr, flush=True)
+    for k in range(args.warmup):
+        j = k % nstage
+        sscan.ssd_step(state, X[j], Dl[j], A, Bs[j], Cs[j], D, y_t=Y[j], stream=stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k, (e0, e1) in enumerate(ev):
+        j = k % nstage
+        e0.record(stream)
+        sscan.ssd_step(state, X[j], Dl[j], A, Bs[j], Cs[j], D, y_t=Y[j], stream=stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per_step = (time.perf_counter() - t0) / args.steps
+    ev_avg = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e-3
+    es = 2 if wl.io == "bf16" else 4
+    chans = wl.batch * wl.nheads * wl.headdim
+    nbytes = (2 * chans * wl.dstate * 4 + 2 * chans * es + wl.batch * wl.nheads * es
+              + 2 * wl.batch * wl.ngroups * wl.dstate * es + 2 * wl.nheads * 4)
+    gbs = nbytes / ev_avg / 1e9
+    print(json.dumps({
+        "metric": "scalar-A-per-head decode step: B*H*P elements/s (+ achieved HBM GB/s vs MI355X peak)",
+        "value": chans / per_step, "unit": "elements/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": per_step * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": f"synthetic (seeded, {nstage} pre-staged tokens cycled)",
+        "config": {"workload": wl.name, "batch": wl.batch, "nheads": wl.nheads, "headdim": wl.headdim,
+                   "ngroups": wl.ngroups, "dstate": wl.dstate, "io_dtype": wl.io},
+        "roofline": {"kernel": "k_ssd_step", "bound": "hbm", "achieved": round(gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": None,
+                     "per_launch": {"algorithmic_bytes": nbytes, "event_avg_us": round(ev_avg * 1e6, 2)}},
+        "cpu_baseline": None}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -421,7 +479,8 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.workload in datagen.SSD_WORKLOADS:
-        return bench_ssd(datagen.SSD_WORKLOADS[args.workload], args, dev)
+        swl = datagen.SSD_WORKLOADS[args.workload]
+        return (bench_ssd_step if swl.mode == "step" else bench_ssd)(swl, args, dev)
     wl = datagen.workload(args.workload)
     if wl.mode == "step":
         return bench_step(wl, args, dev)

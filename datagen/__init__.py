@@ -289,6 +289,7 @@ class SsdWorkload:
     ngroups: int
     dstate: int
     io: str
+    mode: str = "scan"  # "step": seqlen tokens staged for decode steps
 
     @property
     def elements(self) -> int:
@@ -300,6 +301,8 @@ SSD_WORKLOADS = {
         # inner width 4096 (64 heads x 64) as the benchmarked per-channel workload, N = 128
         SsdWorkload("mamba2_bf16", 20, 4, 8192, 64, 64, 1, 128, "bf16"),
         SsdWorkload("mamba2_small_f32", 21, 2, 1000, 8, 64, 2, 64, "f32"),
+        # decode steps at the same width: 64 sequences, 128 MB fp32 state, 64 staged tokens
+        SsdWorkload("mamba2_decode_bf16", 22, 64, 64, 64, 64, 1, 128, "bf16", mode="step"),
     )
 }
 

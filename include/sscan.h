@@ -249,6 +249,31 @@ int sscan_ssd_forward(const void *x, const void *delta, const float *A, const vo
                       int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t ngroups,
                       int64_t dstate, int io_dtype, void *stream);
 
+/*
+ * One decode step of the scalar-A-per-head scan: the recurrence of
+ * sscan_ssd_forward for a single token, with the state read and written in place
+ * (the state of the duality's recurrent form: "Mamba matches the Transformer...",
+ * the duality section; generation at constant work per token, "State space
+ * models and Mamba", cost table).  Per batch row b, head h (group g as above):
+ *     state[b,h,p,n] = exp(delta A[h]) state[b,h,p,n] + gain B[b,g,n] x[b,h,p]
+ *     y[b,h,p] = sum_n C[b,g,n] state[b,h,p,n] + Dskip[h] x[b,h,p]
+ * so that running it over the tokens of a sequence from the final_state of a
+ * sscan_ssd_forward prefill continues that sequence.
+ *
+ *   state         [in/out] (batch, nheads, headdim, dstate) fp32.  Must not overlap any
+ *                      other argument.
+ *   x_t, y_t      (batch, nheads, headdim), io_dtype.
+ *   delta_t       (batch, nheads), io_dtype, after its softplus.
+ *   A             (nheads) fp32.   Dskip (nheads) fp32 or NULL.
+ *   B_t, C_t      (batch, ngroups, dstate), io_dtype.
+ *   headdim == 64; dstate 64 or 128; nheads a multiple of ngroups.
+ * All arithmetic is fp32 (no matrix instructions: one token is a rank-1 update).
+ * Returns SSCAN_OK or a negative sscan_status.
+ */
+int sscan_ssd_step(float *state, const void *x_t, const void *delta_t, const float *A, const void *B_t,
+                   const void *C_t, const float *Dskip, void *y_t, int64_t batch, int64_t nheads,
+                   int64_t headdim, int64_t ngroups, int64_t dstate, int io_dtype, void *stream);
+
 /* Static text for a status code (never NULL). */
 const char *sscan_status_string(int status);
 

@@ -14,6 +14,7 @@ package raises.
     step(state, x_t, delta_t, A, B_t, C_t, Dskip=None, y_t=None, stream=None)
     ssd_forward(x, delta, A, B, C, Dskip=None, initial_state=None, y=None, final_state=None,
                 stream=None)
+    ssd_step(state, x_t, delta_t, A, B_t, C_t, Dskip=None, y_t=None, stream=None)
     step_fused(state, conv_state, x_t, conv_weight, delta_raw_t, A, B_t, C_t, Dskip=None,
                conv_bias=None, delta_bias=None, activation=None, y_t=None, stream=None)
 
@@ -70,6 +71,8 @@ def _load() -> ctypes.CDLL:
     lib.sscan_ssd_forward.argtypes = [vp, vp, fp, vp, vp, fp, fp, vp, fp, i64, i64, i64, i64, i64, i64,
                                       ci, vp]
     lib.sscan_ssd_forward.restype = ctypes.c_int
+    lib.sscan_ssd_step.argtypes = [fp, vp, vp, fp, vp, vp, fp, vp, i64, i64, i64, i64, i64, ci, vp]
+    lib.sscan_ssd_step.restype = ctypes.c_int
     lib.sscan_step.argtypes = [fp, vp, vp, fp, vp, vp, fp, vp, i64, i64, i64, ctypes.c_int, vp]
     lib.sscan_step.restype = ctypes.c_int
     lib.sscan_status_string.argtypes = [ctypes.c_int]
@@ -331,3 +334,29 @@ def ssd_forward(x, delta, A, B, C, Dskip=None, initial_state=None, y=None, final
                                _stream(stream, x.device))
     _check(rc)
     return y
+
+
+def ssd_step(state, x_t, delta_t, A, B_t, C_t, Dskip=None, y_t=None, stream=None):
+    """One decode step of the scalar-A-per-head scan; updates `state` in place and
+    returns y_t.
+
+    state: (batch, H, P, N) fp32 with P = 64, N in {64, 128}; x_t, y_t: (batch, H, P);
+    delta_t: (batch, H); A, Dskip: (H,) fp32; B_t, C_t: (batch, G, N) with G | H."""
+    batch, H, P, N = state.shape
+    G = B_t.shape[1] if B_t.dim() == 3 else -1
+    if tuple(x_t.shape) != (batch, H, P) or tuple(delta_t.shape) != (batch, H) or tuple(A.shape) != (H,) \
+            or tuple(B_t.shape) != (batch, G, N) or C_t.shape != B_t.shape:
+        raise ValueError("inconsistent shapes")
+    if Dskip is not None and tuple(Dskip.shape) != (H,):
+        raise ValueError("Dskip must have shape (H,)")
+    if y_t is None:
+        y_t = torch.empty_like(x_t)
+    _shape(y_t, "y_t", x_t.shape)
+    io = _io_code(x_t, delta_t, B_t, C_t, y_t)
+    _one_device(state, x_t, delta_t, A, B_t, C_t, Dskip, y_t)
+    rc = lib.sscan_ssd_step(_dev(state, "state", torch.float32), _dev(x_t, "x_t"), _dev(delta_t, "delta_t"),
+                            _dev(A, "A", torch.float32), _dev(B_t, "B_t"), _dev(C_t, "C_t"),
+                            _dev(Dskip, "Dskip", torch.float32), _dev(y_t, "y_t"), batch, H, P, G, N, io,
+                            _stream(stream, state.device))
+    _check(rc)
+    return y_t

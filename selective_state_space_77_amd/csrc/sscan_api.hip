@@ -289,6 +289,39 @@ int sscan_ssd_forward(const void *x, const void *delta, const float *A, const vo
     return e == hipSuccess ? SSCAN_OK : fail_hip("ssd launch", e);
 }
 
+int sscan_ssd_step(float *state, const void *x_t, const void *delta_t, const float *A, const void *B_t,
+                   const void *C_t, const float *Dskip, void *y_t, int64_t batch, int64_t nheads,
+                   int64_t headdim, int64_t ngroups, int64_t dstate, int io_dtype, void *stream) {
+    g_last_error[0] = '\0';
+    if (io_dtype != SSCAN_F32 && io_dtype != SSCAN_BF16)
+        return fail(SSCAN_ERR_UNSUPPORTED, "io_dtype must be SSCAN_F32 or SSCAN_BF16");
+    if (headdim != sscan::kSsdHeadDim) return fail(SSCAN_ERR_UNSUPPORTED, "headdim must be 64");
+    if (dstate != 64 && dstate != 128) return fail(SSCAN_ERR_UNSUPPORTED, "dstate must be 64 or 128");
+    if (nheads < 1 || ngroups < 1 || nheads % ngroups != 0)
+        return fail(SSCAN_ERR_SHAPE, "nheads and ngroups must be positive, nheads a multiple of ngroups");
+    const int64_t es = io_dtype == SSCAN_BF16 ? 2 : 4;
+    int64_t bx, bd, bbc, bh, bs;
+    if (!nbytes(&bx, es, batch, nheads * headdim) || !nbytes(&bd, es, batch, nheads) ||
+        !nbytes(&bbc, es, batch, ngroups * dstate) || !nbytes(&bh, 4, nheads) ||
+        !nbytes(&bs, 4, batch, nheads, headdim * dstate))
+        return fail(SSCAN_ERR_SHAPE, "negative size or byte size overflows int64");
+    // one thread per 4 states: the grid's 256-thread blocks must stay below 2^31
+    if (bs / 16 / 256 >= 0x7FFFFFFF) return fail(SSCAN_ERR_SHAPE, "state too large for one launch");
+    const Span ins[] = {{x_t, bx, "x_t"}, {delta_t, bd, "delta_t"}, {A, bh, "A"}, {B_t, bbc, "B_t"},
+                        {C_t, bbc, "C_t"}, {Dskip, Dskip ? bh : 0, "Dskip"}};
+    const Span outs[] = {{state, bs, "state"}, {y_t, bx, "y_t"}};
+    const Span req[] = {ins[0], ins[1], ins[2], ins[3], ins[4], outs[0], outs[1]};
+    int rc = check_ptrs(req, 7);
+    if (rc) return rc;
+    rc = check_alias(outs, 2, ins, 6);
+    if (rc) return rc;
+    if (batch == 0) return SSCAN_OK;
+    sscan::SsdStepArgs a{state, x_t, delta_t, A, B_t, C_t, Dskip, y_t, batch, nheads, headdim, ngroups,
+                         int(dstate), io_dtype};
+    const hipError_t e = sscan::launch_ssd_step(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SSCAN_OK : fail_hip("ssd step launch", e);
+}
+
 static int step_impl(float *state, const void *x_t, const void *delta_t, const float *A,
                      const void *B_t, const void *C_t, const float *Dskip, void *y_t, int64_t batch,
                      int64_t dim, int64_t dstate, int io_dtype, void *stream, const FrontEnd &fe,

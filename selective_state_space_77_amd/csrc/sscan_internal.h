@@ -137,6 +137,20 @@ constexpr int kSsdHeadDim = 64;  // supported P
 
 hipError_t launch_ssd(const SsdArgs &a, hipStream_t s);
 
+// One decode step of the scalar-A-per-head scan, state updated in place.
+struct SsdStepArgs {
+    float *state;           // (batch, H, P, N)
+    const void *x, *delta;  // (batch, H, P), (batch, H)
+    const float *A;         // (H)
+    const void *B, *C;      // (batch, G, N)
+    const float *Dskip;     // (H) or NULL
+    void *y;                // (batch, H, P)
+    int64_t batch, H, P, G;
+    int N;
+    int io;
+};
+hipError_t launch_ssd_step(const SsdStepArgs &a, hipStream_t s);
+
 // Enqueue dst[i] = src ? src[i] : 0 for `count` floats (final_state at seqlen 0).
 hipError_t launch_copy_or_zero(float *dst, const float *src, int64_t count, hipStream_t s);
 

@@ -39,7 +39,8 @@ def _declared():
 def test_header_declares_the_entry_points():
     assert _declared() == ["sscan_backward", "sscan_forward", "sscan_forward_from_state",
                            "sscan_forward_fused", "sscan_last_error", "sscan_ssd_forward",
-                           "sscan_status_string", "sscan_step", "sscan_step_fused", "sscan_version"]
+                           "sscan_ssd_step", "sscan_status_string", "sscan_step", "sscan_step_fused",
+                           "sscan_version"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -202,6 +203,30 @@ def test_ssd_validation(lib):
     assert _ssd(lib, y=0x100010) == -4          # y overlaps x
     assert _ssd(lib, hs=0x300008) == -4         # final state overlaps A
     assert _ssd(lib, batch=0, x=None, d=None, B=None, C=None, y=None) == 0
+
+
+def _ssd_step(lib, **kw):
+    # batch 2, 4 heads of 64 channels, 2 groups, N = 64, bf16: x_t 1 KiB, state 128 KiB
+    a = dict(st=0x1000000, x=0x10000, d=0x20000, A=0x30000, B=0x40000, C=0x50000, D=None, y=0x60000,
+             batch=2, H=4, P=64, G=2, N=64, io=1)
+    a.update(kw)
+    return lib.sscan_ssd_step(a["st"], a["x"], a["d"], a["A"], a["B"], a["C"], a["D"], a["y"], a["batch"],
+                              a["H"], a["P"], a["G"], a["N"], a["io"], None)
+
+
+def test_ssd_step_validation(lib):
+    assert _ssd_step(lib, P=32) == -3
+    assert _ssd_step(lib, N=16) == -3
+    assert _ssd_step(lib, io=2) == -3
+    assert _ssd_step(lib, G=3) == -2             # heads not a multiple of groups
+    assert _ssd_step(lib, batch=-1) == -2
+    assert _ssd_step(lib, st=None) == -1
+    assert _ssd_step(lib, B=None) == -1
+    assert _ssd_step(lib, y=None) == -1
+    assert _ssd_step(lib, y=0x10100) == -4       # y_t overlaps x_t
+    assert _ssd_step(lib, st=0x40000) == -4      # state overlaps B_t
+    assert _ssd_step(lib, D=0x1000100) == -4     # Dskip inside the state
+    assert _ssd_step(lib, batch=0, st=None, x=None, d=None, B=None, C=None, y=None) == 0
 
 
 def _step(lib, **kw):
