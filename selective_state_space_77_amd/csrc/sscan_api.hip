@@ -305,8 +305,8 @@ int sscan_ssd_step(float *state, const void *x_t, const void *delta_t, const flo
         !nbytes(&bbc, es, batch, ngroups * dstate) || !nbytes(&bh, 4, nheads) ||
         !nbytes(&bs, 4, batch, nheads, headdim * dstate))
         return fail(SSCAN_ERR_SHAPE, "negative size or byte size overflows int64");
-    // one thread per 4 states: the grid's 256-thread blocks must stay below 2^31
-    if (bs / 16 / 256 >= 0x7FFFFFFF) return fail(SSCAN_ERR_SHAPE, "state too large for one launch");
+    // one thread per 8 states (32 bytes): the grid's 256-thread blocks must stay below 2^31
+    if (bs / 32 / 256 >= 0x7FFFFFFF) return fail(SSCAN_ERR_SHAPE, "state too large for one launch");
     const Span ins[] = {{x_t, bx, "x_t"}, {delta_t, bd, "delta_t"}, {A, bh, "A"}, {B_t, bbc, "B_t"},
                         {C_t, bbc, "C_t"}, {Dskip, Dskip ? bh : 0, "Dskip"}};
     const Span outs[] = {{state, bs, "state"}, {y_t, bx, "y_t"}};
