@@ -37,7 +37,7 @@ if ROOT not in sys.path:
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 # fp32 VALU without packed-FP32 forms: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz
 # lane-ops/s; an FMA counts 2 flops -> 78.6 TFLOP/s (the published 157.3
-# TFLOP/s fp32-vector figure needs the packed forms, which this build never emits).
+# TFLOP/s fp32-vector figure needs the packed forms, which this library never emits).
 PEAK_VALU_TFLOPS = 78.6
 FLOPS_PER_UPDATE = 8           # per (b,t,d,n): 4 FMA: w - k, the state update, the 1 - Abar recurrence, the readout
 # backward, per (b,t,d,n): the recomputed forward update (8) plus the adjoint and
@@ -467,8 +467,8 @@ def main() -> int:
                     help="also run a 1 GiB device copy (HBM-counter calibration under rocprofv3)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the scan runs on a single MI355X and this build "
-              "has no multi-GPU path (see the sharding note in DESIGN.md).", file=sys.stderr)
+        print("bench.py measures one GPU only: the scan runs on a single MI355X and the library "
+              "has no multi-GPU path.", file=sys.stderr)
         return 2
 
     import torch
