@@ -238,8 +238,9 @@ __global__ __launch_bounds__(kWave) void k_seg(
         fe_prefix<IO>(x, fe, b, L, dim, d, t0, p3, p2, p1);
     }
 
-    // one token: structured-real update on the scaled state, or the general one
-    auto token = [&](int tau, float xv, float dv, const float *row) {
+    // one token: structured-real update on the scaled state, or the general one;
+    // sto is the token's output offset in the row stream
+    auto token = [&](float xv, float dv, const float *row, uint32_t sto) {
         float yacc = 0.f;
         if constexpr (kFast) {
             const float r = exp2_hw(dv * a2);
@@ -258,7 +259,7 @@ __global__ __launch_bounds__(kWave) void k_seg(
         }
         if (kMain) {
             const float yv = kFast ? fmaf(yacc, inv_alpha, dsk * xv) : fmaf(dsk, xv, yacc);
-            if (active) IO::bst(IO::enc(yv), ry, voff, uint32_t(tau) * rowb);
+            if (active) IO::bst(IO::enc(yv), ry, voff, sto);
         } else {
             dsum += dv;
         }
@@ -284,10 +285,15 @@ __global__ __launch_bounds__(kWave) void k_seg(
                 dv[u] = IO::cvt(dr[u]);
             }
         }
+        // token offsets formed here, one add per token, rather than kept live
+        // across the loop as a set of scalar registers
+        uint32_t sl = uint32_t(g0 + U) * rowb, sto = uint32_t(g0) * rowb;
+        asm volatile("" : "+s"(sl), "+s"(sto));
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            xr[u] = IO::bld(rx, voff, uint32_t(g0 + U + u) * rowb);
-            dr[u] = IO::bld(rd, voff, uint32_t(g0 + U + u) * rowb);
+            xr[u] = IO::bld(rx, voff, sl);
+            dr[u] = IO::bld(rd, voff, sl);
+            sl += rowb;
         }
 #pragma unroll
         for (int u = 0; u < U; u += 2) {
@@ -300,7 +306,8 @@ __global__ __launch_bounds__(kWave) void k_seg(
                 for (int i = 0; i < 2 * NT; ++i) rowB[i] = rn[i];
             }
             __builtin_amdgcn_sched_barrier(0);
-            token(tau, xv[u], dv[u], rowA);
+            token(xv[u], dv[u], rowA, sto);
+            sto += rowb;
             __builtin_amdgcn_sched_barrier(0);
             wait_scalar_loads();
             {
@@ -309,7 +316,8 @@ __global__ __launch_bounds__(kWave) void k_seg(
                 for (int i = 0; i < 2 * NT; ++i) rowA[i] = rn[i];
             }
             __builtin_amdgcn_sched_barrier(0);
-            token(tau + 1, xv[u + 1], dv[u + 1], rowB);
+            token(xv[u + 1], dv[u + 1], rowB, sto);
+            sto += rowb;
         }
     }
 #pragma unroll
@@ -479,10 +487,15 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
             // prefetch the next group of this wave's stream: the rest of this run,
             // then the start of its run in the next chunk
             const uint32_t nxt = (g + 1 < TS / U) ? uint32_t((g + 1) * U) : uint32_t(CH);
+            // the token offsets are formed here, one add per token, rather than
+            // hoisted out of the chunk loop as 16 live scalar registers
+            uint32_t so = nxt * rowb;
+            asm volatile("" : "+s"(so));
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                xr[u] = IO::bld(rx, voff, (nxt + u) * rowb);
-                dr[u] = IO::bld(rd, voff, (nxt + u) * rowb);
+                xr[u] = IO::bld(rx, voff, so);
+                dr[u] = IO::bld(rd, voff, so);
+                so += rowb;
             }
             if constexpr (FE) {
                 if (g + 1 == TS / U) {
@@ -515,8 +528,13 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
         }
         if (w == 0 && active) {
             // run 0 started from the carried state: its outputs are final
+            uint32_t sto = 0;
+            asm volatile("" : "+s"(sto));
 #pragma unroll
-            for (int tau = 0; tau < TS; ++tau) IO::bst(IO::enc(yl[tau]), ry, voff, uint32_t(tau) * rowb);
+            for (int tau = 0; tau < TS; ++tau) {
+                IO::bst(IO::enc(yl[tau]), ry, voff, sto);
+                sto += rowb;
+            }
         }
         s_sum[w][lane] = dsum;
 #pragma unroll
@@ -543,14 +561,16 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
             float cA[NT], cB[NT];
 #pragma unroll
             for (int n = 0; n < NT; ++n) cA[n] = bc0[NT + n];
-            auto fix = [&](int tau, const float *crow) {
+            auto fix = [&](int tau, const float *crow, uint32_t sto) {
                 const float rr = rho[tau];
                 float acc = crow[NT - 1] * kin[NT - 1];
 #pragma unroll
                 for (int n = NT - 2; n >= 0; --n) acc = fmaf(acc, rr, crow[n] * kin[n]);
                 acc *= rr;
-                if (active) IO::bst(IO::enc(fmaf(acc, inv_alpha, yl[tau])), ry, voff, uint32_t(tau) * rowb);
+                if (active) IO::bst(IO::enc(fmaf(acc, inv_alpha, yl[tau])), ry, voff, sto);
             };
+            uint32_t sto = 0;
+            asm volatile("" : "+s"(sto));
 #pragma unroll
             for (int tau = 0; tau < TS; tau += 2) {
                 __builtin_amdgcn_sched_barrier(0);
@@ -561,7 +581,8 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
                     for (int n = 0; n < NT; ++n) cB[n] = rn[n];
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                fix(tau, cA);
+                fix(tau, cA, sto);
+                sto += rowb;
                 __builtin_amdgcn_sched_barrier(0);
                 wait_scalar_loads();
                 {
@@ -570,7 +591,8 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
                     for (int n = 0; n < NT; ++n) cA[n] = rn[n];
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                fix(tau + 1, cB);
+                fix(tau + 1, cB, sto);
+                sto += rowb;
             }
         }
     }
