@@ -445,7 +445,9 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
         // range check, which leaves the state exactly unchanged (r = 1, w = 0),
         // and their stores fall outside the range and are dropped.  Only the
         // B/C row index is clamped.
-        const int last = max(nv - 1, 0);
+        // uniform: kept in a scalar register, so the per-token B/C row offsets
+        // below are scalar arithmetic (no per-token move from a vector register)
+        const int last = __builtin_amdgcn_readfirstlane(max(nv - 1, 0));
         // B/(n+1) and C rows of two consecutive tokens (ping-pong): the scalar
         // loads of token tau+1 are issued, after waiting for those of tau,
         // before tau computes, so they have a whole token to arrive.
