@@ -368,6 +368,7 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
     __shared__ float s_sum[W][kWave];
     __shared__ float s_k[W][NT][kWave];
     __shared__ float s_pre[W][NT][kWave];  // [0]: chunk carry-out; [j]: state entering run j
+    __shared__ float s_zero[NT][kWave];    // the (zero) state runs 1.. start from
 
     const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
     const int lane = int(threadIdx.x) % kWave;
@@ -402,9 +403,20 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
             dr[u] = IO::bld(rd, voff, uint32_t(u) * rowb);
         }
     }
-    float k[NT];  // wave 0 enters chunk 0 with the state before token 0 (scaled)
+    // Every run starts from a state read from LDS: run 0 from s_pre[0] (the state
+    // before token 0 for the first chunk, the carry-out of the previous chunk
+    // after it), the others from zeros.  One code path for every wave, so the
+    // reads land in the state registers without copies.
+    if (w == 0) {
 #pragma unroll
-    for (int n = 0; n < NT; ++n) k[n] = (w == 0 && h0 && n < N) ? h0[(b * dim + d) * N + n] * alpha : 0.f;
+        for (int n = 0; n < NT; ++n) s_pre[0][n][lane] = (h0 && n < N) ? h0[(b * dim + d) * N + n] * alpha : 0.f;
+    } else if (w == 1) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n) s_zero[n][lane] = 0.f;
+    }
+    __syncthreads();
+    const float(*kstart)[kWave] = w == 0 ? s_pre[0] : s_zero;
+    float k[NT];
     // front end: per-lane coefficients; the convolution window (raw inputs of
     // the 3 tokens before the current one) starts from the tokens before this
     // wave's first run, and the 3 tokens before its next run are prefetched with
@@ -422,15 +434,8 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
         const int nv = int(max<int64_t>(0, min<int64_t>(TS, L - t0)));
         const rsrc_t rx = rsrc_at(x, t0), rd = rsrc_at(delta, t0), ry = rsrc_at(y, t0);
         const float *bc0 = bcrow + min(t0, L - 1) * (2 * NT);
-        if (w == 0) {
-            if (c > 0) {
 #pragma unroll
-                for (int n = 0; n < NT; ++n) k[n] = s_pre[0][n][lane];
-            }
-        } else {
-#pragma unroll
-            for (int n = 0; n < NT; ++n) k[n] = 0.f;
-        }
+        for (int n = 0; n < NT; ++n) k[n] = kstart[n][lane];
         if constexpr (FE) {
             if (c > 0) {
                 p3 = IO::cvt(pr[0]);
