@@ -836,11 +836,6 @@ void prep_io(const void *B, const void *C, const float *A, float *bc, int *flags
     }
 }
 
-// Lockstep workgroup of the fused (front-end) variant: 8 waves, so each lane may
-// hold 256 VGPRs -- room for the convolution window and coefficients without
-// spilling.
-constexpr int kLockWFe = 8;
-
 template <class IO, int NT, bool FE>
 hipError_t forward_t(const FwdArgs &a, const FwdPlan &p, void *ws, hipStream_t s) {
     using T = typename IO::T;
@@ -862,8 +857,9 @@ hipError_t forward_t(const FwdArgs &a, const FwdPlan &p, void *ws, hipStream_t s
     SSCAN_SEG(true, false, seg_main);
     // structured-real tiles
     if (p.lockstep) {
-        constexpr int LW = FE ? kLockWFe : kLockW;
-        hipLaunchKernelGGL((k_lockstep<IO, NT, LW, kLockT, FE>), dim3(unsigned(p.tiles)), dim3(LW * kWave),
+        // the fused variant too: with the token loop free of register copies it fits
+        // 128 VGPRs (4 waves per SIMD) without spilling
+        hipLaunchKernelGGL((k_lockstep<IO, NT, kLockW, kLockT, FE>), dim3(unsigned(p.tiles)), dim3(kLockW * kWave),
                            0, s, x, dl, a.A, bc, a.Dskip, a.h0, y, a.final_state, flags, a.L, a.dim, a.N,
                            p.tiles_per_batch, a.fe);
     } else {
