@@ -383,7 +383,7 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
     const float alpha = -a0, inv_alpha = 1.f / alpha, a2 = a0 * kLog2e;
     const float dsk = Dskip ? Dskip[d] : 0.f;
     const float *bcrow = bc + (b * L) * (2 * NT);
-    const int64_t nchunks = (L + CH - 1) / CH;
+    const int nchunks = int((L + CH - 1) / CH);  // below 2^31 (launch condition)
     // per-lane byte offset inside a token row; per-token row stride (uniform)
     const uint32_t voff = uint32_t((dbase + lane) * ES);
     const uint32_t rowb = uint32_t(dim * ES);
@@ -429,8 +429,8 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
         fe_prefix<IO>(x, fe, b, L, dim, d, int64_t(w) * TS, p3, p2, p1);
     }
 
-    for (int64_t c = 0; c < nchunks; ++c) {
-        const int64_t t0 = c * CH + int64_t(w) * TS;
+    for (int c = 0; c < nchunks; ++c) {
+        const int64_t t0 = int64_t(c) * CH + int64_t(w) * TS;
         const int nv = int(max<int64_t>(0, min<int64_t>(TS, L - t0)));
         const rsrc_t rx = rsrc_at(x, t0), rd = rsrc_at(delta, t0), ry = rsrc_at(y, t0);
         const float *bc0 = bcrow + min(t0, L - 1) * (2 * NT);
@@ -578,12 +578,19 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
             };
             uint32_t sto = 0;
             asm volatile("" : "+s"(sto));
+            // an opaque copy of the run's last index: the C row addresses are formed
+            // again here (scalar arithmetic) instead of being kept from the token
+            // loop across the barriers, where they would not fit in scalar registers
+            // (with the front end, whose scalar registers are fuller, keeping them
+            // measured no slower)
+            int lastf = last;
+            if constexpr (!FE) asm volatile("" : "+s"(lastf));
 #pragma unroll
             for (int tau = 0; tau < TS; tau += 2) {
                 __builtin_amdgcn_sched_barrier(0);
                 wait_scalar_loads();
                 {
-                    const float *rn = bc0 + min(tau + 1, last) * (2 * NT) + NT;
+                    const float *rn = bc0 + min(tau + 1, lastf) * (2 * NT) + NT;
 #pragma unroll
                     for (int n = 0; n < NT; ++n) cB[n] = rn[n];
                 }
@@ -593,7 +600,7 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
                 __builtin_amdgcn_sched_barrier(0);
                 wait_scalar_loads();
                 {
-                    const float *rn = bc0 + min(tau + 2, last) * (2 * NT) + NT;
+                    const float *rn = bc0 + min(tau + 2, lastf) * (2 * NT) + NT;
 #pragma unroll
                     for (int n = 0; n < NT; ++n) cA[n] = rn[n];
                 }
@@ -710,7 +717,7 @@ __device__ __forceinline__ float step_lane(int q, int N, float dt, float xv, flo
 // With the front end (FE), x and delta are the raw token inputs: the step
 // reads the K-1 carried raw inputs of its channel from conv_state, forms the
 // convolution and softplus, and shifts conv_state by one token in place.
-template <class IO, int NT, int SPL, bool kVec, bool FE>
+template <class IO, int NT, int SPL, bool kVec, bool FE, int BT>
 __global__ __launch_bounds__(256) void k_step(float *__restrict__ state,
                                               const typename IO::T *__restrict__ x,
                                               const typename IO::T *__restrict__ delta,
@@ -723,22 +730,38 @@ __global__ __launch_bounds__(256) void k_step(float *__restrict__ state,
                                               typename IO::T *__restrict__ conv_state) {
     using T = typename IO::T;
     constexpr int LPC = NT / SPL;
+    static_assert(!FE || BT == 1, "the front-end step takes one batch row per thread");
+    // thread -> (group of BT batch rows, channel d, lane q of the channel); the
+    // BT rows of a thread share the A row, Dskip and the channel's constants
     const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    const int64_t chans = batch * dim;
-    const int64_t c0 = i / LPC;
-    const int q = int(i - c0 * LPC);
-    const bool active = c0 < chans;
-    const int64_t c = active ? c0 : chans - 1;
-    const int64_t b = c / dim;
-    const int64_t d = c - b * dim;
-    float xv = IO::ld(x, c);
-    float dt = IO::ld(delta, c);
+    const int64_t units = (batch + BT - 1) / BT * dim;
+    const int64_t u0 = i / LPC;
+    const int q = int(i - u0 * LPC);
+    const bool active = u0 < units;
+    const int64_t u = active ? u0 : units - 1;
+    const int64_t bg = u / dim;
+    const int64_t d = u - bg * dim;
+    int64_t c[BT];
+    bool live[BT];
+#pragma unroll
+    for (int j = 0; j < BT; ++j) {
+        const int64_t b = bg * BT + j;
+        live[j] = active && b < batch;
+        c[j] = (b < batch ? b : batch - 1) * dim + d;
+    }
+    float xv[BT], dt[BT];
+#pragma unroll
+    for (int j = 0; j < BT; ++j) {
+        xv[j] = IO::ld(x, c[j]);
+        dt[j] = IO::ld(delta, c[j]);
+    }
     // every load goes out at the start (a load issued after the readout would add a
     // second memory round trip to each wave's lifetime)
     const float dsk = Dskip ? Dskip[d] : 0.f;
     if constexpr (FE) {
         // carried raw inputs of this channel: row r of conv_state is the token
         // K-1-r before this one
+        const int64_t b = c[0] / dim;
         const int rows = fe.K - 1;
         T cr[kMaxConv - 1];
 #pragma unroll
@@ -749,9 +772,9 @@ __global__ __launch_bounds__(256) void k_step(float *__restrict__ state,
         };
         FeLane fl;
         fl.init(fe, d);
-        const T xraw = x[c];
-        xv = fl.u(back(3), back(2), back(1), xv);
-        dt = fl.delta(dt);
+        const T xraw = x[c[0]];
+        xv[0] = fl.u(back(3), back(2), back(1), xv[0]);
+        dt[0] = fl.delta(dt[0]);
         if (active && q == 0) {
 #pragma unroll
             for (int r = 0; r < kMaxConv - 1; ++r)
@@ -759,54 +782,66 @@ __global__ __launch_bounds__(256) void k_step(float *__restrict__ state,
         }
     }
 
-    float h[SPL], av[SPL], bv[SPL], cv[SPL];
-    float *sp = state + c * N + q * SPL;
+    float h[BT][SPL], av[SPL], bv[BT][SPL], cv[BT][SPL];
     if constexpr (kVec) {
         // N == NT (a multiple of 4), 16-byte aligned state and A, B and C rows
         // aligned to 4 elements: vector accesses
 #pragma unroll
-        for (int j = 0; j < SPL; j += 4) {
-            const float4 v = *reinterpret_cast<const float4 *>(sp + j);
-            h[j] = v.x; h[j + 1] = v.y; h[j + 2] = v.z; h[j + 3] = v.w;
-        }
+        for (int j = 0; j < BT; ++j) ldrow<SPL>(state + c[j] * N + q * SPL, h[j]);
+        ldrow<SPL>(A + d * N + q * SPL, av);
 #pragma unroll
-        for (int j = 0; j < SPL; j += 4) {
-            const float4 va = *reinterpret_cast<const float4 *>(A + d * N + q * SPL + j);
-            av[j] = va.x; av[j + 1] = va.y; av[j + 2] = va.z; av[j + 3] = va.w;
+        for (int j = 0; j < BT; ++j) {
+            const int64_t b = c[j] / dim;
+            ldrow<SPL>(B + b * N + q * SPL, bv[j]);
+            ldrow<SPL>(C + b * N + q * SPL, cv[j]);
         }
-        ldrow<SPL>(B + b * N + q * SPL, bv);
-        ldrow<SPL>(C + b * N + q * SPL, cv);
     } else {
 #pragma unroll
-        for (int j = 0; j < SPL; ++j) {
-            const int n = q * SPL + j;
-            const bool ok = n < N;
-            h[j] = ok ? sp[j] : 0.f;
-            av[j] = ok ? A[d * N + n] : 0.f;
-            bv[j] = ok ? IO::ld(B, b * N + n) : 0.f;
-            cv[j] = ok ? IO::ld(C, b * N + n) : 0.f;
+        for (int k = 0; k < SPL; ++k) {
+            const int n = q * SPL + k;
+            av[k] = n < N ? A[d * N + n] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < BT; ++j) {
+            const int64_t b = c[j] / dim;
+            const float *sp = state + c[j] * N + q * SPL;
+#pragma unroll
+            for (int k = 0; k < SPL; ++k) {
+                const int n = q * SPL + k;
+                const bool ok = n < N;
+                h[j][k] = ok ? sp[k] : 0.f;
+                bv[j][k] = ok ? IO::ld(B, b * N + n) : 0.f;
+                cv[j][k] = ok ? IO::ld(C, b * N + n) : 0.f;
+            }
         }
     }
     const float a0 = A[d * N];
-    float yacc = step_lane<SPL, LPC>(q, N, dt, xv, a0, av, bv, cv, h);
 #pragma unroll
-    for (int off = LPC / 2; off >= 1; off /= 2) yacc += __shfl_xor(yacc, off, LPC);
-    if (!active) return;
-    if constexpr (kVec) {
+    for (int j = 0; j < BT; ++j) {
+        float yacc = step_lane<SPL, LPC>(q, N, dt[j], xv[j], a0, av, bv[j], cv[j], h[j]);
 #pragma unroll
-        for (int j = 0; j < SPL; j += 4)
-            *reinterpret_cast<float4 *>(sp + j) = make_float4(h[j], h[j + 1], h[j + 2], h[j + 3]);
-    } else {
+        for (int off = LPC / 2; off >= 1; off /= 2) yacc += __shfl_xor(yacc, off, LPC);
+        if (!live[j]) continue;
+        float *sp = state + c[j] * N + q * SPL;
+        if constexpr (kVec) {
 #pragma unroll
-        for (int j = 0; j < SPL; ++j)
-            if (q * SPL + j < N) sp[j] = h[j];
+            for (int k = 0; k < SPL; k += 4)
+                *reinterpret_cast<float4 *>(sp + k) = make_float4(h[j][k], h[j][k + 1], h[j][k + 2], h[j][k + 3]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < SPL; ++k)
+                if (q * SPL + k < N) sp[k] = h[j][k];
+        }
+        if (q == 0) y[c[j]] = IO::enc(fmaf(dsk, xv[j], yacc));
     }
-    if (q == 0) y[c] = IO::enc(fmaf(dsk, xv, yacc));
 }
 
 
 // states per lane of the decode step (N above it: several lanes per channel)
 constexpr int kStepSpl = 8;
+// batch rows per thread of the decode step without the front end (they share the
+// channel's A row and Dskip, and a wave keeps that many rows of state in flight)
+constexpr int kStepBt = 4;
 
 int round_nt(int64_t N) { return N <= 1 ? 1 : N <= 2 ? 2 : N <= 4 ? 4 : N <= 8 ? 8 : 16; }
 
@@ -890,7 +925,8 @@ hipError_t step_t(const StepArgs &a, hipStream_t s) {
     using T = typename IO::T;
     constexpr int SPL = NT < kStepSpl ? NT : kStepSpl;
     constexpr int LPC = NT / SPL;
-    const int64_t threads = a.batch * a.dim * LPC;
+    constexpr int BT = FE ? 1 : kStepBt;
+    const int64_t threads = (a.batch + BT - 1) / BT * a.dim * LPC;
     const dim3 grid(unsigned((threads + 255) / 256));
     const uintptr_t rb = (sizeof(T) == 2 && SPL % 8 == 0 ? 8 : 4) * sizeof(T);  // one B or C load
     const bool vec = (SPL % 4 == 0) && (a.N == NT) && (reinterpret_cast<uintptr_t>(a.state) % 16 == 0) &&
@@ -898,13 +934,13 @@ hipError_t step_t(const StepArgs &a, hipStream_t s) {
                      (reinterpret_cast<uintptr_t>(a.C) % rb == 0);
     if (vec) {
         if constexpr (SPL % 4 == 0)
-            hipLaunchKernelGGL((k_step<IO, NT, SPL, true, FE>), grid, dim3(256), 0, s, a.state,
+            hipLaunchKernelGGL((k_step<IO, NT, SPL, true, FE, BT>), grid, dim3(256), 0, s, a.state,
                                static_cast<const T *>(a.x), static_cast<const T *>(a.delta), a.A,
                                static_cast<const T *>(a.B), static_cast<const T *>(a.C), a.Dskip,
                                static_cast<T *>(a.y), a.batch, a.dim, a.N, a.fe,
                                static_cast<T *>(a.conv_state));
     } else {
-        hipLaunchKernelGGL((k_step<IO, NT, SPL, false, FE>), grid, dim3(256), 0, s, a.state,
+        hipLaunchKernelGGL((k_step<IO, NT, SPL, false, FE, BT>), grid, dim3(256), 0, s, a.state,
                            static_cast<const T *>(a.x), static_cast<const T *>(a.delta), a.A,
                            static_cast<const T *>(a.B), static_cast<const T *>(a.C), a.Dskip,
                            static_cast<T *>(a.y), a.batch, a.dim, a.N, a.fe,
@@ -943,7 +979,8 @@ FwdPlan plan_forward(int64_t batch, int64_t L, int64_t dim, int64_t N) {
     // Lockstep kernel when the tiles alone give at least one wave per SIMD.
     // (its buffer offsets reach (W*TS + 8) rows past a run start: keep them 32-bit)
     p.lockstep = p.tiles >= kLockMinTiles &&
-                 (int64_t(kLockW) * kLockT + kUnroll) * dim * 4 < (int64_t(1) << 31);
+                 (int64_t(kLockW) * kLockT + kUnroll) * dim * 4 < (int64_t(1) << 31) &&
+                 L / (int64_t(kLockW) * kLockT) < (int64_t(1) << 30);  // chunk count in 32 bits
     size_t off = 0;
     p.off_bc = off;
     off += align256(size_t(batch) * L * 2 * p.nt * sizeof(float));
