@@ -281,7 +281,8 @@ def bench_fused(wl, args, dev) -> int:
                    "io_dtype": wl.io, "a_init": wl.a_init},
         "roofline": {"kernel": "k_lockstep<.., FE> (timed: the whole sscan_forward_fused call)",
                      "bound": "alu", "achieved": round(tflops, 3), "peak": PEAK_VALU_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_VALU_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_VALU_TFLOPS, 4),
+                     "traffic": recorded_traffic(f"k_lockstep_fused_{wl.name}_hbm_counters.md", FWD_SOURCES),
                      "per_launch": {"updates": updates, "flops": flops, "algorithmic_bytes": nbytes,
                                     "event_avg_us": round(ev_avg * 1e6, 2),
                                     "event_min_us": round(ev_min * 1e6, 2)},
@@ -393,7 +394,7 @@ def bench_step(wl, args, dev) -> int:
                    "io_dtype": wl.io},
         "roofline": {"kernel": "k_step", "bound": "hbm", "achieved": round(gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                     "traffic": None,
+                     "traffic": recorded_traffic(f"k_step_{wl.name}_hbm_counters.md", FWD_SOURCES),
                      "per_launch": {"algorithmic_bytes": nbytes, "event_avg_us": round(ev_avg * 1e6, 2)}},
         "cpu_baseline": None}), flush=True)
     return 0
@@ -449,7 +450,7 @@ def bench_ssd_step(wl, args, dev) -> int:
                    "ngroups": wl.ngroups, "dstate": wl.dstate, "io_dtype": wl.io},
         "roofline": {"kernel": "k_ssd_step", "bound": "hbm", "achieved": round(gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                     "traffic": None,
+                     "traffic": recorded_traffic(f"k_ssd_step_{wl.name}_hbm_counters.md", SSD_SOURCES),
                      "per_launch": {"algorithmic_bytes": nbytes, "event_avg_us": round(ev_avg * 1e6, 2)}},
         "cpu_baseline": None}), flush=True)
     return 0
