@@ -453,6 +453,8 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
         // uniform: kept in a scalar register, so the per-token B/C row offsets
         // below are scalar arithmetic (no per-token move from a vector register)
         const int last = __builtin_amdgcn_readfirstlane(max(nv - 1, 0));
+        int nvs = nv;  // the valid-token count as an opaque 32-bit scalar
+        if constexpr (FE) asm volatile("" : "+s"(nvs));
         // B/(n+1) and C rows of two consecutive tokens (ping-pong): the scalar
         // loads of token tau+1 are issued, after waiting for those of tau,
         // before tau computes, so they have a whole token to arrive.
@@ -476,15 +478,20 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
             for (int u = 0; u < U; ++u) {
                 if constexpr (FE) {
                     // tokens past the end are not neutral after the front end
-                    // (softplus(bias) > 0): they are zeroed explicitly
-                    // (a 0/1 factor rather than a select, so nothing is branched around)
+                    // (softplus(bias) > 0): their step size is zeroed (a 0/1 factor
+                    // rather than a select, so nothing is branched around), which
+                    // leaves the state exactly unchanged (r = 1, 1 - r^(n+1) = 0)
+                    // whatever their input; their outputs are not stored.  The
+                    // factor is chosen on the scalar unit from a 32-bit count.
                     const float xr0 = IO::cvt(xr[u]);
-                    const float vm = g * U + u < nv ? 1.f : 0.f;
+                    int vmb = g * U + u < nvs ? 0x3f800000 : 0;  // 1.0f or 0.0f
+                    asm volatile("" : "+s"(vmb));
+                    const float vm = __int_as_float(vmb);
                     const float uu = fl.u(p3, p2, p1, xr0);
                     p3 = p2;
                     p2 = p1;
                     p1 = xr0;
-                    xv[u] = uu * vm;
+                    xv[u] = uu;
                     dv[u] = fl.delta(IO::cvt(dr[u])) * vm;
                 } else {
                     xv[u] = IO::cvt(xr[u]);
