@@ -126,6 +126,15 @@ def test_steps_structured_A(N, io):
                                     mode="step"), N, io)
 
 
+@pytest.mark.parametrize("batch,io", [(5, "bf16"), (7, "f32"), (1, "bf16")])
+def test_steps_batch_rows_not_a_multiple_of_four(batch, io):
+    """A thread takes four batch rows of one channel: groups with one to three rows past
+    the end (their loads clamped, nothing stored), at the benchmarked channel width."""
+    announce(f"step batch={batch} io={io} (partial row groups)")
+    _steps_vs_oracle(datagen.custom(f"stepbt{batch}{io}", batch, 6, 5120, 16, io, "s4d_real",
+                                    key=70 + batch, mode="step"), 16, io)
+
+
 def test_steps_mixed_A_rows():
     """Structured rows beside general ones, a row structured only in its first eight
     states (its lanes take different updates), A = 0, A > 0 and a tiny A row."""
