@@ -62,7 +62,8 @@ typedef enum {
     SSCAN_OK = 0,
     SSCAN_ERR_NULL = -1,        /* a required pointer is NULL (its tensor is non-empty) */
     SSCAN_ERR_SHAPE = -2,       /* a size is negative, or a byte size overflows int64   */
-    SSCAN_ERR_UNSUPPORTED = -3, /* dstate outside 1..SSCAN_MAX_DSTATE, or bad io_dtype   */
+    SSCAN_ERR_UNSUPPORTED = -3, /* dstate outside 1..SSCAN_MAX_DSTATE, bad io_dtype, or a
+                                   shape beyond a launch limit (see sscan_forward_plan) */
     SSCAN_ERR_ALIAS = -4,       /* an output overlaps an input or another output         */
     SSCAN_ERR_HIP = -5          /* a HIP call (allocation, launch) failed; see last error */
 } sscan_status;
@@ -273,6 +274,38 @@ int sscan_ssd_forward(const void *x, const void *delta, const float *A, const vo
 int sscan_ssd_step(float *state, const void *x_t, const void *delta_t, const float *A, const void *B_t,
                    const void *C_t, const float *Dskip, void *y_t, int64_t batch, int64_t nheads,
                    int64_t headdim, int64_t ngroups, int64_t dstate, int io_dtype, void *stream);
+
+/*
+ * How sscan_forward (and the _from_state and _fused variants) would split a
+ * problem of this shape, computed on the host without touching the GPU: which
+ * kernel scans the structured-real tiles, how the sequence is cut, and the device
+ * scratch the call allocates.  This makes the chosen path visible to the caller
+ * (the pages warn that a benchmark is only meaningful once it is confirmed that
+ * the fused kernel is the one running: "Mamba and State Space Models", failure
+ * modes).
+ *
+ * Launch limits, checked here and by every forward call (SSCAN_ERR_UNSUPPORTED
+ * beyond them): the kernels address x, delta and y through buffer descriptors
+ * with 32-bit offsets, so one token row (dim * element size) may be at most 2^27
+ * bytes, and the segment kernels cut the sequence so that a segment's rows span
+ * below 2^31 bytes; a launch has fewer than 2^32 work items.
+ *
+ *   batch, seqlen, dim, dstate, io_dtype  as for sscan_forward.
+ *   out          [out] the plan (host memory, caller-owned).
+ * Returns SSCAN_OK, or a negative sscan_status with *out zeroed.
+ */
+#define SSCAN_PLAN_LOCKSTEP 1 /* one workgroup per 64-channel tile over the whole sequence */
+#define SSCAN_PLAN_SEGMENT 2  /* one wave per (64-channel tile, time segment), two passes   */
+typedef struct {
+    int32_t kernel;        /* SSCAN_PLAN_LOCKSTEP or SSCAN_PLAN_SEGMENT                    */
+    int32_t segments;      /* time segments per tile of the segment kernels (which also    */
+    int64_t seg_len;       /* take general-A tiles); tokens per segment, the last shorter  */
+    int64_t tiles;         /* batch * ceil(dim / 64)                                       */
+    int64_t chunk_tokens;  /* lockstep: tokens per chunk (waves x run length); else 0      */
+    int64_t scratch_bytes; /* device scratch one call allocates (stream-ordered)           */
+} sscan_plan_info;
+int sscan_forward_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                       sscan_plan_info *out);
 
 /* Static text for a status code (never NULL). */
 const char *sscan_status_string(int status);

@@ -47,6 +47,16 @@ class SScanError(RuntimeError):
         self.status = status
 
 
+class PlanInfo(ctypes.Structure):
+    """sscan_plan_info of include/sscan.h."""
+    _fields_ = [("kernel", ctypes.c_int32), ("segments", ctypes.c_int32), ("seg_len", ctypes.c_int64),
+                ("tiles", ctypes.c_int64), ("chunk_tokens", ctypes.c_int64),
+                ("scratch_bytes", ctypes.c_int64)]
+
+
+PLAN_KERNEL = {1: "lockstep", 2: "segment"}
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
@@ -75,6 +85,8 @@ def _load() -> ctypes.CDLL:
     lib.sscan_ssd_step.restype = ctypes.c_int
     lib.sscan_step.argtypes = [fp, vp, vp, fp, vp, vp, fp, vp, i64, i64, i64, ctypes.c_int, vp]
     lib.sscan_step.restype = ctypes.c_int
+    lib.sscan_forward_plan.argtypes = [i64, i64, i64, i64, ci, ctypes.POINTER(PlanInfo)]
+    lib.sscan_forward_plan.restype = ctypes.c_int
     lib.sscan_status_string.argtypes = [ctypes.c_int]
     lib.sscan_status_string.restype = ctypes.c_char_p
     lib.sscan_last_error.argtypes = []
@@ -91,6 +103,18 @@ def _check(rc: int) -> None:
     if rc != 0:
         detail = lib.sscan_last_error().decode() or lib.sscan_status_string(rc).decode()
         raise SScanError(rc, detail)
+
+
+def forward_plan(batch: int, seqlen: int, dim: int, dstate: int, io_dtype) -> dict:
+    """How sscan_forward would split a problem of this shape (host only, no GPU work):
+    kernel ("lockstep" or "segment"), segments, seg_len, tiles, chunk_tokens, scratch_bytes.
+    io_dtype: torch.float32 / torch.bfloat16 or "f32" / "bf16"."""
+    io = {torch.float32: F32, torch.bfloat16: BF16, "f32": F32, "bf16": BF16}[io_dtype]
+    info = PlanInfo()
+    _check(lib.sscan_forward_plan(batch, seqlen, dim, dstate, io, ctypes.byref(info)))
+    out = {f: getattr(info, f) for f, _ in PlanInfo._fields_}
+    out["kernel"] = PLAN_KERNEL[out["kernel"]]
+    return out
 
 
 def _io_code(*ts: torch.Tensor) -> int:

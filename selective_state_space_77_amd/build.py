@@ -1,8 +1,13 @@
-"""Build libsscan.so in-tree with hipcc for gfx950 (no JIT, no torch extension)."""
+"""Build libsscan.so in-tree with hipcc for gfx950 (no JIT, no torch extension).
+
+Each translation unit is compiled to an object in a temporary directory, in
+parallel, and the objects are linked into the shared library."""
 from __future__ import annotations
 
 import os
 import subprocess
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -12,7 +17,7 @@ ARCH = "gfx950"
 
 # Packed-FP32 VALU forms are kept out of the generated code; the host pass warns
 # that it does not know the target feature, which is harmless.
-FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-command-line-argument"]
 
@@ -22,14 +27,23 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(out: str = LIB, extra: list[str] | None = None, verbose: bool = False) -> str:
-    tmp = out + ".tmp"
-    cmd = [hipcc(), *FLAGS, *(extra or []), "-o", tmp, *SOURCES]
+def _run(cmd: list[str]) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return r.stderr
+
+
+def build(out: str = LIB, extra: list[str] | None = None, verbose: bool = False) -> str:
+    with tempfile.TemporaryDirectory(prefix="sscan_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, os.path.basename(src) + ".o") for src in SOURCES]
+        cmds = [[hipcc(), *FLAGS, *(extra or []), "-c", "-o", obj, src] for src, obj in zip(SOURCES, objs)]
+        with ThreadPoolExecutor(max_workers=len(cmds)) as pool:
+            logs = list(pool.map(_run, cmds))
+        tmp = out + ".tmp"
+        logs.append(_run([hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]))
     if verbose:
-        print(r.stderr)
+        print("\n".join(logs))
     os.replace(tmp, out)
     return out
 

@@ -77,11 +77,34 @@ const char *sscan_status_string(int status) {
         case SSCAN_OK: return "ok";
         case SSCAN_ERR_NULL: return "required pointer is NULL";
         case SSCAN_ERR_SHAPE: return "invalid shape (negative size or int64 overflow)";
-        case SSCAN_ERR_UNSUPPORTED: return "unsupported dstate or io_dtype";
+        case SSCAN_ERR_UNSUPPORTED: return "unsupported dstate, io_dtype or size";
         case SSCAN_ERR_ALIAS: return "output overlaps another argument";
         case SSCAN_ERR_HIP: return "HIP runtime error";
         default: return "unknown status";
     }
+}
+
+int sscan_forward_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                       sscan_plan_info *out) {
+    g_last_error[0] = '\0';
+    if (!out) return fail(SSCAN_ERR_NULL, "required pointer %s is NULL", "out");
+    memset(out, 0, sizeof *out);
+    if (io_dtype != SSCAN_F32 && io_dtype != SSCAN_BF16)
+        return fail(SSCAN_ERR_UNSUPPORTED, "io_dtype must be SSCAN_F32 or SSCAN_BF16");
+    if (dstate < 1 || dstate > SSCAN_MAX_DSTATE)
+        return fail(SSCAN_ERR_UNSUPPORTED, "dstate must be in 1..16");
+    int64_t bx;
+    if (!nbytes(&bx, io_dtype == SSCAN_BF16 ? 2 : 4, batch, seqlen, dim))
+        return fail(SSCAN_ERR_SHAPE, "negative size or byte size overflows int64");
+    const sscan::FwdPlan p = sscan::plan_forward(batch, seqlen, dim, dstate, io_dtype);
+    if (p.reject) return fail(SSCAN_ERR_UNSUPPORTED, "%s", p.reject);
+    out->kernel = p.lockstep ? SSCAN_PLAN_LOCKSTEP : SSCAN_PLAN_SEGMENT;
+    out->segments = p.segments;
+    out->seg_len = p.seg_len;
+    out->tiles = p.tiles;
+    out->chunk_tokens = p.lockstep ? int64_t(sscan::kLockW) * sscan::kLockT : 0;
+    out->scratch_bytes = int64_t(p.ws_bytes);
+    return SSCAN_OK;
 }
 
 // Front end of the fused entry points (d_conv == 0: none).
@@ -140,7 +163,8 @@ static int forward_impl(const void *x, const void *delta, const float *A, const 
         return e == hipSuccess ? SSCAN_OK : fail_hip("state copy launch", e);
     }
 
-    const sscan::FwdPlan plan = sscan::plan_forward(batch, seqlen, dim, dstate);
+    const sscan::FwdPlan plan = sscan::plan_forward(batch, seqlen, dim, dstate, io_dtype);
+    if (plan.reject) return fail(SSCAN_ERR_UNSUPPORTED, "%s", plan.reject);
     void *ws = nullptr;
     hipError_t e = hipMallocAsync(&ws, plan.ws_bytes, s);
     if (e != hipSuccess) return fail_hip("hipMallocAsync (scratch)", e);
@@ -217,6 +241,7 @@ int sscan_backward(const void *x, const void *delta, const float *A, const void 
     }
 
     const sscan::BwdPlan plan = sscan::plan_backward(batch, seqlen, dim, dstate);
+    if (plan.reject) return fail(SSCAN_ERR_UNSUPPORTED, "%s", plan.reject);
     void *ws = nullptr;
     hipError_t e = hipMallocAsync(&ws, plan.ws_bytes, s);
     if (e != hipSuccess) return fail_hip("hipMallocAsync (scratch)", e);
@@ -266,7 +291,12 @@ int sscan_ssd_forward(const void *x, const void *delta, const float *A, const vo
         !nbytes(&bbc, es, batch, seqlen, ngroups * dstate) || !nbytes(&bh, 4, nheads) ||
         !nbytes(&bs, 4, batch, nheads, headdim * dstate) || !nbytes(&tmp, 1, batch, nheads))
         return fail(SSCAN_ERR_SHAPE, "negative size or byte size overflows int64");
-    if (batch * nheads > 0x7FFFFFFF) return fail(SSCAN_ERR_SHAPE, "batch * nheads above 2^31 - 1");
+    {
+        const sscan::SsdArgs probe{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                   nullptr, batch, seqlen, nheads, headdim, ngroups, int(dstate), io_dtype};
+        if (batch > 0 && sscan::ssd_work_items(probe) > sscan::kMaxWorkItems)
+            return fail(SSCAN_ERR_UNSUPPORTED, "batch * nheads too large for one launch");
+    }
     const Span ins[] = {{x, bx, "x"}, {delta, bd, "delta"}, {A, bh, "A"}, {B, bbc, "B"}, {C, bbc, "C"},
                         {Dskip, Dskip ? bh : 0, "Dskip"},
                         {initial_state, initial_state ? bs : 0, "initial_state"}};
@@ -305,8 +335,8 @@ int sscan_ssd_step(float *state, const void *x_t, const void *delta_t, const flo
         !nbytes(&bbc, es, batch, ngroups * dstate) || !nbytes(&bh, 4, nheads) ||
         !nbytes(&bs, 4, batch, nheads, headdim * dstate))
         return fail(SSCAN_ERR_SHAPE, "negative size or byte size overflows int64");
-    // one thread per 8 states (32 bytes): the grid's 256-thread blocks must stay below 2^31
-    if (bs / 32 / 256 >= 0x7FFFFFFF) return fail(SSCAN_ERR_SHAPE, "state too large for one launch");
+    if (sscan::ssd_step_work_items(batch, nheads, headdim, dstate) > sscan::kMaxWorkItems)
+        return fail(SSCAN_ERR_UNSUPPORTED, "state too large for one launch");
     const Span ins[] = {{x_t, bx, "x_t"}, {delta_t, bd, "delta_t"}, {A, bh, "A"}, {B_t, bbc, "B_t"},
                         {C_t, bbc, "C_t"}, {Dskip, Dskip ? bh : 0, "Dskip"}};
     const Span outs[] = {{state, bs, "state"}, {y_t, bx, "y_t"}};
@@ -354,6 +384,8 @@ static int step_impl(float *state, const void *x_t, const void *delta_t, const f
     rc = check_alias(outs, 3, ins, 9);
     if (rc) return rc;
     if (batch == 0 || dim == 0) return SSCAN_OK;
+    if (sscan::step_work_items(batch, dim, dstate, fused) > sscan::kMaxWorkItems)
+        return fail(SSCAN_ERR_UNSUPPORTED, "batch * dim too large for one decode-step launch");
     sscan::StepArgs a{state, x_t, delta_t, A, B_t, C_t, Dskip, y_t, batch, dim, int(dstate), io_dtype};
     if (fused) {
         a.fe = {fe.conv_weight, fe.conv_bias, fe.delta_bias, conv_state, fe.d_conv, fe.activation};

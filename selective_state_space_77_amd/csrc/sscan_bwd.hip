@@ -614,30 +614,33 @@ __global__ __launch_bounds__(256) void k_bwd_reduce(const float *__restrict__ pa
                                                     float *__restrict__ dA, float *__restrict__ dD,
                                                     int64_t batch, int64_t L, int64_t dim, int N,
                                                     int64_t tiles_per_batch) {
-    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t nbc = batch * L * (2 * NT);
-    if (i < nbc) {
-        float s = 0.f;
-        for (int64_t t = 0; t < tiles_per_batch; ++t) s += part_bc[t * nbc + i];
-        const int64_t row = i / (2 * NT);
-        const int j = int(i - row * (2 * NT));
-        if (j < NT) {
-            if (j < N) dB[row * N + j] = s;
-        } else if (j - NT < N) {
-            dC[row * N + (j - NT)] = s;
+    // the blocks stride over both ranges, so the launch stays within the 32-bit
+    // work-item count
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < nbc + dim * (NT + 1);
+         i += int64_t(gridDim.x) * blockDim.x) {
+        if (i < nbc) {
+            float s = 0.f;
+            for (int64_t t = 0; t < tiles_per_batch; ++t) s += part_bc[t * nbc + i];
+            const int64_t row = i / (2 * NT);
+            const int j = int(i - row * (2 * NT));
+            if (j < NT) {
+                if (j < N) dB[row * N + j] = s;
+            } else if (j - NT < N) {
+                dC[row * N + (j - NT)] = s;
+            }
+            continue;
         }
-        return;
-    }
-    const int64_t k = i - nbc;
-    if (k >= dim * (NT + 1)) return;
-    const int64_t dd = k / (NT + 1);
-    const int n = int(k - dd * (NT + 1));
-    float s = 0.f;
-    for (int64_t bb = 0; bb < batch; ++bb) s += part_ad[(bb * dim + dd) * (NT + 1) + n];
-    if (n == NT) {
-        if (dD) dD[dd] = s;
-    } else if (n < N) {
-        dA[dd * N + n] = s;
+        const int64_t k = i - nbc;
+        const int64_t dd = k / (NT + 1);
+        const int n = int(k - dd * (NT + 1));
+        float s = 0.f;
+        for (int64_t bb = 0; bb < batch; ++bb) s += part_ad[(bb * dim + dd) * (NT + 1) + n];
+        if (n == NT) {
+            if (dD) dD[dd] = s;
+        } else if (n < N) {
+            dA[dd * N + n] = s;
+        }
     }
 }
 
@@ -662,7 +665,8 @@ hipError_t backward_t(const BwdArgs &a, const BwdPlan &p, void *ws, hipStream_t 
     SSCAN_BWD(false);
 #undef SSCAN_BWD
     const int64_t n = a.batch * a.L * 2 * NT + a.dim * (NT + 1);
-    hipLaunchKernelGGL((k_bwd_reduce<NT>), dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, part_bc,
+    hipLaunchKernelGGL((k_bwd_reduce<NT>), dim3(unsigned(std::min<int64_t>((n + 255) / 256, int64_t(1) << 20))),
+                       dim3(256), 0, s, part_bc,
                        part_ad, a.dB, a.dC, a.dA, a.dD, a.batch, a.L, a.dim, a.N, p.tiles_per_batch);
     return hipGetLastError();
 }
@@ -687,6 +691,7 @@ BwdPlan plan_backward(int64_t batch, int64_t L, int64_t dim, int64_t N) {
     p.nt = N <= 1 ? 1 : N <= 2 ? 2 : N <= 4 ? 4 : N <= 8 ? 8 : 16;
     p.tiles_per_batch = (dim + kWave - 1) / kWave;
     p.tiles = batch * p.tiles_per_batch;
+    if (p.tiles > kMaxWorkItems / (BW * kWave)) p.reject = "batch * dim too large for one backward launch";
     const int64_t nchunks = (L + BCH - 1) / BCH;
     size_t off = 0;
     p.off_bc = off;

@@ -44,11 +44,23 @@ struct FeArgs {
     int act;                  // 0 none, 1 SiLU
 };
 
+// Limits every launch is planned against.  A raw buffer descriptor covers at
+// most kMaxDescBytes bytes (its record count is kept below 2^31), and the byte
+// offsets added to it are 32-bit: a kernel that walks a span through one
+// descriptor needs the span, plus whatever it prefetches past its end, below
+// 2^32 so that no offset wraps.  A dispatch's total work-item count in x is a
+// 32-bit quantity (kMaxWorkItems).
+constexpr int64_t kMaxDescBytes = 0x7FFFFFFF;
+constexpr int64_t kMaxWorkItems = 0xFFFFFFFFll;
+
 // Work split of one forward pass.  Segment kernels cut the sequence into
 // `segments` time segments of `seg_len` tokens (the last may be shorter); each
 // wave scans one segment of 64 channels of one batch row.  The lockstep kernel
 // gives each 64-channel tile one workgroup for the whole sequence.
+// `reject` is non-NULL when the shape cannot be run within the limits above
+// (then nothing may be launched); it names the reason.
 struct FwdPlan {
+    const char *reject;
     int64_t tiles_per_batch;  // ceil(dim / 64)
     int64_t tiles;            // batch * tiles_per_batch
     int64_t seg_len;
@@ -59,7 +71,8 @@ struct FwdPlan {
     size_t ws_bytes;          // scratch: [B/(n+1), C] rows, tile flags, segment aggregates
 };
 
-FwdPlan plan_forward(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+// io: 0 fp32, 1 bf16 (the element size of x, delta and y sets the segment spans)
+FwdPlan plan_forward(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io);
 
 struct FwdArgs {
     const void *x, *delta;
@@ -90,6 +103,7 @@ hipError_t launch_prep(const void *B, const void *C, const float *A, float *bc, 
 // sequence; scratch holds the staged B/C rows, tile flags, the state entering
 // every chunk, per-tile dB/dC partials and per-batch-row dA/dDskip partials.
 struct BwdPlan {
+    const char *reject;  // non-NULL: the shape exceeds a launch limit (reason)
     int64_t tiles_per_batch, tiles;
     int nt;
     size_t off_bc, off_flags, off_ckpt, off_pbc, off_pad;
@@ -169,5 +183,12 @@ struct StepArgs {
 };
 
 hipError_t launch_step(const StepArgs &a, hipStream_t s);
+
+// Total work items of the decode step's launch (checked against kMaxWorkItems
+// before launching).
+int64_t step_work_items(int64_t batch, int64_t dim, int64_t N, bool front_end);
+// Workgroups x threads of the scalar-A-per-head launches.
+int64_t ssd_work_items(const SsdArgs &a);
+int64_t ssd_step_work_items(int64_t batch, int64_t H, int64_t P, int64_t N);
 
 }  // namespace sscan

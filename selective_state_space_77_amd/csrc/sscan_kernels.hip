@@ -52,6 +52,8 @@ using namespace dev;
 //  * blocks [0, prep_blocks): stage B/(n+1) and C of every token as fp32 rows
 //    of 2*NT floats, so a scan wave reads one token's parameters with two
 //    scalar loads.  States n >= N (padding up to NT) get B = C = 0 and stay 0.
+//    The blocks stride over the rows, so the launch stays within the 32-bit
+//    work-item count however many tokens there are.
 //  * the remaining blocks: one wave per 64-channel tile decides whether every
 //    A row of the tile has the structured-real form A[d,n] = (n+1)*A[d,0],
 //    A[d,0] < 0 (tile_fast = 1) or not (0).  Later launches read the flag and
@@ -64,17 +66,18 @@ __global__ __launch_bounds__(256) void k_prep(const typename IO::T *__restrict__
                                               int *__restrict__ tile_fast, int64_t tiles_per_batch,
                                               int64_t prep_blocks) {
     if (blockIdx.x < prep_blocks) {
-        const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-        if (i >= rows * NT) return;
-        const int64_t r = i / NT;
-        const int n = int(i - r * NT);
-        float bv = 0.f, cv = 0.f;
-        if (n < N) {
-            bv = IO::ld(B, r * N + n);
-            cv = IO::ld(C, r * N + n);
+        for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < rows * NT;
+             i += prep_blocks * blockDim.x) {
+            const int64_t r = i / NT;
+            const int n = int(i - r * NT);
+            float bv = 0.f, cv = 0.f;
+            if (n < N) {
+                bv = IO::ld(B, r * N + n);
+                cv = IO::ld(C, r * N + n);
+            }
+            bc[r * (2 * NT) + n] = bv / float(n + 1);
+            bc[r * (2 * NT) + NT + n] = cv;
         }
-        bc[r * (2 * NT) + n] = bv / float(n + 1);
-        bc[r * (2 * NT) + NT + n] = cv;
         return;
     }
     const int64_t dt = (int64_t(blockIdx.x) - prep_blocks) * 4 + threadIdx.x / kWave;
@@ -88,10 +91,14 @@ __global__ __launch_bounds__(256) void k_prep(const typename IO::T *__restrict__
     if (lane == 0) tile_fast[dt] = all_ok ? 1 : 0;
 }
 
+// Elementwise launches stride over their range with at most this many blocks.
+constexpr int64_t kMaxStrideBlocks = int64_t(1) << 20;
+
 __global__ __launch_bounds__(256) void k_copy_or_zero(float *__restrict__ dst,
                                                       const float *__restrict__ src, int64_t count) {
-    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (i < count) dst[i] = src ? src[i] : 0.f;
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < count;
+         i += int64_t(gridDim.x) * blockDim.x)
+        dst[i] = src ? src[i] : 0.f;
 }
 
 // ----------------------------------------------------------------------------
@@ -120,20 +127,21 @@ __global__ __launch_bounds__(256) void k_conv_tail(const typename IO::T *__restr
                                                    FeArgs fe, typename IO::T *__restrict__ out,
                                                    int64_t batch, int64_t L, int64_t dim) {
     using T = typename IO::T;
-    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t rows = fe.K - 1;
-    if (i >= batch * rows * dim) return;
-    const int64_t d = i % dim;
-    const int64_t j = (i / dim) % rows;
-    const int64_t b = i / (dim * rows);
-    const int64_t t = L - rows + j;
     const T *cs = static_cast<const T *>(fe.conv_state);
-    T v = T(0);
-    if (t >= 0)
-        v = x[(b * L + t) * dim + d];
-    else if (cs)
-        v = cs[(b * rows + (t + rows)) * dim + d];
-    out[i] = v;
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < batch * rows * dim;
+         i += int64_t(gridDim.x) * blockDim.x) {
+        const int64_t d = i % dim;
+        const int64_t j = (i / dim) % rows;
+        const int64_t b = i / (dim * rows);
+        const int64_t t = L - rows + j;
+        T v = T(0);
+        if (t >= 0)
+            v = x[(b * L + t) * dim + d];
+        else if (cs)
+            v = cs[(b * rows + (t + rows)) * dim + d];
+        out[i] = v;
+    }
 }
 
 // ----------------------------------------------------------------------------
@@ -859,7 +867,7 @@ void prep_t(const void *B, const void *C, const float *A, float *bc, int *flags,
             int64_t dim, int N, hipStream_t s) {
     using T = typename IO::T;
     const int64_t tiles_per_batch = (dim + kWave - 1) / kWave;
-    const int64_t prep_blocks = (rows * NT + 255) / 256;
+    const int64_t prep_blocks = std::min<int64_t>((rows * NT + 255) / 256, kMaxStrideBlocks);
     const int64_t cls_blocks = (tiles_per_batch + 3) / 4;
     hipLaunchKernelGGL((k_prep<IO, NT>), dim3(unsigned(prep_blocks + cls_blocks)), dim3(256), 0, s,
                        static_cast<const T *>(B), static_cast<const T *>(C), bc, rows, N, A, dim,
@@ -970,24 +978,40 @@ hipError_t step_io(const StepArgs &a, hipStream_t s) {
 
 }  // namespace
 
-FwdPlan plan_forward(int64_t batch, int64_t L, int64_t dim, int64_t N) {
+FwdPlan plan_forward(int64_t batch, int64_t L, int64_t dim, int64_t N, int io) {
     FwdPlan p{};
     p.nt = round_nt(N);
     p.tiles_per_batch = (dim + kWave - 1) / kWave;
     p.tiles = batch * p.tiles_per_batch;
-    // Segment kernels: enough segments for ~4 waves per SIMD (1024 SIMDs) with
-    // segments of >= 64 tokens.
+    const int64_t rowb = dim * (io == 1 ? 2 : 4);  // bytes of one token row of x, delta or y
+    // Segment kernels walk a segment's token rows through one buffer descriptor
+    // with 32-bit offsets, prefetching up to 2*kUnroll rows past its end: the
+    // segment must fit a descriptor (kMaxDescBytes) and those extra rows must fit
+    // below 2^31 as well, so no offset reaches 2^32.
+    if (rowb * (2 * kUnroll) > kMaxDescBytes) {
+        p.reject = "dim too large: one token row of x exceeds 2^27 bytes";
+        return p;
+    }
+    const int64_t seg_max = rowb > 0 ? kMaxDescBytes / rowb : L;  // tokens per segment, at most
+    // Enough segments for ~4 waves per SIMD (1024 SIMDs) with segments of >= 64
+    // tokens, and at least as many as the descriptor span needs.
     const int64_t target_waves = kTargetWaves;
     int64_t S = p.tiles > 0 ? (target_waves + p.tiles - 1) / p.tiles : 1;
     S = std::min<int64_t>(S, std::max<int64_t>(1, L / 64));
     S = std::max<int64_t>(1, std::min<int64_t>(S, 4096));
+    S = std::max<int64_t>(S, seg_max > 0 ? (L + seg_max - 1) / seg_max : 1);
     p.seg_len = L > 0 ? (L + S - 1) / S : 1;
-    p.segments = L > 0 ? int((L + p.seg_len - 1) / p.seg_len) : 1;
+    p.segments = L > 0 ? int(std::min<int64_t>((L + p.seg_len - 1) / p.seg_len, 0x7FFFFFFF)) : 1;
+    if (p.seg_len > seg_max || p.tiles > kMaxWorkItems / (int64_t(p.segments) * kWave)) {
+        p.reject = "shape too large for the segment kernels' launch";
+        return p;
+    }
     // Lockstep kernel when the tiles alone give at least one wave per SIMD.
-    // (its buffer offsets reach (W*TS + 8) rows past a run start: keep them 32-bit)
-    p.lockstep = p.tiles >= kLockMinTiles &&
-                 (int64_t(kLockW) * kLockT + kUnroll) * dim * 4 < (int64_t(1) << 31) &&
-                 L / (int64_t(kLockW) * kLockT) < (int64_t(1) << 30);  // chunk count in 32 bits
+    // Its buffer offsets reach (W*TS + kUnroll) rows past a run start (keep them
+    // below 2^31), its token arithmetic is 32-bit (L < 2^31), and its launch is
+    // tiles x W*64 work items.
+    p.lockstep = p.tiles >= kLockMinTiles && (int64_t(kLockW) * kLockT + kUnroll) * rowb <= kMaxDescBytes &&
+                 L < (int64_t(1) << 31) && p.tiles <= kMaxWorkItems / (kLockW * kWave);
     size_t off = 0;
     p.off_bc = off;
     off += align256(size_t(batch) * L * 2 * p.nt * sizeof(float));
@@ -1018,7 +1042,7 @@ hipError_t launch_conv_tail(const void *x, const FeArgs &fe, void *conv_state_ou
                             int64_t seqlen, int64_t dim, int io, hipStream_t s) {
     const int64_t n = batch * (fe.K - 1) * dim;
     if (n <= 0) return hipSuccess;
-    const dim3 grid(unsigned((n + 255) / 256));
+    const dim3 grid(unsigned(std::min<int64_t>((n + 255) / 256, kMaxStrideBlocks)));
     if (io == 1)
         hipLaunchKernelGGL((k_conv_tail<IoBF16>), grid, dim3(256), 0, s, static_cast<const uint16_t *>(x), fe,
                            static_cast<uint16_t *>(conv_state_out), batch, seqlen, dim);
@@ -1030,13 +1054,20 @@ hipError_t launch_conv_tail(const void *x, const FeArgs &fe, void *conv_state_ou
 
 hipError_t launch_copy_or_zero(float *dst, const float *src, int64_t count, hipStream_t s) {
     if (count <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_copy_or_zero, dim3(unsigned((count + 255) / 256)), dim3(256), 0, s, dst, src,
-                       count);
+    hipLaunchKernelGGL(k_copy_or_zero, dim3(unsigned(std::min<int64_t>((count + 255) / 256, kMaxStrideBlocks))),
+                       dim3(256), 0, s, dst, src, count);
     return hipGetLastError();
 }
 
 hipError_t launch_step(const StepArgs &a, hipStream_t s) {
     return a.io == 1 ? step_io<IoBF16>(a, s) : step_io<IoF32>(a, s);
+}
+
+int64_t step_work_items(int64_t batch, int64_t dim, int64_t N, bool front_end) {
+    const int nt = round_nt(N);
+    const int64_t lpc = nt < kStepSpl ? 1 : nt / kStepSpl;
+    const int64_t bt = front_end ? 1 : kStepBt;
+    return ((batch + bt - 1) / bt * dim * lpc + 255) / 256 * 256;
 }
 
 }  // namespace sscan

@@ -842,4 +842,13 @@ hipError_t launch_ssd_step(const SsdStepArgs &a, hipStream_t s) {
     return a.io == 1 ? ssd_step_io<dev::IoBF16>(a, s) : ssd_step_io<dev::IoF32>(a, s);
 }
 
+int64_t ssd_work_items(const SsdArgs &a) {
+    // either kernel: one workgroup per (batch row, head), the larger of the two shapes
+    return a.batch * a.H * std::max<int64_t>(BTH, SWV * kWave);
+}
+
+int64_t ssd_step_work_items(int64_t batch, int64_t H, int64_t P, int64_t N) {
+    return (batch * H * P * (N / kSsdStepSpt) + 255) / 256 * 256;
+}
+
 }  // namespace sscan
