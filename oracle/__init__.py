@@ -52,7 +52,7 @@ def _load():
         lib.oracle_frontend.argtypes = [dp, dp, dp, ctypes.c_int, ctypes.c_int, dp, dp, dp, dp, dp, dp,
                                         i64, i64, i64]
         lib.oracle_frontend.restype = ctypes.c_int
-        lib.oracle_ssd_forward.argtypes = [dp] * 9 + [i64] * 6
+        lib.oracle_ssd_forward.argtypes = [dp] * 9 + [i64] * 6 + [ctypes.c_int]
         lib.oracle_ssd_forward.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -172,8 +172,8 @@ def forward_fused(xin, conv_w, delta_raw, A, B, C, Dskip=None, conv_bias=None, d
     return y, hs, cs
 
 
-def ssd_forward(x, delta, A, B, C, D=None, h0=None, want_state: bool = True):
-    """fp64 scalar-A-per-head scan (Mamba-2's SSM).
+def ssd_forward(x, delta, A, B, C, D=None, h0=None, want_state: bool = True, nthreads: int = 1):
+    """fp64 scalar-A-per-head scan (Mamba-2's SSM); rows (b, h, p) split over nthreads.
 
     x: (batch, L, H, P); delta: (batch, L, H); A: (H,); B, C: (batch, L, G, N) with G | H;
     D: (H,) or None; h0: (batch, H, P, N) or None.  Returns (y (batch, L, H, P), final state
@@ -192,7 +192,7 @@ def ssd_forward(x, delta, A, B, C, D=None, h0=None, want_state: bool = True):
     y = np.empty_like(x)
     hT = np.empty((batch, H, P, N)) if want_state else None
     rc = _load().oracle_ssd_forward(_p(x), _p(delta), _p(A), _p(B), _p(C), _p(D), _p(h0), _p(y), _p(hT),
-                                    batch, L, H, P, G, N)
+                                    batch, L, H, P, G, N, int(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle_ssd_forward failed ({rc})")
     return y, hT

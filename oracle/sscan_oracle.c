@@ -64,7 +64,8 @@
  * Every function here is pinned.
  *
  * Threads: channels (b, d) are independent, so `nthreads` workers take
- * disjoint sets of channels; each channel's token loop stays sequential.
+ * disjoint sets of channels; each channel's token loop stays sequential.  The
+ * scalar-A-per-head variant splits its independent (b, h, p) rows the same way.
  */
 #include <math.h>
 #include <pthread.h>
@@ -396,44 +397,84 @@ int oracle_frontend(const double *xin, const double *w, const double *conv_bias,
  * zero, NULL hT not written.  Written as its own loop (not through token()),
  * so that the two can be checked against each other.
  */
+typedef struct {
+    const double *x, *delta, *A, *B, *C, *D, *h0;
+    double *y, *hT;
+    int64_t batch, L, H, P, G, N;
+    int64_t first, last; /* state-row range [first, last) over batch*H*P */
+    double *st;          /* N doubles */
+} ssd_job;
+
+/* The rows (b, h, p) of [first, last), each with its own sequential token loop. */
+static void *ssd_worker(void *arg) {
+    const ssd_job *j = (const ssd_job *)arg;
+    const int64_t L = j->L, H = j->H, P = j->P, G = j->G, N = j->N;
+    const int64_t hpg = H / G;
+    double *st = j->st;
+    for (int64_t row = j->first; row < j->last; ++row) {
+        const int64_t p = row % P, h = (row / P) % H, b = row / (P * H);
+        const int64_t g = h / hpg;
+        const double a = j->A[h];
+        const double dsk = j->D ? j->D[h] : 0.0;
+        const int64_t so = row * N; /* state row of (b, h, p) */
+        for (int64_t n = 0; n < N; ++n) st[n] = j->h0 ? j->h0[so + n] : 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            const double dt = j->delta[(b * L + t) * H + h];
+            const double abar = exp(dt * a);
+            const double gain = (a != 0.0) ? expm1(dt * a) / a : dt;
+            const double xv = j->x[((b * L + t) * H + h) * P + p];
+            const double *Bt = j->B + ((b * L + t) * G + g) * N;
+            const double *Ct = j->C + ((b * L + t) * G + g) * N;
+            double acc = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                st[n] = abar * st[n] + gain * Bt[n] * xv;
+                acc += Ct[n] * st[n];
+            }
+            j->y[((b * L + t) * H + h) * P + p] = acc + dsk * xv;
+        }
+        if (j->hT)
+            for (int64_t n = 0; n < N; ++n) j->hT[so + n] = st[n];
+    }
+    return NULL;
+}
+
+/* Rows (b, h, p) are independent: `nthreads` workers take disjoint row ranges, and
+ * every row's token loop stays sequential, so the result does not depend on the
+ * thread count. */
 int oracle_ssd_forward(const double *x, const double *delta, const double *A, const double *B,
                        const double *C, const double *D, const double *h0, double *y, double *hT,
-                       int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N) {
+                       int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
+                       int nthreads) {
     if (!x || !delta || !A || !B || !C || !y || batch < 0 || L < 0 || H < 1 || P < 1 || G < 1 ||
         N < 1 || H % G != 0)
         return ORACLE_ERR_ARG;
-    double *st = (double *)malloc((size_t)N * sizeof(double));
-    if (!st) return ORACLE_ERR_ARG;
-    const int64_t hpg = H / G;
-    for (int64_t b = 0; b < batch; ++b) {
-        for (int64_t h = 0; h < H; ++h) {
-            const int64_t g = h / hpg;
-            const double a = A[h];
-            const double dsk = D ? D[h] : 0.0;
-            for (int64_t p = 0; p < P; ++p) {
-                const int64_t so = ((b * H + h) * P + p) * N; /* state row of (b, h, p) */
-                for (int64_t n = 0; n < N; ++n) st[n] = h0 ? h0[so + n] : 0.0;
-                for (int64_t t = 0; t < L; ++t) {
-                    const double dt = delta[(b * L + t) * H + h];
-                    const double abar = exp(dt * a);
-                    const double gain = (a != 0.0) ? expm1(dt * a) / a : dt;
-                    const double xv = x[((b * L + t) * H + h) * P + p];
-                    const double *Bt = B + ((b * L + t) * G + g) * N;
-                    const double *Ct = C + ((b * L + t) * G + g) * N;
-                    double acc = 0.0;
-                    for (int64_t n = 0; n < N; ++n) {
-                        st[n] = abar * st[n] + gain * Bt[n] * xv;
-                        acc += Ct[n] * st[n];
-                    }
-                    y[((b * L + t) * H + h) * P + p] = acc + dsk * xv;
-                }
-                if (hT)
-                    for (int64_t n = 0; n < N; ++n) hT[so + n] = st[n];
-            }
-        }
+    const int64_t rows = batch * H * P;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > rows) nthreads = rows > 0 ? (int)rows : 1;
+    ssd_job *jobs = (ssd_job *)calloc((size_t)nthreads, sizeof(ssd_job));
+    pthread_t *tid = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    double *st = (double *)calloc((size_t)(nthreads * N), sizeof(double));
+    char *started = (char *)calloc((size_t)nthreads, 1);
+    if (!jobs || !tid || !st || !started) {
+        free(jobs); free(tid); free(st); free(started);
+        return ORACLE_ERR_ARG;
     }
-    free(st);
+    for (int i = 0; i < nthreads; ++i) {
+        ssd_job j = {x, delta, A, B, C, D, h0, y, hT, batch, L, H, P, G, N,
+                     rows * i / nthreads, rows * (i + 1) / nthreads, st + (int64_t)i * N};
+        jobs[i] = j;
+    }
+    /* a worker that cannot be started runs on the calling thread instead */
+    for (int i = 0; i < nthreads; ++i) {
+        if (nthreads > 1 && pthread_create(&tid[i], NULL, ssd_worker, &jobs[i]) == 0)
+            started[i] = 1;
+        else
+            ssd_worker(&jobs[i]);
+    }
+    for (int i = 0; i < nthreads; ++i)
+        if (started[i]) pthread_join(tid[i], NULL);
+    free(jobs); free(tid); free(st); free(started);
     return ORACLE_OK;
 }
 
-int oracle_version(void) { return 4; }
+int oracle_version(void) { return 5; }

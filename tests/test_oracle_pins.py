@@ -618,3 +618,16 @@ def test_ssd_resumes_from_its_state():
     yb, hb = oracle.ssd_forward(x[:, 11:], delta[:, 11:], A, B[:, 11:], C[:, 11:], D, h0=ha)
     np.testing.assert_allclose(np.concatenate([ya, yb], axis=1), y, rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(hb, hT, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("nthreads", [2, 3, 7, 64])
+def test_ssd_threads_do_not_change_the_result(nthreads):
+    """Rows (batch row, head, channel) split over worker threads give the single-thread
+    result bit for bit, with groups and an initial state (every row's loop is unchanged)."""
+    rng = np.random.default_rng(55)
+    x, delta, A, B, C, D = _ssd_inputs(rng, H=4, G=2, A_zero_head=True)
+    h0 = rng.standard_normal((x.shape[0], 4, x.shape[3], B.shape[3]))
+    y1, h1 = oracle.ssd_forward(x, delta, A, B, C, D, h0=h0, nthreads=1)
+    yn, hn = oracle.ssd_forward(x, delta, A, B, C, D, h0=h0, nthreads=nthreads)
+    np.testing.assert_array_equal(y1, yn)
+    np.testing.assert_array_equal(h1, hn)
