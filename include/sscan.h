@@ -278,8 +278,8 @@ int sscan_ssd_step(float *state, const void *x_t, const void *delta_t, const flo
 /*
  * How sscan_forward (and the _from_state and _fused variants) would split a
  * problem of this shape, computed on the host without touching the GPU: which
- * kernel scans the structured-real tiles, how the sequence is cut, and the device
- * scratch the call allocates.  This makes the chosen path visible to the caller
+ * kernel scans the sequence (either takes tiles of any A), how the sequence is
+ * cut, and the device scratch the call allocates.  This makes the chosen path visible to the caller
  * (the pages warn that a benchmark is only meaningful once it is confirmed that
  * the fused kernel is the one running: "Mamba and State Space Models", failure
  * modes).
@@ -298,8 +298,8 @@ int sscan_ssd_step(float *state, const void *x_t, const void *delta_t, const flo
 #define SSCAN_PLAN_SEGMENT 2  /* one wave per (64-channel tile, time segment), two passes   */
 typedef struct {
     int32_t kernel;        /* SSCAN_PLAN_LOCKSTEP or SSCAN_PLAN_SEGMENT                    */
-    int32_t segments;      /* time segments per tile of the segment kernels (which also    */
-    int64_t seg_len;       /* take general-A tiles); tokens per segment, the last shorter  */
+    int32_t segments;      /* time segments per tile (1 for the lockstep kernel)           */
+    int64_t seg_len;       /* tokens per segment, the last shorter (lockstep: seqlen)      */
     int64_t tiles;         /* batch * ceil(dim / 64)                                       */
     int64_t chunk_tokens;  /* lockstep: tokens per chunk (waves x run length); else 0      */
     int64_t scratch_bytes; /* device scratch one call allocates (stream-ordered)           */

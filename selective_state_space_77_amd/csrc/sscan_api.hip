@@ -99,8 +99,8 @@ int sscan_forward_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstat
     const sscan::FwdPlan p = sscan::plan_forward(batch, seqlen, dim, dstate, io_dtype);
     if (p.reject) return fail(SSCAN_ERR_UNSUPPORTED, "%s", p.reject);
     out->kernel = p.lockstep ? SSCAN_PLAN_LOCKSTEP : SSCAN_PLAN_SEGMENT;
-    out->segments = p.segments;
-    out->seg_len = p.seg_len;
+    out->segments = p.lockstep ? 1 : p.segments;
+    out->seg_len = p.lockstep ? seqlen : p.seg_len;
     out->tiles = p.tiles;
     out->chunk_tokens = p.lockstep ? int64_t(sscan::kLockW) * sscan::kLockT : 0;
     out->scratch_bytes = int64_t(p.ws_bytes);

@@ -38,6 +38,22 @@ __device__ __forceinline__ float zoh_gain(float dt, float a, float z, float abar
     return (abar - 1.f) / a;
 }
 
+// The same gain without a branch or an IEEE division, for kernels that hold many
+// states per lane: both forms are evaluated and one selected, and (Abar - 1)/A
+// uses the hardware reciprocal (1 ulp), so the result is within a few ulp of the
+// form above.
+__device__ __forceinline__ float zoh_gain_nb(float dt, float a, float z, float abar) {
+    float p = 1.f / 5040.f;
+    p = fmaf(p, z, 1.f / 720.f);
+    p = fmaf(p, z, 1.f / 120.f);
+    p = fmaf(p, z, 1.f / 24.f);
+    p = fmaf(p, z, 1.f / 6.f);
+    p = fmaf(p, z, 0.5f);
+    p = fmaf(p, z, 1.f);
+    const float big = (abar - 1.f) * __builtin_amdgcn_rcpf(a);
+    return fabsf(z) < 0.25f ? dt * p : big;
+}
+
 // 1 - exp(z) given r = exp(z), without the cancellation of 1 - r near z = 0:
 // -z (1 + z/2 + z^2/6 + ... + z^5/720) for |z| < 1/8 (truncation below 1e-9
 // relative), 1 - r otherwise (there the cancellation costs at most a factor
@@ -51,6 +67,25 @@ __device__ __forceinline__ float one_minus_exp(float z, float r) {
     p = fmaf(p, z, 0.5f);
     p = fmaf(p, z, 1.f);
     return fabsf(z) < 0.125f ? -z * p : 1.f - r;
+}
+
+// 1 - 2^u given r = 2^u (hardware exp2, within 1 ulp), in five operations and
+// without a branch or a compare: the smaller of
+//   * the series -u ln2 (1 + u ln2/2 + (u ln2)^2/6), which for u <= 0 is never
+//     below the true value and exceeds it by (u ln2)^4/24 at most, and
+//   * (1 + 2^-22) - r, which is never below the true value either (2^-22 is twice
+//     the largest error of r next to 1) and exceeds it by at most 3 * 2^-24.
+// For small |u| the series is the smaller (it is the accurate one there, where
+// 1 - r cancels); from |u ln2| ~ 0.05 on, 1 - r is, with a relative error below
+// 1e-5.  The same ordering holds for u > 0 (negative step sizes), where both
+// underestimate the magnitude of a negative value.  u = 0 gives -0 (a zero step
+// leaves the state exactly unchanged); NaN propagates.
+__device__ __forceinline__ float one_minus_exp2(float u, float r) {
+    constexpr float c0 = -0.69314718055994530942f;   // -ln2
+    constexpr float c1 = -0.24022650695910071233f;   // -ln2^2/2
+    constexpr float c2 = -0.05550410866482157995f;   // -ln2^3/6
+    const float p = fmaf(fmaf(u, c2, c1), u, c0);
+    return fminf(p * u, (1.f + 0x1p-22f) - r);
 }
 
 // Structured-real state update shared by the scan kernels.  With A[d,n] =

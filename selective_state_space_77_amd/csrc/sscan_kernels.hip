@@ -251,8 +251,9 @@ __global__ __launch_bounds__(kWave) void k_seg(
     auto token = [&](float xv, float dv, const float *row, uint32_t sto) {
         float yacc = 0.f;
         if constexpr (kFast) {
-            const float r = exp2_hw(dv * a2);
-            sr_update<NT>(r, one_minus_exp(dv * a[0], r), xv, row, k, [&](int n) {
+            const float u = dv * a2;
+            const float r = exp2_hw(u);
+            sr_update<NT>(r, one_minus_exp2(u, r), xv, row, k, [&](int n) {
                 if (kMain) yacc = fmaf(row[NT + n], k[n], yacc);
             });
         } else {
@@ -345,85 +346,100 @@ __global__ __launch_bounds__(kWave) void k_seg(
 }
 
 // ----------------------------------------------------------------------------
-// Lockstep chunked scan for structured-real tiles (one launch, no aggregate
-// pass).  A workgroup of W waves owns one 64-channel tile for the whole
-// sequence, processed in chunks of W*TS tokens; wave w takes the w-th run of
-// TS tokens of every chunk:
+// Lockstep chunked scan (one launch, no aggregate pass).  A workgroup of W waves
+// owns one 64-channel tile for the whole sequence, processed in chunks of W*TS
+// tokens; wave w takes the w-th run of TS tokens of every chunk:
 //   1. local pass: wave 0 starts from the chunk's carried state, the others
-//      from zero; each keeps its TS finished outputs and the running decay
-//      rho_tau = prod r (r = exp(delta*A[d,0])) in VGPRs;
-//   2. every wave publishes (sum of delta, local final state) in LDS; after a
+//      from zero; each keeps its TS outputs and what it needs to rebuild the
+//      decay since its run start in VGPRs;
+//   2. every wave publishes (sum of delta, local end state) in LDS; after a
 //      barrier the states are split across the waves (NT/W each) and every
 //      wave folds the W aggregates of its states in order with the
-//      associative combine, writing the state entering each wave's run and
-//      the chunk's carry-out back to LDS;
+//      associative combine -- the decay of a run is exp(A sum(delta)) -- writing
+//      the state entering each wave's run and the chunk's carry-out to LDS;
 //   3. after a second barrier waves 1..W-1 add the contribution of the state
-//      they entered with, sum_n C_n rho_tau^(n+1) k_in[n], evaluated as a
-//      Horner polynomial in rho_tau, and store y.
-template <class IO, int NT, int W, int TS, bool FE>
-__global__ __launch_bounds__(W *kWave) void k_lockstep(
-    const typename IO::T *__restrict__ x, const typename IO::T *__restrict__ delta,
+//      they entered with, sum_n C_n Abar_n(run start..t) k_in[n], and store y.
+// A tile whose A rows all have the structured-real form takes the fast path:
+// one exp per token, the scaled state k = -A[d,0] h, and the step-3 sum as a
+// Horner polynomial in rho = prod r (2 VALU per state).  Any other tile takes
+// the general path in the same launch: an exp and the ZOH gain per state, and
+// the step-3 decays exp(A[d,n] * (sum of delta since the run start)).
+template <int NT, int W>
+struct LockLds {
+    float sum[W][kWave];      // sum of delta over each run
+    float k[W][NT][kWave];    // each run's end state from its starting state
+    float pre[W][NT][kWave];  // [0]: the chunk's carry-out; [j]: state entering run j
+    float zero[NT][kWave];    // the (zero) state runs 1.. start from
+    float arow[NT][kWave];    // general path: each lane's A row (kept out of VGPRs)
+};
+
+template <class IO, int NT, int W, int TS, bool FE, bool kFast>
+__device__ __forceinline__ void lockstep_tile(
+    LockLds<NT, W> &sh, const typename IO::T *__restrict__ x, const typename IO::T *__restrict__ delta,
     const float *__restrict__ A, const float *__restrict__ bc, const float *__restrict__ Dskip,
-    const float *__restrict__ h0, typename IO::T *__restrict__ y, float *__restrict__ final_state,
-    const int *__restrict__ tile_fast, int64_t L, int64_t dim, int N, int64_t tiles_per_batch,
-    FeArgs fe) {
+    const float *__restrict__ h0, typename IO::T *__restrict__ y, float *__restrict__ final_state, int L,
+    int64_t dim, int N, int64_t b, int64_t dbase, int w, int lane, const FeArgs &fe) {
     using T = typename IO::T;
     constexpr int U = kUnroll;
     static_assert(TS % U == 0 && U % 2 == 0, "TS must be a multiple of the prefetch group");
+    static_assert(W >= 3, "waves 0, 1 and 2 each initialise a part of the LDS");
     constexpr int NPW = (NT + W - 1) / W;  // states each wave folds
     constexpr int CH = W * TS;             // tokens per chunk
     constexpr int ES = IO::kBytes;
-    __shared__ float s_sum[W][kWave];
-    __shared__ float s_k[W][NT][kWave];
-    __shared__ float s_pre[W][NT][kWave];  // [0]: chunk carry-out; [j]: state entering run j
-    __shared__ float s_zero[NT][kWave];    // the (zero) state runs 1.. start from
 
-    const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
-    const int lane = int(threadIdx.x) % kWave;
-    const int64_t tile = blockIdx.x;
-    const int64_t b = tile / tiles_per_batch;
-    const int64_t dt = tile - b * tiles_per_batch;
-    if (!tile_fast[dt]) return;  // whole workgroup
-    const int64_t dbase = dt * kWave;
     const bool active = dbase + lane < dim;
     const int64_t d = active ? dbase + lane : dim - 1;
     const float a0 = A[d * N];
-    const float alpha = -a0, inv_alpha = 1.f / alpha, a2 = a0 * kLog2e;
-    const float dsk = Dskip ? Dskip[d] : 0.f;
+    // structured-real: the state is held scaled, k = alpha h with alpha = -A[d,0] > 0
+    const float alpha = kFast ? -a0 : 1.f;
+    const float inv_alpha = kFast ? 1.f / alpha : 1.f;
+    const float a2 = a0 * kLog2e;
+    const float dska = (Dskip ? Dskip[d] : 0.f) * alpha;  // the skip in the state's scale
+    // the states this wave folds: their decay exponent (log2) per unit of delta
+    float afold[NPW];
+#pragma unroll
+    for (int i = 0; i < NPW; ++i) {
+        const int n = w * NPW + i;
+        afold[i] = (n < N ? A[d * N + n] : 0.f) * kLog2e;
+    }
     const float *bcrow = bc + (b * L) * (2 * NT);
-    const int nchunks = int((L + CH - 1) / CH);  // below 2^31 (launch condition)
-    // per-lane byte offset inside a token row; per-token row stride (uniform)
+    const int nchunks = (L + CH - 1) / CH;
+    // per-lane byte offset inside a token row; per-token row stride (uniform).
+    // Stores of lanes past dim go to an offset beyond every descriptor's range.
     const uint32_t voff = uint32_t((dbase + lane) * ES);
+    const uint32_t voff_st = active ? voff : 0x80000000u;
     const uint32_t rowb = uint32_t(dim * ES);
 
-    // descriptors over [token t0 of chunk c, end of the sequence) of this batch row
-    auto rsrc_at = [&](const T *base, int64_t t0) {
-        return make_rsrc(base + (b * L + t0) * dim, (L - t0) * dim * ES);
+    // descriptors over [token t0, end of the sequence) of this batch row
+    auto rsrc_at = [&](const T *base, int t0) {
+        return make_rsrc(base + (b * L + t0) * dim, int64_t(L - t0) * dim * ES);
     };
 
     T xr[U], dr[U];
     {
-        const int64_t t0 = int64_t(w) * TS;
-        const rsrc_t rx = rsrc_at(x, t0), rd = rsrc_at(delta, t0);
+        const rsrc_t rx = rsrc_at(x, w * TS), rd = rsrc_at(delta, w * TS);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             xr[u] = IO::bld(rx, voff, uint32_t(u) * rowb);
             dr[u] = IO::bld(rd, voff, uint32_t(u) * rowb);
         }
     }
-    // Every run starts from a state read from LDS: run 0 from s_pre[0] (the state
+    // Every run starts from a state read from LDS: run 0 from pre[0] (the state
     // before token 0 for the first chunk, the carry-out of the previous chunk
     // after it), the others from zeros.  One code path for every wave, so the
     // reads land in the state registers without copies.
     if (w == 0) {
 #pragma unroll
-        for (int n = 0; n < NT; ++n) s_pre[0][n][lane] = (h0 && n < N) ? h0[(b * dim + d) * N + n] * alpha : 0.f;
+        for (int n = 0; n < NT; ++n) sh.pre[0][n][lane] = (h0 && n < N) ? h0[(b * dim + d) * N + n] * alpha : 0.f;
     } else if (w == 1) {
 #pragma unroll
-        for (int n = 0; n < NT; ++n) s_zero[n][lane] = 0.f;
+        for (int n = 0; n < NT; ++n) sh.zero[n][lane] = 0.f;
+    } else if (!kFast && w == 2) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n) sh.arow[n][lane] = n < N ? A[d * N + n] : 0.f;
     }
     __syncthreads();
-    const float(*kstart)[kWave] = w == 0 ? s_pre[0] : s_zero;
+    const float(*kstart)[kWave] = w == 0 ? sh.pre[0] : sh.zero;
     float k[NT];
     // front end: per-lane coefficients; the convolution window (raw inputs of
     // the 3 tokens before the current one) starts from the tokens before this
@@ -438,10 +454,10 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
     }
 
     for (int c = 0; c < nchunks; ++c) {
-        const int64_t t0 = int64_t(c) * CH + int64_t(w) * TS;
-        const int nv = int(max<int64_t>(0, min<int64_t>(TS, L - t0)));
+        const int t0 = c * CH + w * TS;  // below 2^31 (launch condition)
+        const int nv = __builtin_amdgcn_readfirstlane(max(0, min(TS, L - t0)));  // uniform
         const rsrc_t rx = rsrc_at(x, t0), rd = rsrc_at(delta, t0), ry = rsrc_at(y, t0);
-        const float *bc0 = bcrow + min(t0, L - 1) * (2 * NT);
+        const float *bc0 = bcrow + int64_t(min(t0, L - 1)) * (2 * NT);
 #pragma unroll
         for (int n = 0; n < NT; ++n) k[n] = kstart[n][lane];
         if constexpr (FE) {
@@ -451,15 +467,17 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
                 p1 = IO::cvt(pr[2]);
             }
         }
-        float yl[TS], rho[TS];
-        float cum = 1.f, dsum = 0.f;
+        // yl: the run's outputs from its starting state (fast path: in the state's
+        // scale); tk: fast path r of each token (rho = their running product),
+        // general path the running sum of delta after each token
+        float yl[TS], tk[TS];
+        float dsum = 0.f;
         // The run is processed branch-free even when it is ragged: tokens past
         // the end of the sequence read x = delta = 0 through the descriptor's
-        // range check, which leaves the state exactly unchanged (r = 1, w = 0),
-        // and their stores fall outside the range and are dropped.  Only the
-        // B/C row index is clamped.
-        // uniform: kept in a scalar register, so the per-token B/C row offsets
-        // below are scalar arithmetic (no per-token move from a vector register)
+        // range check, which leaves the state exactly unchanged, and their stores
+        // fall outside the range and are dropped.  Only the B/C row index is
+        // clamped.  uniform: kept in a scalar register, so the per-token B/C row
+        // offsets below are scalar arithmetic
         const int last = __builtin_amdgcn_readfirstlane(max(nv - 1, 0));
         int nvs = nv;  // the valid-token count as an opaque 32-bit scalar
         if constexpr (FE) asm volatile("" : "+s"(nvs));
@@ -470,14 +488,26 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
 #pragma unroll
         for (int i = 0; i < 2 * NT; ++i) rowA[i] = bc0[i];
         auto token = [&](int tau, float xv, float dv, const float *row) {
-            const float r = exp2_hw(dv * a2);
-            cum *= r;
-            rho[tau] = cum;
             dsum += dv;
-            float yacc = 0.f;
-            sr_update<NT>(r, one_minus_exp(dv * a0, r), xv, row, k,
-                          [&](int n) { yacc = fmaf(row[NT + n], k[n], yacc); });
-            yl[tau] = fmaf(yacc, inv_alpha, dsk * xv);
+            float yacc = dska * xv;
+            if constexpr (kFast) {
+                const float u = dv * a2;
+                const float r = exp2_hw(u);
+                tk[tau] = r;
+                sr_update<NT>(r, one_minus_exp2(u, r), xv, row, k,
+                              [&](int n) { yacc = fmaf(row[NT + n], k[n], yacc); });
+            } else {
+                tk[tau] = dsum;
+#pragma unroll
+                for (int n = 0; n < NT; ++n) {
+                    const float an = sh.arow[n][lane];
+                    const float abar = exp2_hw(dv * (an * kLog2e));
+                    const float g = zoh_gain_nb(dv, an, dv * an, abar);
+                    k[n] = fmaf(abar, k[n], g * ((row[n] * float(n + 1)) * xv));
+                    yacc = fmaf(row[NT + n], k[n], yacc);
+                }
+            }
+            yl[tau] = yacc;
         };
 #pragma unroll
         for (int g = 0; g < TS / U; ++g) {
@@ -488,9 +518,9 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
                     // tokens past the end are not neutral after the front end
                     // (softplus(bias) > 0): their step size is zeroed (a 0/1 factor
                     // rather than a select, so nothing is branched around), which
-                    // leaves the state exactly unchanged (r = 1, 1 - r^(n+1) = 0)
-                    // whatever their input; their outputs are not stored.  The
-                    // factor is chosen on the scalar unit from a 32-bit count.
+                    // leaves the state exactly unchanged whatever their input; their
+                    // outputs are not stored.  The factor is chosen on the scalar
+                    // unit from a 32-bit count.
                     const float xr0 = IO::cvt(xr[u]);
                     int vmb = g * U + u < nvs ? 0x3f800000 : 0;  // 1.0f or 0.0f
                     asm volatile("" : "+s"(vmb));
@@ -548,56 +578,64 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
                 token(tau + 1, xv[u + 1], dv[u + 1], rowB);
             }
         }
-        if (w == 0 && active) {
+        if (w == 0) {
             // run 0 started from the carried state: its outputs are final
             uint32_t sto = 0;
             asm volatile("" : "+s"(sto));
 #pragma unroll
             for (int tau = 0; tau < TS; ++tau) {
-                IO::bst(IO::enc(yl[tau]), ry, voff, sto);
+                IO::bst(IO::enc(yl[tau] * inv_alpha), ry, voff_st, sto);
                 sto += rowb;
             }
         }
-        s_sum[w][lane] = dsum;
+        sh.sum[w][lane] = dsum;
 #pragma unroll
-        for (int n = 0; n < NT; ++n) s_k[w][n][lane] = k[n];
+        for (int n = 0; n < NT; ++n) sh.k[w][n][lane] = k[n];
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < NPW; ++i) {
             const int n = w * NPW + i;
             if (n < NT) {
-                const float an2 = a2 * float(n + 1);
-                float P = s_k[0][n][lane];  // run 0 started from the carry: its end state is exact
+                float P = sh.k[0][n][lane];  // run 0 started from the carry: its end state is exact
                 for (int j = 1; j < W; ++j) {
-                    s_pre[j][n][lane] = P;
-                    P = fmaf(exp2_hw(an2 * s_sum[j][lane]), P, s_k[j][n][lane]);
+                    sh.pre[j][n][lane] = P;
+                    P = fmaf(exp2_hw(afold[i] * sh.sum[j][lane]), P, sh.k[j][n][lane]);
                 }
-                s_pre[0][n][lane] = P;
+                sh.pre[0][n][lane] = P;
             }
         }
         __syncthreads();
         if (w != 0 && nv > 0) {
             float kin[NT];
 #pragma unroll
-            for (int n = 0; n < NT; ++n) kin[n] = s_pre[w][n][lane];
+            for (int n = 0; n < NT; ++n) kin[n] = sh.pre[w][n][lane];
             float cA[NT], cB[NT];
 #pragma unroll
             for (int n = 0; n < NT; ++n) cA[n] = bc0[NT + n];
+            float rho = 1.f;
             auto fix = [&](int tau, const float *crow, uint32_t sto) {
-                const float rr = rho[tau];
-                float acc = crow[NT - 1] * kin[NT - 1];
+                float yv;
+                if constexpr (kFast) {
+                    // sum_n C_n rho^(n+1) k_in[n] as a Horner polynomial in rho
+                    rho *= tk[tau];
+                    float acc = crow[NT - 1] * kin[NT - 1];
 #pragma unroll
-                for (int n = NT - 2; n >= 0; --n) acc = fmaf(acc, rr, crow[n] * kin[n]);
-                acc *= rr;
-                if (active) IO::bst(IO::enc(fmaf(acc, inv_alpha, yl[tau])), ry, voff, sto);
+                    for (int n = NT - 2; n >= 0; --n) acc = fmaf(acc, rho, crow[n] * kin[n]);
+                    yv = fmaf(acc, rho, yl[tau]) * inv_alpha;
+                } else {
+                    float acc = yl[tau];
+#pragma unroll
+                    for (int n = 0; n < NT; ++n)
+                        acc = fmaf(crow[n] * kin[n], exp2_hw((sh.arow[n][lane] * kLog2e) * tk[tau]), acc);
+                    yv = acc;
+                }
+                IO::bst(IO::enc(yv), ry, voff_st, sto);
             };
             uint32_t sto = 0;
             asm volatile("" : "+s"(sto));
             // an opaque copy of the run's last index: the C row addresses are formed
             // again here (scalar arithmetic) instead of being kept from the token
             // loop across the barriers, where they would not fit in scalar registers
-            // (with the front end, whose scalar registers are fuller, keeping them
-            // measured no slower)
             int lastf = last;
             if constexpr (!FE) asm volatile("" : "+s"(lastf));
 #pragma unroll
@@ -629,9 +667,30 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
 #pragma unroll
         for (int i = 0; i < NPW; ++i) {
             const int n = w * NPW + i;
-            if (n < N) final_state[(b * dim + d) * N + n] = s_pre[0][n][lane] * inv_alpha;
+            if (n < N) final_state[(b * dim + d) * N + n] = sh.pre[0][n][lane] * inv_alpha;
         }
     }
+}
+
+template <class IO, int NT, int W, int TS, bool FE>
+__global__ __launch_bounds__(W *kWave) void k_lockstep(
+    const typename IO::T *__restrict__ x, const typename IO::T *__restrict__ delta,
+    const float *__restrict__ A, const float *__restrict__ bc, const float *__restrict__ Dskip,
+    const float *__restrict__ h0, typename IO::T *__restrict__ y, float *__restrict__ final_state,
+    const int *__restrict__ tile_fast, int L, int64_t dim, int N, int64_t tiles_per_batch, FeArgs fe) {
+    __shared__ LockLds<NT, W> sh;
+    const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
+    const int lane = int(threadIdx.x) % kWave;
+    const int64_t tile = blockIdx.x;
+    const int64_t b = tile / tiles_per_batch;
+    const int64_t dt = tile - b * tiles_per_batch;
+    // the tile's path is uniform over the workgroup
+    if (tile_fast[dt])
+        lockstep_tile<IO, NT, W, TS, FE, true>(sh, x, delta, A, bc, Dskip, h0, y, final_state, L, dim, N, b,
+                                                dt * kWave, w, lane, fe);
+    else
+        lockstep_tile<IO, NT, W, TS, FE, false>(sh, x, delta, A, bc, Dskip, h0, y, final_state, L, dim, N, b,
+                                                 dt * kWave, w, lane, fe);
 }
 
 // 1/(n+1) for state n = q SPL + j of a lane (q < LPC): constants for one or two
@@ -902,17 +961,17 @@ hipError_t forward_t(const FwdArgs &a, const FwdPlan &p, void *ws, hipStream_t s
     hipLaunchKernelGGL((k_seg<IO, NT, MAIN, FAST, FE>), GRID, dim3(kWave), 0, s, x, dl, a.A, bc,       \
                        a.Dskip, a.h0, y, a.final_state, agg_sum, agg_h, flags, a.batch, a.L, a.dim,    \
                        a.N, p.seg_len, p.segments, p.tiles_per_batch, p.tiles, a.fe)
-    // general-A tiles (waves of structured-real tiles exit at once)
-    if (p.segments > 1) SSCAN_SEG(false, false, seg_agg);
-    SSCAN_SEG(true, false, seg_main);
-    // structured-real tiles
     if (p.lockstep) {
+        // every tile in one launch (the general-A tiles take their own path in it);
         // the fused variant too: with the token loop free of register copies it fits
         // 128 VGPRs (4 waves per SIMD) without spilling
         hipLaunchKernelGGL((k_lockstep<IO, NT, kLockW, kLockT, FE>), dim3(unsigned(p.tiles)), dim3(kLockW * kWave),
-                           0, s, x, dl, a.A, bc, a.Dskip, a.h0, y, a.final_state, flags, a.L, a.dim, a.N,
+                           0, s, x, dl, a.A, bc, a.Dskip, a.h0, y, a.final_state, flags, int(a.L), a.dim, a.N,
                            p.tiles_per_batch, a.fe);
     } else {
+        // general-A tiles, then structured-real tiles (waves of the other kind exit at once)
+        if (p.segments > 1) SSCAN_SEG(false, false, seg_agg);
+        SSCAN_SEG(true, false, seg_main);
         if (p.segments > 1) SSCAN_SEG(false, true, seg_agg);
         SSCAN_SEG(true, true, seg_main);
     }
@@ -1017,10 +1076,12 @@ FwdPlan plan_forward(int64_t batch, int64_t L, int64_t dim, int64_t N, int io) {
     off += align256(size_t(batch) * L * 2 * p.nt * sizeof(float));
     p.off_flags = off;
     off += align256(size_t(p.tiles_per_batch) * sizeof(int));
+    // segment aggregates: the segment path only (the lockstep kernel takes every tile)
+    const size_t nagg = p.lockstep ? 0 : size_t(p.segments) * batch * dim;
     p.off_sum = off;
-    off += align256(size_t(p.segments) * batch * dim * sizeof(float));
+    off += align256(nagg * sizeof(float));
     p.off_h = off;
-    off += align256(size_t(p.segments) * batch * dim * p.nt * sizeof(float));
+    off += align256(nagg * p.nt * sizeof(float));
     p.ws_bytes = off;
     return p;
 }

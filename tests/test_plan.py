@@ -58,21 +58,26 @@ def test_plan_keeps_every_offset_in_range(sscan, shape):
     S, sl = p["segments"], p["seg_len"]
     assert S >= 1 and sl >= 1
     assert (S - 1) * sl < L <= S * sl
-    # segment kernels (also used for general-A tiles on the lockstep path): a segment's
-    # rows fit one descriptor and no prefetched offset wraps past 2^32
-    assert sl * rowb <= MAX_DESC
-    assert (sl + PREFETCH_ROWS) * rowb < 2**32
-    assert S * tiles * 64 <= MAX_ITEMS
+    nt = 1 if N <= 1 else 2 if N <= 2 else 4 if N <= 4 else 8 if N <= 8 else 16
+    staged = batch * L * 2 * nt * 4  # B/(n+1) and C rows, fp32
     if p["kernel"] == "lockstep":
+        # one workgroup per tile walks the whole sequence chunk by chunk
+        assert S == 1 and sl == L
         assert tiles >= 192
         assert p["chunk_tokens"] == 256
         assert LOCK_REACH_ROWS * rowb <= MAX_DESC
         assert tiles * 1024 <= MAX_ITEMS
         assert L < 2**31
+        # no segment aggregates on this path: staged rows + tile flags only
+        assert staged <= p["scratch_bytes"] <= staged + 4 * tiles + 512
     else:
         assert p["kernel"] == "segment"
         assert p["chunk_tokens"] == 0
-    assert p["scratch_bytes"] >= batch * L * 2 * 16 * 4 * (1 if N > 8 else 0)
+        # a segment's rows fit one descriptor and no prefetched offset wraps past 2^32
+        assert sl * rowb <= MAX_DESC
+        assert (sl + PREFETCH_ROWS) * rowb < 2**32
+        assert S * tiles * 64 <= MAX_ITEMS
+        assert p["scratch_bytes"] >= staged + S * batch * dim * (1 + nt) * 4
 
 
 def test_named_workloads_take_the_expected_kernels(sscan):
