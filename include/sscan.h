@@ -37,7 +37,8 @@
  *   - Any tensor with zero elements may be passed as NULL.
  *   - Calls on different streams may run concurrently; each call owns the
  *     stream-ordered scratch memory it allocates (hipMallocAsync) and frees it on
- *     the same stream.
+ *     the same stream.  The exception is sscan_forward_noalloc, which allocates
+ *     nothing and shares one static scratch array per GPU among its calls.
  */
 #ifndef SSCAN_H
 #define SSCAN_H
@@ -106,6 +107,27 @@ int sscan_forward_from_state(const void *x, const void *delta, const float *A, c
                              const void *C, const float *Dskip, const float *initial_state,
                              void *y, float *final_state, int64_t batch, int64_t seqlen,
                              int64_t dim, int64_t dstate, int io_dtype, void *stream);
+
+/*
+ * sscan_forward_from_state for callers that cannot allocate device memory: code
+ * being captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc.  It makes no allocation of any kind (no hipMalloc, hipMallocAsync or
+ * hipFree); its scratch (staged B/C rows, tile flags, segment aggregates) is a
+ * static array of 64 MiB that the library holds on each GPU it runs on until the
+ * process ends.  Every call on one GPU uses that GPU's array: calls that overlap in
+ * time on one GPU (on different streams, or from several threads) race and give
+ * wrong results; serialise them.  Nothing in the array needs to start at zero.
+ *
+ *   Arguments and results exactly as for sscan_forward_from_state.
+ * Returns SSCAN_ERR_UNSUPPORTED, before anything is enqueued, when the call needs more
+ * than 64 MiB of scratch (sscan_forward_plan reports scratch_bytes: 128 bytes per
+ * (batch row, token) at dstate 9..16, fewer below, plus the segment aggregates of the
+ * segment kernels), or SSCAN_ERR_HIP if the array's address cannot be obtained.
+ */
+int sscan_forward_noalloc(const void *x, const void *delta, const float *A, const void *B,
+                          const void *C, const float *Dskip, const float *initial_state, void *y,
+                          float *final_state, int64_t batch, int64_t seqlen, int64_t dim,
+                          int64_t dstate, int io_dtype, void *stream);
 
 /*
  * One recurrent decode step (generation: constant work and memory per token;

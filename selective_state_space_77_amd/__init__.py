@@ -7,6 +7,7 @@ package raises.
 
     forward(x, delta, A, B, C, Dskip=None, y=None, final_state=None, stream=None,
             initial_state=None)
+    forward_noalloc(...)   the same without any device allocation (static scratch)
     forward_fused(x, conv_weight, delta_raw, A, B, C, Dskip=None, conv_bias=None, delta_bias=None,
                   activation=None, conv_state=None, initial_state=None, y=None, final_state=None,
                   conv_state_out=None, stream=None)
@@ -68,6 +69,9 @@ def _load() -> ctypes.CDLL:
     lib.sscan_forward_from_state.argtypes = [vp, vp, fp, vp, vp, fp, fp, vp, fp, i64, i64, i64, i64,
                                              ctypes.c_int, vp]
     lib.sscan_forward_from_state.restype = ctypes.c_int
+    lib.sscan_forward_noalloc.argtypes = [vp, vp, fp, vp, vp, fp, fp, vp, fp, i64, i64, i64, i64,
+                                          ctypes.c_int, vp]
+    lib.sscan_forward_noalloc.restype = ctypes.c_int
     lib.sscan_backward.argtypes = [vp, vp, fp, vp, vp, fp, fp, vp, fp, vp, vp, fp, fp, fp, fp, fp,
                                    i64, i64, i64, i64, ctypes.c_int, vp]
     lib.sscan_backward.restype = ctypes.c_int
@@ -158,11 +162,7 @@ def _stream(stream, device) -> int:
     return s.cuda_stream if isinstance(s, torch.cuda.Stream) else int(s)
 
 
-def forward(x, delta, A, B, C, Dskip=None, y=None, final_state=None, stream=None,
-            initial_state=None):
-    """Whole-sequence selective scan; returns y (written into `y` when given).
-
-    initial_state: (batch, dim, N) fp32 state before the first token (default zero)."""
+def _forward(entry, x, delta, A, B, C, Dskip, y, final_state, stream, initial_state):
     batch, L, dim = x.shape
     N = A.shape[1]
     if delta.shape != x.shape or tuple(A.shape) != (dim, N) or B.shape != (batch, L, N) or C.shape != B.shape:
@@ -178,13 +178,31 @@ def forward(x, delta, A, B, C, Dskip=None, y=None, final_state=None, stream=None
         raise ValueError("final_state must have shape (batch, dim, N)")
     if initial_state is not None and tuple(initial_state.shape) != (batch, dim, N):
         raise ValueError("initial_state must have shape (batch, dim, N)")
-    rc = lib.sscan_forward_from_state(_dev(x, "x"), _dev(delta, "delta"), _dev(A, "A", torch.float32),
-                                      _dev(B, "B"), _dev(C, "C"), _dev(Dskip, "Dskip", torch.float32),
-                                      _dev(initial_state, "initial_state", torch.float32),
-                                      _dev(y, "y"), _dev(final_state, "final_state", torch.float32),
-                                      batch, L, dim, N, io, _stream(stream, x.device))
+    rc = entry(_dev(x, "x"), _dev(delta, "delta"), _dev(A, "A", torch.float32),
+               _dev(B, "B"), _dev(C, "C"), _dev(Dskip, "Dskip", torch.float32),
+               _dev(initial_state, "initial_state", torch.float32),
+               _dev(y, "y"), _dev(final_state, "final_state", torch.float32),
+               batch, L, dim, N, io, _stream(stream, x.device))
     _check(rc)
     return y
+
+
+def forward(x, delta, A, B, C, Dskip=None, y=None, final_state=None, stream=None,
+            initial_state=None):
+    """Whole-sequence selective scan; returns y (written into `y` when given).
+
+    initial_state: (batch, dim, N) fp32 state before the first token (default zero)."""
+    return _forward(lib.sscan_forward_from_state, x, delta, A, B, C, Dskip, y, final_state, stream,
+                    initial_state)
+
+
+def forward_noalloc(x, delta, A, B, C, Dskip=None, y=None, final_state=None, stream=None,
+                    initial_state=None):
+    """forward() through sscan_forward_noalloc: no device allocation (the library's static
+    per-GPU scratch, 64 MiB); pass y (and final_state) to allocate nothing at all.  Calls
+    that overlap on one GPU race (they share that scratch)."""
+    return _forward(lib.sscan_forward_noalloc, x, delta, A, B, C, Dskip, y, final_state, stream,
+                    initial_state)
 
 
 def _act_code(activation) -> int:

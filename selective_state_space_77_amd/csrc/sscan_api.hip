@@ -4,6 +4,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/sscan.h"
 #include "sscan_internal.h"
 
@@ -64,6 +66,53 @@ int check_ptrs(const Span *s, int n) {
     return SSCAN_OK;
 }
 
+// Scratch of sscan_forward_noalloc, for callers that cannot allocate: a file-scope
+// device array (every GPU the library runs on holds its own copy until the process
+// ends).  In host code `scratch` only names the symbol: kernels receive the
+// per-device address that hipGetSymbolAddress returns for it, looked up once per
+// device with that device current and kept in g_scratch_dev.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices];
+
+// The address of `scratch` on the device of `stream` (NULL stream: the current
+// device), or NULL with the status in *rc.
+void *noalloc_scratch(hipStream_t stream, int *rc) {
+    int cur = 0, dev = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess) e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        *rc = fail_hip("device of the stream", e);
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxDevices) {
+        *rc = fail(SSCAN_ERR_UNSUPPORTED, "device ordinal beyond the library's table");
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) {
+            *rc = fail_hip("hipSetDevice", e);
+            return nullptr;
+        }
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess || !p) {
+            *rc = fail_hip("hipGetSymbolAddress (static scratch)", e);
+            return nullptr;
+        }
+        g_scratch_dev[dev] = p;
+    }
+    return g_scratch_dev[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -118,7 +167,8 @@ struct FrontEnd {
 static int forward_impl(const void *x, const void *delta, const float *A, const void *B,
                         const void *C, const float *Dskip, const float *initial_state, void *y,
                         float *final_state, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
-                        int io_dtype, void *stream, const FrontEnd &fe = FrontEnd()) {
+                        int io_dtype, void *stream, const FrontEnd &fe = FrontEnd(),
+                        bool static_scratch = false) {
     g_last_error[0] = '\0';
     if (io_dtype != SSCAN_F32 && io_dtype != SSCAN_BF16)
         return fail(SSCAN_ERR_UNSUPPORTED, "io_dtype must be SSCAN_F32 or SSCAN_BF16");
@@ -165,12 +215,26 @@ static int forward_impl(const void *x, const void *delta, const float *A, const 
 
     const sscan::FwdPlan plan = sscan::plan_forward(batch, seqlen, dim, dstate, io_dtype);
     if (plan.reject) return fail(SSCAN_ERR_UNSUPPORTED, "%s", plan.reject);
-    void *ws = nullptr;
-    hipError_t e = hipMallocAsync(&ws, plan.ws_bytes, s);
-    if (e != hipSuccess) return fail_hip("hipMallocAsync (scratch)", e);
     sscan::FwdArgs a{x,   delta,  A,           B,      C,   Dskip,         initial_state,
                      y,   final_state, batch, seqlen, dim, int(dstate), io_dtype,
                      fa,  fe.conv_state_out};
+    if (static_scratch) {
+        // no allocation: the library's per-device scratch array (every byte a launch
+        // reads from it is written earlier in the same call, so nothing is cleared)
+        if (plan.ws_bytes > kNoAllocScratchBytes) {
+            char need[64];
+            snprintf(need, sizeof need, "%zu", plan.ws_bytes);
+            return fail(SSCAN_ERR_UNSUPPORTED, "needs %s bytes of scratch, above the static %s",
+                        need, "64 MiB");
+        }
+        void *ws = noalloc_scratch(s, &rc);
+        if (!ws) return rc;
+        const hipError_t el = sscan::launch_forward(a, plan, ws, s);
+        return el == hipSuccess ? SSCAN_OK : fail_hip("forward launch", el);
+    }
+    void *ws = nullptr;
+    hipError_t e = hipMallocAsync(&ws, plan.ws_bytes, s);
+    if (e != hipSuccess) return fail_hip("hipMallocAsync (scratch)", e);
     e = sscan::launch_forward(a, plan, ws, s);
     const hipError_t ef = hipFreeAsync(ws, s);
     if (e != hipSuccess) return fail_hip("forward launch", e);
@@ -191,6 +255,14 @@ int sscan_forward_from_state(const void *x, const void *delta, const float *A, c
                              int64_t dstate, int io_dtype, void *stream) {
     return forward_impl(x, delta, A, B, C, Dskip, initial_state, y, final_state, batch, seqlen, dim,
                         dstate, io_dtype, stream);
+}
+
+int sscan_forward_noalloc(const void *x, const void *delta, const float *A, const void *B,
+                          const void *C, const float *Dskip, const float *initial_state, void *y,
+                          float *final_state, int64_t batch, int64_t seqlen, int64_t dim,
+                          int64_t dstate, int io_dtype, void *stream) {
+    return forward_impl(x, delta, A, B, C, Dskip, initial_state, y, final_state, batch, seqlen, dim,
+                        dstate, io_dtype, stream, FrontEnd(), true);
 }
 
 int sscan_backward(const void *x, const void *delta, const float *A, const void *B, const void *C,

@@ -38,7 +38,8 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     assert _declared() == ["sscan_backward", "sscan_forward", "sscan_forward_from_state",
-                           "sscan_forward_fused", "sscan_forward_plan", "sscan_last_error", "sscan_ssd_forward",
+                           "sscan_forward_fused", "sscan_forward_noalloc", "sscan_forward_plan", "sscan_last_error",
+                           "sscan_ssd_forward",
                            "sscan_ssd_step", "sscan_status_string", "sscan_step", "sscan_step_fused",
                            "sscan_version"]
 

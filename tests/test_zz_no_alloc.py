@@ -1,0 +1,112 @@
+"""sscan_forward_noalloc (no device allocation: the library's static per-GPU scratch)
+through the C ABI: two calls in a row, the second smaller and on the other kernel path,
+each equal to sscan_forward_from_state on the same inputs; the size limit; replays of
+the call captured in a HIP graph."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+from oracle.compare import TOL, rel_err
+from tests.gpuutil import announce, oracle_threads, to_host, upload_scan
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import selective_state_space_77_amd as sscan  # noqa: E402
+
+
+def _call(entry, t, wl, h0, y, hs, stream):
+    io = 1 if wl.io == "bf16" else 0
+    p = lambda v: None if v is None else ctypes.c_void_p(v.data_ptr())
+    return entry(p(t["x"]), p(t["delta"]), p(t["A"]), p(t["B"]), p(t["C"]), p(t["Dskip"]), p(h0), p(y), p(hs),
+                 wl.batch, wl.seqlen, wl.dim, wl.dstate, io, ctypes.c_void_p(stream.cuda_stream))
+
+
+def _both(wl, seed_state):
+    """The same inputs through sscan_forward_noalloc and sscan_forward_from_state."""
+    inp = datagen.scan_inputs(wl)
+    t = upload_scan(inp, wl.io)
+    h0 = torch.from_numpy(np.random.default_rng(seed_state).standard_normal(
+        (wl.batch, wl.dim, wl.dstate)).astype(np.float32)).cuda()
+    s = torch.cuda.current_stream()
+    out = {}
+    for name, entry in (("noalloc", sscan.lib.sscan_forward_noalloc),
+                        ("from_state", sscan.lib.sscan_forward_from_state)):
+        y = torch.full_like(t["x"], float("nan"))
+        hs = torch.full((wl.batch, wl.dim, wl.dstate), float("nan"), device="cuda")
+        assert _call(entry, t, wl, h0, y, hs, s) == 0, sscan.lib.sscan_last_error()
+        out[name] = (y, hs)
+    torch.cuda.synchronize()
+    return inp, h0, out
+
+
+@pytest.mark.parametrize("order", ["large_then_small"])
+def test_two_calls_in_a_row_match_the_allocating_entry_point(order):
+    # 1st: 256 tiles of structured-real A, lockstep kernel (4 MiB of scratch)
+    big = datagen.custom("noalloc_big", 4, 2048, 4096, 16, "bf16", "s4d_real", key=90)
+    # 2nd, smaller: 2 tiles of random A, segment kernels with aggregates (reusing the same
+    # scratch, which holds the first call's contents)
+    small = datagen.custom("noalloc_small", 2, 777, 100, 16, "f32", "loguniform", key=91)
+    assert sscan.forward_plan(4, 2048, 4096, 16, "bf16")["kernel"] == "lockstep"
+    assert sscan.forward_plan(2, 777, 100, 16, "f32")["kernel"] == "segment"
+    for wl, seed in ((big, 1), (small, 2)):
+        announce(f"noalloc {wl.name}")
+        inp, h0, out = _both(wl, seed)
+        (y1, h1), (y2, h2) = out["noalloc"], out["from_state"]
+        assert torch.equal(y1, y2) and torch.equal(h1, h2), wl.name
+        if wl is small:  # and the oracle, on the small one
+            yr, hr = oracle.forward(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["Dskip"],
+                                    h0=h0.cpu().numpy(), nthreads=oracle_threads())
+            assert rel_err(to_host(y1), yr) <= TOL[wl.io]
+            assert rel_err(h1.cpu().numpy(), hr) <= TOL[wl.io]
+
+
+def test_a_call_needing_more_scratch_than_the_static_array_is_refused():
+    # 2^20 tokens of staged B/C rows (128 MiB) exceed the 64 MiB array; refused before
+    # anything is enqueued
+    wl = datagen.custom("noalloc_huge", 1, 1 << 20, 64, 16, "bf16", "s4d_real", key=92)
+    assert sscan.forward_plan(1, 1 << 20, 64, 16, "bf16")["scratch_bytes"] > 64 << 20
+    x = torch.zeros(1, 1 << 20, 64, dtype=torch.bfloat16, device="cuda")
+    bc = torch.zeros(1, 1 << 20, 16, dtype=torch.bfloat16, device="cuda")
+    A = -torch.arange(1, 17, dtype=torch.float32, device="cuda").repeat(64, 1)
+    with pytest.raises(sscan.SScanError) as e:
+        sscan.forward_noalloc(x, x.clone(), A, bc, bc.clone())
+    assert e.value.status == -3 and "scratch" in str(e.value)
+
+
+def test_captured_in_a_graph_and_replayed():
+    """The reason for the entry point: it can be captured (no allocation inside the
+    capture).  Three replays, with other work and synchronisation between them, each
+    equal to the eager call."""
+    wl = datagen.custom("noalloc_graph", 256, 300, 64, 16, "bf16", "s4d_real", key=93)
+    inp = datagen.scan_inputs(wl)
+    t = upload_scan(inp, wl.io)
+    y_e = sscan.forward(t["x"], t["delta"], t["A"], t["B"], t["C"], t["Dskip"])
+    h_e = torch.empty(wl.batch, wl.dim, wl.dstate, device="cuda")
+    sscan.forward(t["x"], t["delta"], t["A"], t["B"], t["C"], t["Dskip"], final_state=h_e)
+    y = torch.empty_like(t["x"])
+    hs = torch.empty(wl.batch, wl.dim, wl.dstate, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm-up outside the capture (resolves the scratch address)
+        sscan.forward_noalloc(t["x"], t["delta"], t["A"], t["B"], t["C"], t["Dskip"], y=y, final_state=hs,
+                              stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sscan.forward_noalloc(t["x"], t["delta"], t["A"], t["B"], t["C"], t["Dskip"], y=y, final_state=hs)
+    for k in range(3):
+        y.fill_(float("nan"))
+        hs.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_e) and torch.equal(hs, h_e), k
+        _ = (t["x"].float() * 2).sum().item()  # eager work between replays
