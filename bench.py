@@ -640,9 +640,13 @@ def main() -> int:
     hbm_gbs = nbytes / ev_avg / 1e9
     tflops = updates * FLOPS_PER_UPDATE / ev_avg / 1e12
     sq = f"k_lockstep_{wl.name}_sq_counters.md"
+    plan = sscan.forward_plan(wl.batch, wl.seqlen, wl.dim, wl.dstate, wl.io)
+    kname = ("k_lockstep (timed: the whole sscan_forward call on its stream; the lockstep kernel is ~99% "
+             "of it, the rest is the B/C staging launch)" if plan["kernel"] == "lockstep" else
+             f"k_seg, {plan['segments']} segments of {plan['seg_len']} tokens: aggregate and main passes "
+             f"(timed: the whole sscan_forward call on its stream)")
     roof = {
-        "kernel": "k_lockstep (timed: the whole sscan_forward call on its stream; the lockstep kernel is ~99% "
-                  "of it, the rest is the B/C staging launch)",
+        "kernel": kname,
         "bound": "alu",
         "achieved": round(tflops, 3),
         "peak": PEAK_VALU_TFLOPS,

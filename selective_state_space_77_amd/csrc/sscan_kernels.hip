@@ -739,47 +739,65 @@ __device__ __forceinline__ void ldrow(const uint16_t *p, float *o) {
 
 // One lane's SPL states of one channel (states n = q SPL + j, those >= N padded
 // with zeros): the state update, and the lane's part of the readout C.h.
+// The per-channel constants (which form the A row has, 1/A[d,0], the 1/(n+1) of
+// the lane's states) are formed once by init() and shared by every batch row the
+// thread updates.
 template <int SPL, int LPC>
-__device__ __forceinline__ float step_lane(int q, int N, float dt, float xv, float a0, const float *av,
-                                           const float *bv, const float *cv, float *h) {
-    // structured-real states (A[d,n] = (n+1) A[d,0], A[d,0] < 0, the form the scan
-    // kernels classify): one exp per lane, and with r = exp(delta A[d,0]) and
+struct StepLane {
+    bool sr;           // structured-real: A[d,n] = (n+1) A[d,0], A[d,0] < 0 for the lane's states
+    float a0, a2, ra;  // A[d,0], A[d,0] log2(e), -1/A[d,0]
+    float w[SPL];      // 1/(n+1) of the lane's states
+    int n0;            // the lane's first state
+
+    __device__ __forceinline__ void init(int q, int N, float a0_, const float *av) {
+        a0 = a0_;
+        a2 = a0 * kLog2e;
+        ra = -1.f / a0;
+        n0 = q * SPL;
+        sr = (a0 < 0.f) && (a0 > -INFINITY);
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) {
+            w[j] = inv_np1<SPL, LPC>(q, j);
+            if (n0 + j < N) sr = sr && (av[j] == a0 * float(n0 + j + 1));
+        }
+    }
+
+    // structured-real states: one exp per lane, and with r = exp(delta A[d,0]) and
     // q_n = 1 - r^(n+1) = r q_(n-1) + q_0,
     //     h_n <- h_n + q_n (B_n x / ((n+1) alpha) - h_n),  alpha = -A[d,0],
     // the update of the scan kernels on the unscaled state; other states take
     // the general form (an exp and the ZOH gain per state)
-    bool sr = (a0 < 0.f) && (a0 > -INFINITY);
+    __device__ __forceinline__ float row(float dt, float xv, const float *av, const float *bv,
+                                         const float *cv, float *h) const {
+        float yacc = 0.f;
+        if (sr) {
+            const float u = dt * a2;
+            const float r = exp2_hw(u);
+            const float q0 = one_minus_exp2(u, r);
+            // q_(n0-1) = 1 - r^n0 for this lane's first state n0
+            const float un = u * float(n0);
+            float qn = n0 == 0 ? 0.f : one_minus_exp2(un, exp2_hw(un));
+            const float xa = xv * ra;
 #pragma unroll
-    for (int j = 0; j < SPL; ++j)
-        if (q * SPL + j < N) sr = sr && (av[j] == a0 * float(q * SPL + j + 1));
-    float yacc = 0.f;
-    if (sr) {
-        const float z = dt * a0;
-        const float r = exp2_hw(z * kLog2e);
-        const float q0 = one_minus_exp(z, r);
-        // q_(n0-1) = 1 - r^n0 for this lane's first state n0
-        const float zn = z * float(q * SPL);
-        float qn = q == 0 ? 0.f : one_minus_exp(zn, exp2_hw(zn * kLog2e));
-        const float xa = xv / -a0;
+            for (int j = 0; j < SPL; ++j) {
+                qn = fmaf(qn, r, q0);
+                const float e = fmaf(bv[j] * w[j], xa, -h[j]);
+                h[j] = fmaf(qn, e, h[j]);
+                yacc = fmaf(cv[j], h[j], yacc);
+            }
+        } else {
 #pragma unroll
-        for (int j = 0; j < SPL; ++j) {
-            qn = fmaf(qn, r, q0);
-            const float e = fmaf(bv[j] * inv_np1<SPL, LPC>(q, j), xa, -h[j]);
-            h[j] = fmaf(qn, e, h[j]);
-            yacc = fmaf(cv[j], h[j], yacc);
+            for (int j = 0; j < SPL; ++j) {
+                const float z = dt * av[j];
+                const float abar = exp2_hw(dt * (av[j] * kLog2e));
+                const float g = zoh_gain(dt, av[j], z, abar);
+                h[j] = fmaf(abar, h[j], g * (bv[j] * xv));
+                yacc = fmaf(cv[j], h[j], yacc);
+            }
         }
-    } else {
-#pragma unroll
-        for (int j = 0; j < SPL; ++j) {
-            const float z = dt * av[j];
-            const float abar = exp2_hw(dt * (av[j] * kLog2e));
-            const float g = zoh_gain(dt, av[j], z, abar);
-            h[j] = fmaf(abar, h[j], g * (bv[j] * xv));
-            yacc = fmaf(cv[j], h[j], yacc);
-        }
+        return yacc;
     }
-    return yacc;
-}
+};
 
 // ----------------------------------------------------------------------------
 // Decode step: LPC lanes share one channel, each owning SPL consecutive states,
@@ -823,11 +841,31 @@ __global__ __launch_bounds__(256) void k_step(float *__restrict__ state,
         live[j] = active && b < batch;
         c[j] = (b < batch ? b : batch - 1) * dim + d;
     }
+    // the two lanes of a channel (adjacent lanes) load x and delta of different batch
+    // rows -- lane q rows q, 2+q, ... -- and swap them with a DPP move: one load
+    // instruction per two rows
+    constexpr bool kPairs = !FE && LPC == 2 && BT % 2 == 0;
     float xv[BT], dt[BT];
+    if constexpr (kPairs) {
+        auto swap = [](float v) {  // the value of the other lane of the pair
+            return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+        };
 #pragma unroll
-    for (int j = 0; j < BT; ++j) {
-        xv[j] = IO::ld(x, c[j]);
-        dt[j] = IO::ld(delta, c[j]);
+        for (int j = 0; j < BT; j += 2) {
+            const int64_t cq = min(bg * BT + j + q, batch - 1) * dim + d;
+            const float xo = IO::ld(x, cq), dto = IO::ld(delta, cq);
+            const float xn = swap(xo), dtn = swap(dto);
+            xv[j] = q ? xn : xo;
+            xv[j + 1] = q ? xo : xn;
+            dt[j] = q ? dtn : dto;
+            dt[j + 1] = q ? dto : dtn;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < BT; ++j) {
+            xv[j] = IO::ld(x, c[j]);
+            dt[j] = IO::ld(delta, c[j]);
+        }
     }
     // every load goes out at the start (a load issued after the readout would add a
     // second memory round trip to each wave's lifetime)
@@ -889,12 +927,15 @@ __global__ __launch_bounds__(256) void k_step(float *__restrict__ state,
             }
         }
     }
-    const float a0 = A[d * N];
+    StepLane<SPL, LPC> sl;
+    sl.init(q, N, A[d * N], av);
+    float yrow[BT];
 #pragma unroll
     for (int j = 0; j < BT; ++j) {
-        float yacc = step_lane<SPL, LPC>(q, N, dt[j], xv[j], a0, av, bv[j], cv[j], h[j]);
+        float yacc = sl.row(dt[j], xv[j], av, bv[j], cv[j], h[j]);
 #pragma unroll
         for (int off = LPC / 2; off >= 1; off /= 2) yacc += __shfl_xor(yacc, off, LPC);
+        yrow[j] = fmaf(dsk, xv[j], yacc);
         if (!live[j]) continue;
         float *sp = state + c[j] * N + q * SPL;
         if constexpr (kVec) {
@@ -906,7 +947,16 @@ __global__ __launch_bounds__(256) void k_step(float *__restrict__ state,
             for (int k = 0; k < SPL; ++k)
                 if (q * SPL + k < N) sp[k] = h[j][k];
         }
-        if (q == 0) y[c[j]] = IO::enc(fmaf(dsk, xv[j], yacc));
+        if (!kPairs && q == 0) y[c[j]] = IO::enc(yrow[j]);
+    }
+    if constexpr (kPairs) {
+        // both lanes of a channel hold every row's output: lane q stores rows q, 2+q, ...
+#pragma unroll
+        for (int j = 0; j < BT; j += 2) {
+            const int64_t b = bg * BT + j + q;
+            const float ya = yrow[j], yb = yrow[j + 1];
+            if (active && b < batch) y[b * dim + d] = IO::enc(q ? yb : ya);
+        }
     }
 }
 
