@@ -20,7 +20,7 @@ constexpr int kWave = 64;  // CDNA wavefront width: one lane per channel
 #define SSCAN_LOCK_T 16
 #endif
 #ifndef SSCAN_TARGET_WAVES
-#define SSCAN_TARGET_WAVES 4096
+#define SSCAN_TARGET_WAVES 32768
 #endif
 constexpr int kLockW = SSCAN_LOCK_W;
 constexpr int kLockT = SSCAN_LOCK_T;

@@ -23,8 +23,10 @@
 // no per-token product: the Abar of a diagonal mode multiply to exp(A*sum(delta)).
 //   k_lockstep: one workgroup of W waves per 64-channel tile; runs of a chunk
 //               are scanned locally, composed through LDS, and corrected.
-//   k_seg:      one wave per (tile, time segment); an aggregate pass and a
-//               main pass that folds the aggregates of earlier segments.
+//   k_seg:      one wave per (tile, time segment) scans its segment from
+//               zero; k_carry chains the segment end states into the state
+//               each segment really started from; k_segfix adds that state's
+//               decayed contribution to the segment's outputs.
 //
 // Structured-real fast path.  When every A row of a tile is
 // A[d,n] = (n+1)*A[d,0] with A[d,0] < 0, Abar_n = r^(n+1) with
@@ -145,29 +147,33 @@ __global__ __launch_bounds__(256) void k_conv_tail(const typename IO::T *__restr
 }
 
 // ----------------------------------------------------------------------------
-// Segment scan: one wave = 64 channels x one time segment.  kMain = false:
-// aggregate pass; kMain = true: carried-state scan with readout.  kFast picks
-// the structured-real (one exp per token) or general (exp and expm1 per state)
-// update; a wave whose tile flag says otherwise exits at once.
+// Segment kernels (shapes with too few 64-channel tiles to fill the chip with
+// the lockstep kernel): the sequence is cut into time segments and
+//   k_seg:    one wave per (tile, segment) scans its segment -- segment 0 from
+//             the state before token 0, every other one from zero -- stores
+//             its outputs and writes its aggregate (sum of delta, end state);
+//   k_carry:  per (batch row, state, channel), folds the aggregates in segment
+//             order with the associative combine (groups of segments composed
+//             through LDS), overwriting each with the state that enters the
+//             next segment, and writes the final state;
+//   k_segfix: one wave per (tile, segment >= 1) reads the state k_in its
+//             segment really started from and adds its contribution
+//             sum_n C_n Abar_n(segment start..t) k_in[n] to the stored outputs
+//             (2 operations per state and token, against 3 for a second pass
+//             over the recurrence).
+// The contribution decays with exp(A * (sum of delta since the segment start)):
+// on the structured-real path, once that decay is exactly 0 in every lane (and
+// k_in is finite) every later term is exactly 0 and the wave stops.
 constexpr int kUnroll = 8;  // tokens of x/delta prefetched ahead
 
-template <class IO, int NT, bool kMain, bool kFast, bool FE>
-__global__ __launch_bounds__(kWave) void k_seg(
+template <class IO, int NT, bool kFast, bool FE>
+__device__ __forceinline__ void seg_scan(
     const typename IO::T *__restrict__ x, const typename IO::T *__restrict__ delta,
     const float *__restrict__ A, const float *__restrict__ bc, const float *__restrict__ Dskip,
     const float *__restrict__ h0, typename IO::T *__restrict__ y, float *__restrict__ final_state,
-    float *__restrict__ agg_sum, float *__restrict__ agg_h, const int *__restrict__ tile_fast,
-    int64_t batch, int64_t L, int64_t dim, int N, int64_t seg_len, int segments,
-    int64_t tiles_per_batch, int64_t tiles, FeArgs fe) {
+    float *__restrict__ agg_sum, float *__restrict__ agg_h, int64_t batch, int64_t L, int64_t dim, int N,
+    int64_t seg_len, int segments, int seg, int64_t b, int64_t dbase, int lane, const FeArgs &fe) {
     using T = typename IO::T;
-    const int lane = threadIdx.x;
-    const int64_t wid = blockIdx.x;
-    const int seg = int(wid / tiles);
-    const int64_t tile = wid - int64_t(seg) * tiles;
-    const int64_t b = tile / tiles_per_batch;
-    const int64_t dt = tile - b * tiles_per_batch;
-    if ((tile_fast[dt] != 0) != kFast) return;
-    const int64_t dbase = dt * kWave;  // first channel of the wave
     const bool active = dbase + lane < dim;
     const int lo = active ? lane : int(dim - 1 - dbase);  // clamped lane offset
     const int64_t d = dbase + lo;
@@ -178,31 +184,10 @@ __global__ __launch_bounds__(kWave) void k_seg(
 #pragma unroll
     for (int n = 0; n < NT; ++n) a[n] = (n < N) ? A[d * N + n] : 0.f;
 
-    // ---- carried state at the segment start (pass 2 only): the state before
-    // token 0, then the aggregates of all earlier segments folded in with
-    // (a1,b1) o (a2,b2) = (a1*a2, a2*b1 + b2)
+    // segment 0 starts from the state before token 0, the others from zero
     float h[NT];
 #pragma unroll
-    for (int n = 0; n < NT; ++n) h[n] = (kMain && h0 && n < N) ? h0[(b * dim + d) * N + n] : 0.f;
-    if (kMain) {
-        for (int j = 0; j < seg; ++j) {
-            const int64_t cj = int64_t(j) * batch + b;
-            const float s = agg_sum[cj * dim + d];
-            if (kFast) {
-                const float rho = exp2_hw(a[0] * kLog2e * s);
-                float dec = rho;
-#pragma unroll
-                for (int n = 0; n < NT; ++n) {
-                    h[n] = fmaf(dec, h[n], agg_h[(cj * NT + n) * dim + d]);
-                    dec *= rho;
-                }
-            } else {
-#pragma unroll
-                for (int n = 0; n < NT; ++n)
-                    h[n] = fmaf(exp2_hw(a[n] * kLog2e * s), h[n], agg_h[(cj * NT + n) * dim + d]);
-            }
-        }
-    }
+    for (int n = 0; n < NT; ++n) h[n] = (seg == 0 && h0 && n < N) ? h0[(b * dim + d) * N + n] : 0.f;
 
     // Descriptors cover exactly this segment: tokens past its end read x = delta
     // = 0 (the state is left unchanged) and their stores are dropped, so the
@@ -216,9 +201,8 @@ __global__ __launch_bounds__(kWave) void k_seg(
     const int64_t seg_bytes = int64_t(nseg) * dim * ES;
     const rsrc_t rx = make_rsrc(x + (b * L + t0) * dim, seg_bytes);
     const rsrc_t rd = make_rsrc(delta + (b * L + t0) * dim, seg_bytes);
-    const rsrc_t ry = make_rsrc(kMain ? y + (b * L + t0) * dim : nullptr, kMain ? seg_bytes : 0);
+    const rsrc_t ry = make_rsrc(y + (b * L + t0) * dim, seg_bytes);
     const float *bc0 = bc + (b * L + t0) * (2 * NT);
-    const float dsk = (kMain && Dskip) ? Dskip[d] : 0.f;
     float dsum = 0.f;
 
     T xr[U], dr[U];
@@ -234,6 +218,8 @@ __global__ __launch_bounds__(kWave) void k_seg(
     const float alpha = -a[0];
     const float inv_alpha = 1.f / alpha;
     const float a2 = a[0] * kLog2e;
+    // the structured-real state is held scaled, k = alpha h
+    const float dska = (Dskip ? Dskip[d] : 0.f) * (kFast ? alpha : 1.f);
     float k[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) k[n] = kFast ? h[n] * alpha : h[n];
@@ -249,13 +235,13 @@ __global__ __launch_bounds__(kWave) void k_seg(
     // one token: structured-real update on the scaled state, or the general one;
     // sto is the token's output offset in the row stream
     auto token = [&](float xv, float dv, const float *row, uint32_t sto) {
-        float yacc = 0.f;
+        float yacc = dska * xv;
+        dsum += dv;
         if constexpr (kFast) {
             const float u = dv * a2;
             const float r = exp2_hw(u);
-            sr_update<NT>(r, one_minus_exp2(u, r), xv, row, k, [&](int n) {
-                if (kMain) yacc = fmaf(row[NT + n], k[n], yacc);
-            });
+            sr_update<NT>(r, one_minus_exp2(u, r), xv, row, k,
+                          [&](int n) { yacc = fmaf(row[NT + n], k[n], yacc); });
         } else {
 #pragma unroll
             for (int n = 0; n < NT; ++n) {
@@ -263,15 +249,10 @@ __global__ __launch_bounds__(kWave) void k_seg(
                 const float abar = exp2_hw(dv * (an * kLog2e));
                 const float g = zoh_gain(dv, an, dv * an, abar);
                 k[n] = fmaf(abar, k[n], g * ((row[n] * float(n + 1)) * xv));
-                if (kMain) yacc = fmaf(row[NT + n], k[n], yacc);
+                yacc = fmaf(row[NT + n], k[n], yacc);
             }
         }
-        if (kMain) {
-            const float yv = kFast ? fmaf(yacc, inv_alpha, dsk * xv) : fmaf(dsk, xv, yacc);
-            if (active) IO::bst(IO::enc(yv), ry, voff, sto);
-        } else {
-            dsum += dv;
-        }
+        if (active) IO::bst(IO::enc(kFast ? yacc * inv_alpha : yacc), ry, voff, sto);
     };
     for (int g0 = 0; g0 < nseg; g0 += U) {
         float xv[U], dv[U];
@@ -329,20 +310,247 @@ __global__ __launch_bounds__(kWave) void k_seg(
             sto += rowb;
         }
     }
-#pragma unroll
-    for (int n = 0; n < NT; ++n) h[n] = kFast ? k[n] * inv_alpha : k[n];
-
     if (!active) return;
-    if (!kMain) {
-        const int64_t cs = int64_t(seg) * batch + b;
-        agg_sum[cs * dim + d] = dsum;
+    if (segments == 1) {
+        // one segment: its end state is the final state
+        if (final_state) {
 #pragma unroll
-        for (int n = 0; n < NT; ++n) agg_h[(cs * NT + n) * dim + d] = h[n];
-    } else if (final_state && seg == segments - 1) {
-#pragma unroll
-        for (int n = 0; n < NT; ++n)
-            if (n < N) final_state[(b * dim + d) * N + n] = h[n];
+            for (int n = 0; n < NT; ++n)
+                if (n < N) final_state[(b * dim + d) * N + n] = kFast ? k[n] * inv_alpha : k[n];
+        }
+        return;
     }
+    const int64_t cs = int64_t(seg) * batch + b;
+    agg_sum[cs * dim + d] = dsum;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) agg_h[(cs * NT + n) * dim + d] = kFast ? k[n] * inv_alpha : k[n];
+}
+
+// one launch per A path (a wave of a tile of the other kind returns at once):
+// the general path's registers would otherwise set the fast path's occupancy
+template <class IO, int NT, bool kFast, bool FE>
+__global__ __launch_bounds__(kWave) void k_seg(
+    const typename IO::T *__restrict__ x, const typename IO::T *__restrict__ delta,
+    const float *__restrict__ A, const float *__restrict__ bc, const float *__restrict__ Dskip,
+    const float *__restrict__ h0, typename IO::T *__restrict__ y, float *__restrict__ final_state,
+    float *__restrict__ agg_sum, float *__restrict__ agg_h, const int *__restrict__ tile_fast,
+    int64_t batch, int64_t L, int64_t dim, int N, int64_t seg_len, int segments,
+    int64_t tiles_per_batch, int64_t tiles, FeArgs fe) {
+    const int lane = threadIdx.x;
+    const int64_t wid = blockIdx.x;
+    const int seg = int(wid / tiles);
+    const int64_t tile = wid - int64_t(seg) * tiles;
+    const int64_t b = tile / tiles_per_batch;
+    const int64_t dt = tile - b * tiles_per_batch;
+    if ((tile_fast[dt] != 0) != kFast) return;
+    seg_scan<IO, NT, kFast, FE>(x, delta, A, bc, Dskip, h0, y, final_state, agg_sum, agg_h, batch, L, dim, N,
+                                seg_len, segments, seg, b, dt * kWave, lane, fe);
+}
+
+// Carry pass: the aggregates of segment j (sum of delta, end state from zero,
+// unscaled) are folded in order, H <- exp(A[d,n] * sum_j) H + h_j, starting
+// from zero (segment 0 started from the state before token 0, so its end state
+// already holds it); aggregate j is overwritten with H, the state that enters
+// segment j+1, and the last H is the final state.
+// A workgroup takes 64 channels of one (batch row, state) and splits the
+// segments into kCarryG consecutive groups, one wave each: every wave folds its
+// group from zero, the group results are composed through LDS into the state
+// entering each group, and every wave walks its group again from that state,
+// storing the entering states (the second walk reads what the first brought
+// into L2).  The loads of kCarryU segments are issued ahead of their fold.
+constexpr int kCarryU = 8;
+constexpr int kCarryG = 16;
+
+__global__ __launch_bounds__(kCarryG *kWave) void k_carry(const float *__restrict__ A,
+                                                          const float *__restrict__ agg_sum,
+                                                          float *__restrict__ agg_h, float *__restrict__ final_state,
+                                                          int64_t batch, int64_t dim, int N, int nt, int segments) {
+    __shared__ float lsum[kCarryG][kWave], lh[kCarryG][kWave];
+    const int lane = threadIdx.x % kWave, g = threadIdx.x / kWave;
+    const int64_t tpb = (dim + kWave - 1) / kWave;
+    const int64_t blocks = batch * nt * tpb;
+    const int per = (segments + kCarryG - 1) / kCarryG;
+    const int j0 = min(segments, g * per), j1 = min(segments, j0 + per);
+    for (int64_t blk = blockIdx.x; blk < blocks; blk += gridDim.x) {
+        const int64_t dt = blk % tpb;
+        const int64_t bn = blk / tpb;
+        const int n = int(bn % nt);
+        const int64_t b = bn / nt;
+        const bool active = dt * kWave + lane < dim;
+        const int64_t d = active ? dt * kWave + lane : dim - 1;
+        const float an = n < N ? A[d * N + n] * kLog2e : 0.f;  // padded states: sums of zeros
+        // walk this wave's group from H; `store` writes each entering state
+        auto walk = [&](float H, float &ssum, bool store) {
+            for (int j = j0; j < j1; j += kCarryU) {
+                float sv[kCarryU], hv[kCarryU];
+#pragma unroll
+                for (int u = 0; u < kCarryU; ++u) {
+                    const int64_t cj = int64_t(min(j + u, j1 - 1)) * batch + b;
+                    sv[u] = agg_sum[cj * dim + d];
+                    hv[u] = agg_h[(cj * nt + n) * dim + d];
+                }
+#pragma unroll
+                for (int u = 0; u < kCarryU; ++u) {
+                    if (j + u < j1) {
+                        ssum += sv[u];
+                        H = fmaf(exp2_hw(an * sv[u]), H, hv[u]);
+                        if (store && active) agg_h[((int64_t(j + u) * batch + b) * nt + n) * dim + d] = H;
+                    }
+                }
+            }
+            return H;
+        };
+        float ssum = 0.f;
+        const float Hg = walk(0.f, ssum, false);
+        lsum[g][lane] = ssum;
+        lh[g][lane] = Hg;
+        __syncthreads();
+        float E = 0.f;  // the state entering this wave's group
+        for (int q = 0; q < g; ++q) E = fmaf(exp2_hw(an * lsum[q][lane]), E, lh[q][lane]);
+        float unused = 0.f;
+        const float H = walk(E, unused, true);
+        // the last group ends at the last segment (an empty group: E is the total)
+        if (g == kCarryG - 1 && active && n < N && final_state) final_state[(b * dim + d) * N + n] = H;
+        __syncthreads();  // LDS reused by the next block of the loop
+    }
+}
+
+template <class IO, int NT, bool kFast, bool FE>
+__device__ __forceinline__ void seg_fix(
+    const typename IO::T *__restrict__ delta, const float *__restrict__ A, const float *__restrict__ bc,
+    typename IO::T *__restrict__ y, const float *__restrict__ carried, int64_t batch, int64_t L,
+    int64_t dim, int N, int64_t seg_len, int seg, int64_t b, int64_t dbase, int lane, const FeArgs &fe) {
+    using T = typename IO::T;
+    const bool active = dbase + lane < dim;
+    const int lo = active ? lane : int(dim - 1 - dbase);
+    const int64_t d = dbase + lo;
+    float a[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) a[n] = (n < N) ? A[d * N + n] : 0.f;
+    // the state entering this segment, from the carry pass
+    const int64_t cs = int64_t(seg - 1) * batch + b;
+    float kin[NT];
+    const float alpha = -a[0];
+    const float inv_alpha = 1.f / alpha;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        const float h = carried[(cs * NT + n) * dim + d];
+        kin[n] = kFast ? h * alpha : h;
+    }
+    // early exit needs k_in finite in every lane (an infinite or NaN entering
+    // state keeps adding to the outputs however small the decay)
+    bool fin = true;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) fin = fin && (fabsf(kin[n]) <= 3.402823466e38f);
+    const bool may_stop = kFast && __all(fin);
+
+    constexpr int ES = IO::kBytes;
+    constexpr int U = kUnroll;
+    const int64_t t0 = int64_t(seg) * seg_len;
+    const int nseg = int(min(L, t0 + seg_len) - t0);
+    const int last = nseg - 1;
+    const uint32_t voff = uint32_t((dbase + lane) * ES);
+    const uint32_t voff_st = active ? voff : 0x80000000u;  // lanes past dim: beyond every range
+    const uint32_t rowb = uint32_t(dim * ES);
+    const int64_t seg_bytes = int64_t(nseg) * dim * ES;
+    const rsrc_t rd = make_rsrc(delta + (b * L + t0) * dim, seg_bytes);
+    const rsrc_t ry = make_rsrc(y + (b * L + t0) * dim, seg_bytes);
+    const float *cc0 = bc + (b * L + t0) * (2 * NT) + NT;
+    const float a2 = a[0] * kLog2e;
+    float db = 0.f;
+    if constexpr (FE) db = fe.delta_bias ? fe.delta_bias[d] : 0.f;
+    float rho = 1.f, cum = 0.f;  // decay / sum of delta since the segment start
+
+    // the step sizes and stored outputs of a group of U tokens are loaded one group
+    // ahead of their use
+    T dr[U], yr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        dr[u] = IO::bld(rd, voff, uint32_t(u) * rowb);
+        yr[u] = IO::bld(ry, voff, uint32_t(u) * rowb);
+    }
+    float cA[NT], cB[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) cA[n] = cc0[n];
+    auto fix = [&](float dv, float yl, const float *crow, uint32_t sto) {
+        float corr;
+        if constexpr (kFast) {
+            rho *= exp2_hw(dv * a2);
+            float acc = crow[NT - 1] * kin[NT - 1];
+#pragma unroll
+            for (int n = NT - 2; n >= 0; --n) acc = fmaf(acc, rho, crow[n] * kin[n]);
+            corr = acc * rho * inv_alpha;
+        } else {
+            cum += dv;
+            corr = 0.f;
+#pragma unroll
+            for (int n = 0; n < NT; ++n) corr = fmaf(crow[n] * kin[n], exp2_hw((a[n] * kLog2e) * cum), corr);
+        }
+        IO::bst(IO::enc(yl + corr), ry, voff_st, sto);
+    };
+    for (int g0 = 0; g0 < nseg; g0 += U) {
+        uint32_t sy = uint32_t(g0) * rowb, sl = uint32_t(g0 + U) * rowb;
+        asm volatile("" : "+s"(sy), "+s"(sl));
+        float dv[U], yv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if constexpr (FE)
+                dv[u] = softplus_f(IO::cvt(dr[u]) + db);  // tokens past the end: never stored
+            else
+                dv[u] = IO::cvt(dr[u]);
+            yv[u] = IO::cvt(yr[u]);
+        }
+        // the next group's loads
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            dr[u] = IO::bld(rd, voff, sl);
+            yr[u] = IO::bld(ry, voff, sl);
+            sl += rowb;
+        }
+        uint32_t sto = sy;
+#pragma unroll
+        for (int u = 0; u < U; u += 2) {
+            const int tau = g0 + u;
+            __builtin_amdgcn_sched_barrier(0);
+            wait_scalar_loads();
+            {
+                const float *rn = cc0 + min(tau + 1, last) * (2 * NT);
+#pragma unroll
+                for (int n = 0; n < NT; ++n) cB[n] = rn[n];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            fix(dv[u], yv[u], cA, sto);
+            sto += rowb;
+            __builtin_amdgcn_sched_barrier(0);
+            wait_scalar_loads();
+            {
+                const float *rn = cc0 + min(tau + 2, last) * (2 * NT);
+#pragma unroll
+                for (int n = 0; n < NT; ++n) cA[n] = rn[n];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            fix(dv[u + 1], yv[u + 1], cB, sto);
+            sto += rowb;
+        }
+        // every later contribution is exactly zero once the decay is
+        if (may_stop && !__any(rho != 0.f)) break;
+    }
+}
+
+template <class IO, int NT, bool kFast, bool FE>
+__global__ __launch_bounds__(kWave) void k_segfix(
+    const typename IO::T *__restrict__ delta, const float *__restrict__ A, const float *__restrict__ bc,
+    typename IO::T *__restrict__ y, const float *__restrict__ carried, const int *__restrict__ tile_fast, int64_t batch, int64_t L,
+    int64_t dim, int N, int64_t seg_len, int64_t tiles_per_batch, int64_t tiles, FeArgs fe) {
+    const int lane = threadIdx.x;
+    const int64_t wid = blockIdx.x;
+    const int seg = 1 + int(wid / tiles);  // segments 1 .. segments-1
+    const int64_t tile = wid - int64_t(seg - 1) * tiles;
+    const int64_t b = tile / tiles_per_batch;
+    const int64_t dt = tile - b * tiles_per_batch;
+    if ((tile_fast[dt] != 0) != kFast) return;
+    seg_fix<IO, NT, kFast, FE>(delta, A, bc, y, carried, batch, L, dim, N, seg_len, seg, b, dt * kWave, lane,
+                               fe);
 }
 
 // ----------------------------------------------------------------------------
@@ -1006,11 +1214,6 @@ hipError_t forward_t(const FwdArgs &a, const FwdPlan &p, void *ws, hipStream_t s
     const T *x = static_cast<const T *>(a.x), *dl = static_cast<const T *>(a.delta);
     T *y = static_cast<T *>(a.y);
     prep_t<IO, NT>(a.B, a.C, a.A, bc, flags, a.batch * a.L, a.dim, a.N, s);
-    const dim3 seg_agg(unsigned((p.segments - 1) * p.tiles)), seg_main(unsigned(p.segments * p.tiles));
-#define SSCAN_SEG(MAIN, FAST, GRID)                                                                 \
-    hipLaunchKernelGGL((k_seg<IO, NT, MAIN, FAST, FE>), GRID, dim3(kWave), 0, s, x, dl, a.A, bc,       \
-                       a.Dskip, a.h0, y, a.final_state, agg_sum, agg_h, flags, a.batch, a.L, a.dim,    \
-                       a.N, p.seg_len, p.segments, p.tiles_per_batch, p.tiles, a.fe)
     if (p.lockstep) {
         // every tile in one launch (the general-A tiles take their own path in it);
         // the fused variant too: with the token loop free of register copies it fits
@@ -1019,13 +1222,28 @@ hipError_t forward_t(const FwdArgs &a, const FwdPlan &p, void *ws, hipStream_t s
                            0, s, x, dl, a.A, bc, a.Dskip, a.h0, y, a.final_state, flags, int(a.L), a.dim, a.N,
                            p.tiles_per_batch, a.fe);
     } else {
-        // general-A tiles, then structured-real tiles (waves of the other kind exit at once)
-        if (p.segments > 1) SSCAN_SEG(false, false, seg_agg);
-        SSCAN_SEG(true, false, seg_main);
-        if (p.segments > 1) SSCAN_SEG(false, true, seg_agg);
-        SSCAN_SEG(true, true, seg_main);
-    }
+        // every segment from its own start, then the segments after the first
+        // corrected for the state they really started from
+#define SSCAN_SEG(FAST)                                                                                   \
+    hipLaunchKernelGGL((k_seg<IO, NT, FAST, FE>), dim3(unsigned(p.segments * p.tiles)), dim3(kWave), 0, s, x, dl,  \
+                       a.A, bc, a.Dskip, a.h0, y, a.final_state, agg_sum, agg_h, flags, a.batch, a.L, a.dim,     \
+                       a.N, p.seg_len, p.segments, p.tiles_per_batch, p.tiles, a.fe)
+#define SSCAN_SEGFIX(FAST)                                                                                \
+    hipLaunchKernelGGL((k_segfix<IO, NT, FAST, FE>), dim3(unsigned((p.segments - 1) * p.tiles)), dim3(kWave),   \
+                       0, s, dl, a.A, bc, y, agg_h, flags, a.batch, a.L, a.dim, a.N, p.seg_len,               \
+                       p.tiles_per_batch, p.tiles, a.fe)
+        SSCAN_SEG(true);
+        SSCAN_SEG(false);
+        if (p.segments > 1) {
+            const int64_t blocks = std::min<int64_t>(a.batch * NT * p.tiles_per_batch, kMaxStrideBlocks / 16);
+            hipLaunchKernelGGL(k_carry, dim3(unsigned(blocks)), dim3(kCarryG * kWave), 0, s, a.A, agg_sum, agg_h,
+                               a.final_state, a.batch, a.dim, a.N, NT, p.segments);
+            SSCAN_SEGFIX(true);
+            SSCAN_SEGFIX(false);
+        }
 #undef SSCAN_SEG
+#undef SSCAN_SEGFIX
+    }
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && FE && a.conv_state_out)
         e = launch_conv_tail(a.x, a.fe, a.conv_state_out, a.batch, a.L, a.dim, a.io, s);
@@ -1102,7 +1320,9 @@ FwdPlan plan_forward(int64_t batch, int64_t L, int64_t dim, int64_t N, int io) {
         return p;
     }
     const int64_t seg_max = rowb > 0 ? kMaxDescBytes / rowb : L;  // tokens per segment, at most
-    // Enough segments for ~4 waves per SIMD (1024 SIMDs) with segments of >= 64
+    // Enough segments for ~32 waves per SIMD (1024 SIMDs), several rounds of
+    // waves, so that waves of uneven speed even out before the launch ends (a
+    // segment costs one aggregate in the carry pass), with segments of >= 64
     // tokens, and at least as many as the descriptor span needs.
     const int64_t target_waves = kTargetWaves;
     int64_t S = p.tiles > 0 ? (target_waves + p.tiles - 1) / p.tiles : 1;
