@@ -166,6 +166,17 @@ __global__ __launch_bounds__(256) void k_conv_tail(const typename IO::T *__restr
 // k_in is finite) every later term is exactly 0 and the wave stops.
 constexpr int kUnroll = 8;  // tokens of x/delta prefetched ahead
 
+// Workgroups are handed to the 8 XCDs in turn (workgroup i to XCD i mod 8), and
+// each XCD has its own L2.  The segment kernels renumber them so that XCD x
+// takes the x-th eighth of the (segment, tile) order, in order: the tiles of one
+// segment run on one XCD at about the same time and read each B/C row from that
+// XCD's L2 instead of each fetching it.  (Launches not a multiple of 8 keep the
+// plain order.)
+constexpr int kXcds = 8;
+__device__ __forceinline__ int64_t xcd_order(int64_t wid, int64_t n) {
+    return n % kXcds == 0 ? (wid % kXcds) * (n / kXcds) + wid / kXcds : wid;
+}
+
 template <class IO, int NT, bool kFast, bool FE>
 __device__ __forceinline__ void seg_scan(
     const typename IO::T *__restrict__ x, const typename IO::T *__restrict__ delta,
@@ -337,7 +348,7 @@ __global__ __launch_bounds__(kWave) void k_seg(
     int64_t batch, int64_t L, int64_t dim, int N, int64_t seg_len, int segments,
     int64_t tiles_per_batch, int64_t tiles, FeArgs fe) {
     const int lane = threadIdx.x;
-    const int64_t wid = blockIdx.x;
+    const int64_t wid = xcd_order(blockIdx.x, gridDim.x);
     const int seg = int(wid / tiles);
     const int64_t tile = wid - int64_t(seg) * tiles;
     const int64_t b = tile / tiles_per_batch;
@@ -427,16 +438,11 @@ __device__ __forceinline__ void seg_fix(
     float a[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) a[n] = (n < N) ? A[d * N + n] : 0.f;
-    // the state entering this segment, from the carry pass
+    // the state entering this segment (unscaled), from the carry pass
     const int64_t cs = int64_t(seg - 1) * batch + b;
     float kin[NT];
-    const float alpha = -a[0];
-    const float inv_alpha = 1.f / alpha;
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-        const float h = carried[(cs * NT + n) * dim + d];
-        kin[n] = kFast ? h * alpha : h;
-    }
+    for (int n = 0; n < NT; ++n) kin[n] = carried[(cs * NT + n) * dim + d];
     // early exit needs k_in finite in every lane (an infinite or NaN entering
     // state keeps adding to the outputs however small the decay)
     bool fin = true;
@@ -479,7 +485,7 @@ __device__ __forceinline__ void seg_fix(
             float acc = crow[NT - 1] * kin[NT - 1];
 #pragma unroll
             for (int n = NT - 2; n >= 0; --n) acc = fmaf(acc, rho, crow[n] * kin[n]);
-            corr = acc * rho * inv_alpha;
+            corr = acc * rho;
         } else {
             cum += dv;
             corr = 0.f;
@@ -543,7 +549,7 @@ __global__ __launch_bounds__(kWave) void k_segfix(
     typename IO::T *__restrict__ y, const float *__restrict__ carried, const int *__restrict__ tile_fast, int64_t batch, int64_t L,
     int64_t dim, int N, int64_t seg_len, int64_t tiles_per_batch, int64_t tiles, FeArgs fe) {
     const int lane = threadIdx.x;
-    const int64_t wid = blockIdx.x;
+    const int64_t wid = xcd_order(blockIdx.x, gridDim.x);
     const int seg = 1 + int(wid / tiles);  // segments 1 .. segments-1
     const int64_t tile = wid - int64_t(seg - 1) * tiles;
     const int64_t b = tile / tiles_per_batch;
