@@ -639,12 +639,16 @@ def main() -> int:
     updates = wl.elements * wl.dstate
     hbm_gbs = nbytes / ev_avg / 1e9
     tflops = updates * FLOPS_PER_UPDATE / ev_avg / 1e12
-    sq = f"k_lockstep_{wl.name}_sq_counters.md"
     plan = sscan.forward_plan(wl.batch, wl.seqlen, wl.dim, wl.dstate, wl.io)
+    lock = plan["kernel"] == "lockstep"
+    # counter summaries: the lockstep kernel, or the segment path's kernels of one call together
+    prof = f"k_lockstep_{wl.name}" if lock else f"k_seg_{wl.name}"
+    sq = f"{prof}_sq_counters.md"
     kname = ("k_lockstep (timed: the whole sscan_forward call on its stream; the lockstep kernel is ~99% "
-             "of it, the rest is the B/C staging launch)" if plan["kernel"] == "lockstep" else
-             f"k_seg, {plan['segments']} segments of {plan['seg_len']} tokens: aggregate and main passes "
-             f"(timed: the whole sscan_forward call on its stream)")
+             "of it, the rest is the B/C staging launch)" if lock else
+             f"k_seg + k_carry + k_segfix, {plan['segments']} segments of {plan['seg_len']} tokens: scan "
+             f"from zero, carry of the segment end states, correction of the outputs (timed: the whole "
+             f"sscan_forward call on its stream; traffic and VALU figures cover all kernels of one call)")
     roof = {
         "kernel": kname,
         "bound": "alu",
@@ -652,7 +656,7 @@ def main() -> int:
         "peak": PEAK_VALU_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(tflops / PEAK_VALU_TFLOPS, 4),
-        "traffic": recorded_traffic(f"k_lockstep_{wl.name}_hbm_counters.md", FWD_SOURCES),
+        "traffic": recorded_traffic(f"{prof}_hbm_counters.md", FWD_SOURCES),
         "per_launch": {"updates": updates, "flops_per_update": FLOPS_PER_UPDATE,
                        "algorithmic_bytes": nbytes, "event_avg_us": round(ev_avg * 1e6, 2),
                        "event_min_us": round(float(durs.min()) * 1e6, 2),
