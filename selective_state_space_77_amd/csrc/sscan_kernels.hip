@@ -1055,59 +1055,10 @@ __global__ __launch_bounds__(256) void k_step(float *__restrict__ state,
         live[j] = active && b < batch;
         c[j] = (b < batch ? b : batch - 1) * dim + d;
     }
-    // the two lanes of a channel (adjacent lanes) load x and delta of different batch
-    // rows -- lane q rows q, 2+q, ... -- and swap them with a DPP move: one load
-    // instruction per two rows
-    constexpr bool kPairs = !FE && LPC == 2 && BT % 2 == 0;
-    float xv[BT], dt[BT];
-    if constexpr (kPairs) {
-        auto swap = [](float v) {  // the value of the other lane of the pair
-            return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
-        };
-#pragma unroll
-        for (int j = 0; j < BT; j += 2) {
-            const int64_t cq = min(bg * BT + j + q, batch - 1) * dim + d;
-            const float xo = IO::ld(x, cq), dto = IO::ld(delta, cq);
-            const float xn = swap(xo), dtn = swap(dto);
-            xv[j] = q ? xn : xo;
-            xv[j + 1] = q ? xo : xn;
-            dt[j] = q ? dtn : dto;
-            dt[j + 1] = q ? dto : dtn;
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < BT; ++j) {
-            xv[j] = IO::ld(x, c[j]);
-            dt[j] = IO::ld(delta, c[j]);
-        }
-    }
-    // every load goes out at the start (a load issued after the readout would add a
-    // second memory round trip to each wave's lifetime)
-    const float dsk = Dskip ? Dskip[d] : 0.f;
-    if constexpr (FE) {
-        // carried raw inputs of this channel: row r of conv_state is the token
-        // K-1-r before this one
-        const int64_t b = c[0] / dim;
-        const int rows = fe.K - 1;
-        T cr[kMaxConv - 1];
-#pragma unroll
-        for (int r = 0; r < kMaxConv - 1; ++r) cr[r] = r < rows ? conv_state[(b * rows + r) * dim + d] : T(0);
-        auto back = [&](int j) {  // raw input of token t-j (selects: no indexed local array)
-            const int r = rows - j;
-            return r == 0 ? IO::cvt(cr[0]) : r == 1 ? IO::cvt(cr[1]) : r == 2 ? IO::cvt(cr[2]) : 0.f;
-        };
-        FeLane fl;
-        fl.init(fe, d);
-        const T xraw = x[c[0]];
-        xv[0] = fl.u(back(3), back(2), back(1), xv[0]);
-        dt[0] = fl.delta(dt[0]);
-        if (active && q == 0) {
-#pragma unroll
-            for (int r = 0; r < kMaxConv - 1; ++r)
-                if (r < rows) conv_state[(b * rows + r) * dim + d] = r + 1 < rows ? cr[r + 1] : xraw;
-        }
-    }
-
+    // Every load goes out at the start, the state, A, B and C rows first and x and delta
+    // last: a wait for x (the swaps below, the front end) then comes after every load
+    // has been issued.  (A load issued after that wait, or after the readout, would put
+    // a second memory round trip in each wave's lifetime.)
     float h[BT][SPL], av[SPL], bv[BT][SPL], cv[BT][SPL];
     if constexpr (kVec) {
         // N == NT (a multiple of 4), 16-byte aligned state and A, B and C rows
@@ -1141,8 +1092,85 @@ __global__ __launch_bounds__(256) void k_step(float *__restrict__ state,
             }
         }
     }
+    const float a0 = A[d * N];
+    const float dsk = Dskip ? Dskip[d] : 0.f;
+    // front end: the carried raw inputs of this channel, row r of conv_state being the
+    // token K-1-r before this one
+    // (rows past K-1 repeat the last one, so the loads take no branch, and with no carried
+    // rows, where conv_state may be NULL, they read x; neither is ever used)
+    T cr[kMaxConv - 1];
+    if constexpr (FE) {
+        const int64_t b = c[0] / dim;
+        const int rows = fe.K - 1;
+        const T *cs = rows > 0 ? conv_state : x;
+        const int64_t rb = b * rows;
+#pragma unroll
+        for (int r = 0; r < kMaxConv - 1; ++r) cr[r] = cs[(rb + min(r, max(rows - 1, 0))) * dim + d];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // the two lanes of a channel (adjacent lanes) load x and delta of different batch
+    // rows -- lane q rows q, 2+q, ... -- and swap them with a DPP move: one load
+    // instruction per two rows
+    constexpr bool kPairs = !FE && LPC == 2 && BT % 2 == 0;
+    float xv[BT], dt[BT];
+    T xraw = T(0);
+    if constexpr (kPairs) {
+        auto swap = [](float v) {  // the value of the other lane of the pair
+            return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+        };
+        T xr[BT / 2], dr[BT / 2];  // raw: converted after the barrier, so no load waits for one
+#pragma unroll
+        for (int j = 0; j < BT; j += 2) {
+            const int64_t cq = min(bg * BT + j + q, batch - 1) * dim + d;
+            xr[j / 2] = x[cq];
+            dr[j / 2] = delta[cq];
+        }
+        // the swaps wait for these loads: every other load is already in flight
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < BT; j += 2) {
+            const float xo = IO::cvt(xr[j / 2]), dto = IO::cvt(dr[j / 2]);
+            const float xn = swap(xo), dtn = swap(dto);
+            xv[j] = q ? xn : xo;
+            xv[j + 1] = q ? xo : xn;
+            dt[j] = q ? dtn : dto;
+            dt[j + 1] = q ? dto : dtn;
+        }
+    } else {
+        T xr[BT], dr[BT];
+#pragma unroll
+        for (int j = 0; j < BT; ++j) {
+            xr[j] = x[c[j]];
+            dr[j] = delta[c[j]];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        xraw = xr[0];  // the front end carries the raw input
+#pragma unroll
+        for (int j = 0; j < BT; ++j) {
+            xv[j] = IO::cvt(xr[j]);
+            dt[j] = IO::cvt(dr[j]);
+        }
+    }
+    if constexpr (FE) {
+        const int64_t b = c[0] / dim;
+        const int rows = fe.K - 1;
+        auto back = [&](int j) {  // raw input of token t-j (selects: no indexed local array)
+            const int r = rows - j;
+            return r == 0 ? IO::cvt(cr[0]) : r == 1 ? IO::cvt(cr[1]) : r == 2 ? IO::cvt(cr[2]) : 0.f;
+        };
+        FeLane fl;
+        fl.init(fe, d);
+        xv[0] = fl.u(back(3), back(2), back(1), xv[0]);
+        dt[0] = fl.delta(dt[0]);
+        if (active && q == 0) {
+#pragma unroll
+            for (int r = 0; r < kMaxConv - 1; ++r)
+                if (r < rows) conv_state[(b * rows + r) * dim + d] = r + 1 < rows ? cr[r + 1] : xraw;
+        }
+    }
+
     StepLane<SPL, LPC> sl;
-    sl.init(q, N, A[d * N], av);
+    sl.init(q, N, a0, av);
     float yrow[BT];
 #pragma unroll
     for (int j = 0; j < BT; ++j) {
@@ -1176,10 +1204,16 @@ __global__ __launch_bounds__(256) void k_step(float *__restrict__ state,
 
 
 // states per lane of the decode step (N above it: several lanes per channel)
-constexpr int kStepSpl = 8;
+#ifndef SSCAN_STEP_SPL
+#define SSCAN_STEP_SPL 8
+#endif
+constexpr int kStepSpl = SSCAN_STEP_SPL;
 // batch rows per thread of the decode step without the front end (they share the
 // channel's A row and Dskip, and a wave keeps that many rows of state in flight)
-constexpr int kStepBt = 4;
+#ifndef SSCAN_STEP_BT
+#define SSCAN_STEP_BT 4
+#endif
+constexpr int kStepBt = SSCAN_STEP_BT;
 
 int round_nt(int64_t N) { return N <= 1 ? 1 : N <= 2 ? 2 : N <= 4 ? 4 : N <= 8 ? 8 : 16; }
 
