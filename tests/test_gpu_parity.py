@@ -264,6 +264,25 @@ def test_non_finite_inputs_propagate_like_the_oracle():
     assert rel_err(y[ok], yr[ok]) <= TOL["f32"]
 
 
+@pytest.mark.parametrize("a_init", ["s4d_real", "loguniform"])
+def test_infinite_input_makes_its_channel_non_finite_like_the_oracle(a_init):
+    """An infinite x makes the channel's state infinite from that token on.  The oracle's
+    update Abar h + Bbar x keeps +-Inf; the structured-real update k + q (w - k) gives
+    Inf - Inf = NaN on the next token (a state that is not finite either way), so what is
+    compared is where the results are finite, and the finite values."""
+    wl = datagen.custom("inf", 1, 400, 64, 16, "f32", a_init, key=18)
+    inp = datagen.scan_inputs(wl)
+    inp["x"][0, 150, 3] = np.inf
+    t = upload_scan(inp, "f32")
+    y, hs = _run(t, wl)
+    yr, hr = oracle.forward(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["Dskip"])
+    np.testing.assert_array_equal(np.isfinite(y), np.isfinite(yr))
+    np.testing.assert_array_equal(np.isfinite(hs), np.isfinite(hr))
+    assert not np.isfinite(yr[0, 150:, 3]).any() and np.isfinite(yr[0, :150, 3]).all()
+    ok = np.isfinite(yr)
+    assert rel_err(y[ok], yr[ok]) <= TOL["f32"]
+
+
 def test_run_to_run_bitwise_determinism():
     wl = datagen.custom("det", 2, 3000, 256, 16, "bf16", "s4d_real", key=13)
     t = upload_scan(datagen.scan_inputs(wl), "bf16")
