@@ -312,6 +312,10 @@ STATE_SHAPES = [
     (2, 700, 100, 8, "bf16", "loguniform"),   # segment kernels, general A
     (256, 300, 64, 16, "bf16", "s4d_real"),   # lockstep kernel
     (1, 20000, 64, 16, "f32", "s4d_real"),    # ~300 segments
+    # segment counts that leave groups of the carry kernel (16 per workgroup) partly
+    # filled or empty: 17 segments (groups of 2: nine used), 33 (groups of 3: eleven)
+    (2, 64 * 17, 96, 16, "f32", "s4d_real"),
+    (3, 64 * 33 + 5, 130, 16, "bf16", "loguniform"),
 ]
 
 
