@@ -312,12 +312,19 @@ int sscan_ssd_step(float *state, const void *x_t, const void *delta_t, const flo
  * bytes, and the segment kernels cut the sequence so that a segment's rows span
  * below 2^31 bytes; a launch has fewer than 2^32 work items.
  *
+ * Testing hook: with the environment variable SSCAN_FORCE_SEGMENTS=n (n > 0) set,
+ * every forward of the process plans the segment path with n segments (at most one
+ * per token, at least what the descriptor bound needs), so that one shape can be
+ * scanned through differently cut decompositions and the results compared; unset
+ * or 0, the plan is automatic.  It is read at each call.
+ *
  *   batch, seqlen, dim, dstate, io_dtype  as for sscan_forward.
  *   out          [out] the plan (host memory, caller-owned).
  * Returns SSCAN_OK, or a negative sscan_status with *out zeroed.
  */
 #define SSCAN_PLAN_LOCKSTEP 1 /* one workgroup per 64-channel tile over the whole sequence */
-#define SSCAN_PLAN_SEGMENT 2  /* one wave per (64-channel tile, time segment), two passes   */
+#define SSCAN_PLAN_SEGMENT 2  /* one wave per (64-channel tile, time segment): a scan from  */
+                              /* zero, a carry of the segment end states, a correction      */
 typedef struct {
     int32_t kernel;        /* SSCAN_PLAN_LOCKSTEP or SSCAN_PLAN_SEGMENT                    */
     int32_t segments;      /* time segments per tile (1 for the lockstep kernel)           */

@@ -32,6 +32,8 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsscan.so")
+# debug build of the same sources: every kernel fills its LDS with NaN before use
+POISON_LIB_PATH = os.path.join(_HERE, "libsscan_poison.so")
 
 F32, BF16 = 0, 1
 MAX_DSTATE = 16
@@ -58,11 +60,14 @@ class PlanInfo(ctypes.Structure):
 PLAN_KERNEL = {1: "lockstep", 2: "segment"}
 
 
-def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+def _load(path: str = None) -> ctypes.CDLL:
+    """Load the library (or another build of it, such as the LDS-poison debug build) and
+    declare its entry points."""
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run __graft_entry__.build() "
                           "(hipcc --offload-arch=gfx950)")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     vp, fp, i64 = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64
     lib.sscan_forward.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i64, i64, i64, i64, ctypes.c_int, vp]
     lib.sscan_forward.restype = ctypes.c_int

@@ -12,6 +12,8 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsscan.so")
+# debug build: every kernel fills its LDS with NaN before use (tests/test_gpu_debug.py)
+POISON_LIB = os.path.join(HERE, "libsscan_poison.so")
 SOURCES = [os.path.join(CSRC, f) for f in ("sscan_api.hip", "sscan_kernels.hip", "sscan_bwd.hip", "sscan_ssd.hip")]
 ARCH = "gfx950"
 
@@ -48,5 +50,10 @@ def build(out: str = LIB, extra: list[str] | None = None, verbose: bool = False)
     return out
 
 
+def build_all(verbose: bool = False) -> list[str]:
+    """The library and its LDS-poison debug build, both compiled from the same sources."""
+    return [build(LIB, verbose=verbose), build(POISON_LIB, ["-DSSCAN_LDS_POISON=1"], verbose=verbose)]
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build_all(verbose=True))

@@ -311,6 +311,7 @@ __global__ __launch_bounds__(BW *kWave) void k_bwd(
     // barrier, before any wave writes it
     float(*s_red)[2 * NT][kWave] = reinterpret_cast<float(*)[2 * NT][kWave]>(&s_pm[0][0][0][0]);
     static_assert(sizeof(s_pm) == sizeof(float) * BW * 2 * NT * kWave, "reduction buffer");
+    lds_poison(s_sum, s_k, s_q, s_pm);
 
     const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
     const int lane = int(threadIdx.x) % kWave;

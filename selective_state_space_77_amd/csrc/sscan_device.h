@@ -13,6 +13,26 @@ constexpr float kLog2e = 1.44269504088896340736f;
 
 __device__ __forceinline__ float exp2_hw(float v) { return __builtin_amdgcn_exp2f(v); }
 
+// Debug build (SSCAN_LDS_POISON=1, libsscan_poison.so): every kernel that uses LDS
+// first fills it with a NaN pattern (0x7FC07FC0: a quiet NaN as fp32 and as each of
+// its two bf16 halves) and waits at a barrier, so a read of LDS that nothing wrote
+// turns into NaN outputs instead of a stale value from an earlier workgroup.  Called
+// by every thread of the workgroup, before any early exit.  No-op otherwise.
+#ifndef SSCAN_LDS_POISON
+#define SSCAN_LDS_POISON 0
+#endif
+template <class... Ts>
+__device__ __forceinline__ void lds_poison(Ts &...arrays) {
+    if constexpr (SSCAN_LDS_POISON != 0) {
+        auto fill = [](void *p, size_t bytes) {
+            uint32_t *w = static_cast<uint32_t *>(p);
+            for (size_t i = threadIdx.x; i < bytes / 4; i += blockDim.x) w[i] = 0x7FC07FC0u;
+        };
+        (fill(static_cast<void *>(&arrays), sizeof(arrays)), ...);
+        __syncthreads();
+    }
+}
+
 // s_waitcnt lgkmcnt(0) alone (gfx9 encoding: vmcnt and expcnt fields left at
 // their "no wait" maxima).  Scalar loads return out of order, so the only wait
 // for one is lgkmcnt(0); issuing it before the next token's loads makes that

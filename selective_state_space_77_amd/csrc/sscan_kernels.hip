@@ -40,6 +40,7 @@
 // general path (exp2 and the ZOH gain per state).
 
 #include <math.h>
+#include <cstdlib>
 #include <type_traits>
 
 #include "sscan_device.h"
@@ -377,6 +378,7 @@ __global__ __launch_bounds__(kCarryG *kWave) void k_carry(const float *__restric
                                                           float *__restrict__ agg_h, float *__restrict__ final_state,
                                                           int64_t batch, int64_t dim, int N, int nt, int segments) {
     __shared__ float lsum[kCarryG][kWave], lh[kCarryG][kWave];
+    lds_poison(lsum, lh);
     const int lane = threadIdx.x % kWave, g = threadIdx.x / kWave;
     const int64_t tpb = (dim + kWave - 1) / kWave;
     const int64_t blocks = batch * nt * tpb;
@@ -893,6 +895,7 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
     const float *__restrict__ h0, typename IO::T *__restrict__ y, float *__restrict__ final_state,
     const int *__restrict__ tile_fast, int L, int64_t dim, int N, int64_t tiles_per_batch, FeArgs fe) {
     __shared__ LockLds<NT, W> sh;
+    lds_poison(sh);
     const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
     const int lane = int(threadIdx.x) % kWave;
     const int64_t tile = blockIdx.x;
@@ -1368,6 +1371,13 @@ FwdPlan plan_forward(int64_t batch, int64_t L, int64_t dim, int64_t N, int io) {
     int64_t S = p.tiles > 0 ? (target_waves + p.tiles - 1) / p.tiles : 1;
     S = std::min<int64_t>(S, std::max<int64_t>(1, L / 64));
     S = std::max<int64_t>(1, std::min<int64_t>(S, 4096));
+    // Test hook: SSCAN_FORCE_SEGMENTS=n (n > 0) sends every shape down the segment path
+    // with n segments (at most one per token, and at least as many as the descriptor
+    // bound below needs), so that one shape can be scanned through differently cut
+    // decompositions and the results compared with each other.
+    int64_t force = 0;
+    if (const char *e = std::getenv("SSCAN_FORCE_SEGMENTS")) force = std::max<long long>(0, std::atoll(e));
+    if (force > 0) S = std::min<int64_t>(force, std::max<int64_t>(1, L));
     S = std::max<int64_t>(S, seg_max > 0 ? (L + seg_max - 1) / seg_max : 1);
     p.seg_len = L > 0 ? (L + S - 1) / S : 1;
     p.segments = L > 0 ? int(std::min<int64_t>((L + p.seg_len - 1) / p.seg_len, 0x7FFFFFFF)) : 1;
@@ -1379,7 +1389,7 @@ FwdPlan plan_forward(int64_t batch, int64_t L, int64_t dim, int64_t N, int io) {
     // Its buffer offsets reach (W*TS + kUnroll) rows past a run start (keep them
     // below 2^31), its token arithmetic is 32-bit (L < 2^31), and its launch is
     // tiles x W*64 work items.
-    p.lockstep = p.tiles >= kLockMinTiles && (int64_t(kLockW) * kLockT + kUnroll) * rowb <= kMaxDescBytes &&
+    p.lockstep = force == 0 && p.tiles >= kLockMinTiles && (int64_t(kLockW) * kLockT + kUnroll) * rowb <= kMaxDescBytes &&
                  L < (int64_t(1) << 31) && p.tiles <= kMaxWorkItems / (kLockW * kWave);
     size_t off = 0;
     p.off_bc = off;

@@ -107,6 +107,7 @@ __global__ __launch_bounds__(SWV *kWave) void k_ssd(
     __shared__ float sS[SP][NS + 4];    // state entering the chunk, [channel][state]
     __shared__ float sCum[SQ], sGain[SQ], sW[SQ], sE[SQ];
     __shared__ float sDec;
+    lds_poison(sX, sBt, sS, sCum, sGain, sW, sE, sDec);
 
     const int tid = int(threadIdx.x);
     const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -385,6 +386,7 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
     // per-token scalars, two sets: those of chunk c + 1 are formed during chunk c
     __shared__ __align__(16) float sCum[2][SQ], sGain[2][SQ], sW[2][SQ], sE[2][SQ];
     __shared__ float sDec[2];
+    lds_poison(sX, sXWh, sXWl, sB, sC, sSh, sSl, sGh, sGl, sCum, sGain, sW, sE, sDec);
 
     const int tid = int(threadIdx.x);
     const int v = __builtin_amdgcn_readfirstlane(tid / kWave);

@@ -87,6 +87,23 @@ def test_named_workloads_take_the_expected_kernels(sscan):
     assert long1m["kernel"] == "segment" and long1m["tiles"] == 32
 
 
+def test_forced_segment_counts(sscan, monkeypatch):
+    """SSCAN_FORCE_SEGMENTS=n takes the segment path with n segments (at most one per
+    token, at least what the descriptor bound needs); unset or 0, the plan is automatic."""
+    for n in (1, 7, 33, 300):
+        monkeypatch.setenv("SSCAN_FORCE_SEGMENTS", str(n))
+        p = sscan.forward_plan(3, 3000, 4096, 16, "f32")
+        assert p["kernel"] == "segment" and p["segments"] == n, (n, p)
+        assert (p["segments"] - 1) * p["seg_len"] < 3000 <= p["segments"] * p["seg_len"]
+    monkeypatch.setenv("SSCAN_FORCE_SEGMENTS", "5000")
+    assert sscan.forward_plan(1, 100, 64, 16, "f32")["segments"] == 100   # one per token at most
+    monkeypatch.setenv("SSCAN_FORCE_SEGMENTS", "1")
+    p = sscan.forward_plan(1, 2**20, 12160, 16, "f32")                    # the descriptor bound wins
+    assert p["segments"] >= 23 and p["seg_len"] * 12160 * 4 <= MAX_DESC
+    monkeypatch.setenv("SSCAN_FORCE_SEGMENTS", "0")
+    assert sscan.forward_plan(4, 8192, 4096, 16, "bf16")["kernel"] == "lockstep"
+
+
 def test_the_previously_unbounded_segment_shapes_are_now_split_finer(sscan):
     # 190 tiles: ~22 segments by occupancy alone, which would give 2.3 GB segments
     p = sscan.forward_plan(1, 2**20, 12160, 16, "f32")
