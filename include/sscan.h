@@ -118,11 +118,14 @@ int sscan_forward_from_state(const void *x, const void *delta, const float *A, c
  * time on one GPU (on different streams, or from several threads) race and give
  * wrong results; serialise them.  Nothing in the array needs to start at zero.
  *
- *   Arguments and results exactly as for sscan_forward_from_state.
+ *   Arguments and results exactly as for sscan_forward_from_state; on the segment
+ *   path it may cut the sequence into fewer segments than sscan_forward_plan
+ *   reports, so that their aggregates fit the array (the same result to rounding).
  * Returns SSCAN_ERR_UNSUPPORTED, before anything is enqueued, when the call needs more
- * than 64 MiB of scratch (sscan_forward_plan reports scratch_bytes: 128 bytes per
- * (batch row, token) at dstate 9..16, fewer below, plus the segment aggregates of the
- * segment kernels), or SSCAN_ERR_HIP if the array's address cannot be obtained.
+ * than 64 MiB of scratch even so (sscan_forward_plan reports the allocating call's
+ * scratch_bytes: 128 bytes per (batch row, token) at dstate 9..16, fewer below, plus
+ * the segment aggregates of the segment kernels), or SSCAN_ERR_HIP if the array's
+ * address cannot be obtained.
  */
 int sscan_forward_noalloc(const void *x, const void *delta, const float *A, const void *B,
                           const void *C, const float *Dskip, const float *initial_state, void *y,

@@ -213,7 +213,8 @@ static int forward_impl(const void *x, const void *delta, const float *A, const 
         return e == hipSuccess ? SSCAN_OK : fail_hip("state copy launch", e);
     }
 
-    const sscan::FwdPlan plan = sscan::plan_forward(batch, seqlen, dim, dstate, io_dtype);
+    const sscan::FwdPlan plan =
+        sscan::plan_forward(batch, seqlen, dim, dstate, io_dtype, static_scratch ? kNoAllocScratchBytes : 0);
     if (plan.reject) return fail(SSCAN_ERR_UNSUPPORTED, "%s", plan.reject);
     sscan::FwdArgs a{x,   delta,  A,           B,      C,   Dskip,         initial_state,
                      y,   final_state, batch, seqlen, dim, int(dstate), io_dtype,

@@ -71,8 +71,9 @@ struct FwdPlan {
     size_t ws_bytes;          // scratch: [B/(n+1), C] rows, tile flags, segment aggregates
 };
 
-// io: 0 fp32, 1 bf16 (the element size of x, delta and y sets the segment spans)
-FwdPlan plan_forward(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io);
+// io: 0 fp32, 1 bf16 (the element size of x, delta and y sets the segment spans);
+// max_ws > 0: a scratch budget the segment path is fitted to where it can be
+FwdPlan plan_forward(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io, size_t max_ws = 0);
 
 struct FwdArgs {
     const void *x, *delta;

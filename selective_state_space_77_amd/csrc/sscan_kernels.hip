@@ -1348,7 +1348,7 @@ hipError_t step_io(const StepArgs &a, hipStream_t s) {
 
 }  // namespace
 
-FwdPlan plan_forward(int64_t batch, int64_t L, int64_t dim, int64_t N, int io) {
+FwdPlan plan_forward(int64_t batch, int64_t L, int64_t dim, int64_t N, int io, size_t max_ws) {
     FwdPlan p{};
     p.nt = round_nt(N);
     p.tiles_per_batch = (dim + kWave - 1) / kWave;
@@ -1378,19 +1378,35 @@ FwdPlan plan_forward(int64_t batch, int64_t L, int64_t dim, int64_t N, int io) {
     int64_t force = 0;
     if (const char *e = std::getenv("SSCAN_FORCE_SEGMENTS")) force = std::max<long long>(0, std::atoll(e));
     if (force > 0) S = std::min<int64_t>(force, std::max<int64_t>(1, L));
-    S = std::max<int64_t>(S, seg_max > 0 ? (L + seg_max - 1) / seg_max : 1);
+    const int64_t s_min = seg_max > 0 ? (L + seg_max - 1) / seg_max : 1;  // the descriptor bound
+    S = std::max<int64_t>(S, s_min);
+    // Lockstep kernel when the tiles alone give at least one wave per SIMD.
+    // Its buffer offsets reach (W*TS + kUnroll) rows past a run start (keep them
+    // below 2^31), its token arithmetic is 32-bit (L < 2^31), and its launch is
+    // tiles x W*64 work items.
+    const bool lockstep = force == 0 && p.tiles >= kLockMinTiles &&
+                          (int64_t(kLockW) * kLockT + kUnroll) * rowb <= kMaxDescBytes && L < (int64_t(1) << 31) &&
+                          p.tiles <= kMaxWorkItems / (kLockW * kWave);
+    // A fixed scratch budget (the no-allocation entry point): on the segment path,
+    // fewer segments when their aggregates would not fit beside the staged B/C rows,
+    // never fewer than the descriptor bound needs (a shape that still does not fit is
+    // refused by the caller).
+    if (max_ws > 0 && !lockstep) {
+        const size_t fixed = align256(size_t(batch) * L * 2 * p.nt * sizeof(float)) +
+                             align256(size_t(p.tiles_per_batch) * sizeof(int)) + 512;  // + the aggregates' alignment
+        const size_t per_seg = size_t(batch) * dim * (1 + p.nt) * sizeof(float);
+        if (fixed < max_ws && per_seg > 0) {
+            const int64_t fit = int64_t(std::min<size_t>((max_ws - fixed) / per_seg, size_t(1) << 40));
+            S = std::max<int64_t>(s_min, std::min<int64_t>(S, std::max<int64_t>(fit, 1)));
+        }
+    }
     p.seg_len = L > 0 ? (L + S - 1) / S : 1;
     p.segments = L > 0 ? int(std::min<int64_t>((L + p.seg_len - 1) / p.seg_len, 0x7FFFFFFF)) : 1;
     if (p.seg_len > seg_max || p.tiles > kMaxWorkItems / (int64_t(p.segments) * kWave)) {
         p.reject = "shape too large for the segment kernels' launch";
         return p;
     }
-    // Lockstep kernel when the tiles alone give at least one wave per SIMD.
-    // Its buffer offsets reach (W*TS + kUnroll) rows past a run start (keep them
-    // below 2^31), its token arithmetic is 32-bit (L < 2^31), and its launch is
-    // tiles x W*64 work items.
-    p.lockstep = force == 0 && p.tiles >= kLockMinTiles && (int64_t(kLockW) * kLockT + kUnroll) * rowb <= kMaxDescBytes &&
-                 L < (int64_t(1) << 31) && p.tiles <= kMaxWorkItems / (kLockW * kWave);
+    p.lockstep = lockstep;
     size_t off = 0;
     p.off_bc = off;
     off += align256(size_t(batch) * L * 2 * p.nt * sizeof(float));

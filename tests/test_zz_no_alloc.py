@@ -1,7 +1,8 @@
 """sscan_forward_noalloc (no device allocation: the library's static per-GPU scratch)
 through the C ABI: two calls in a row, the second smaller and on the other kernel path,
-each equal to sscan_forward_from_state on the same inputs; the size limit; replays of
-the call captured in a HIP graph."""
+each equal to sscan_forward_from_state on the same inputs; a segment count fitted to the
+static array where the allocating call would plan more; the size limit; replays of the
+call captured in a HIP graph."""
 import ctypes
 
 import numpy as np
@@ -65,6 +66,23 @@ def test_two_calls_in_a_row_match_the_allocating_entry_point(order):
                                     h0=h0.cpu().numpy(), nthreads=oracle_threads())
             assert rel_err(to_host(y1), yr) <= TOL[wl.io]
             assert rel_err(h1.cpu().numpy(), hr) <= TOL[wl.io]
+
+
+def test_segment_count_fitted_to_the_static_array():
+    """64 tiles, segment path: the allocating call plans ~256 segments, whose aggregates
+    need more than the 64 MiB array; the no-allocation call plans fewer segments so that
+    they fit, and its result matches the oracle (and the allocating call's, to rounding)."""
+    wl = datagen.custom("noalloc_fit", 1, 16384, 4096, 16, "bf16", "s4d_real", key=93)
+    plan = sscan.forward_plan(wl.batch, wl.seqlen, wl.dim, wl.dstate, wl.io)
+    assert plan["kernel"] == "segment" and plan["scratch_bytes"] > 64 << 20, plan
+    announce(f"noalloc {wl.name}: the allocating plan needs {plan['scratch_bytes']} bytes")
+    inp, h0, out = _both(wl, 3)
+    yr, hr = oracle.forward(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["Dskip"],
+                            h0=h0.cpu().numpy(), nthreads=oracle_threads())
+    for name, (y, hs) in out.items():
+        ey, eh = rel_err(to_host(y), yr), rel_err(hs.cpu().numpy(), hr)
+        announce(f"  {name}: err(y)={ey:.2e} err(h)={eh:.2e}")
+        assert ey <= TOL[wl.io] and eh <= TOL[wl.io], name
 
 
 def test_a_call_needing_more_scratch_than_the_static_array_is_refused():
