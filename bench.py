@@ -231,23 +231,24 @@ def _upload(wl, t, dev):
 
 
 def _time(call, steps, warmup, stream):
-    """W untimed calls, then exactly K timed calls with HIP events on the launch stream.
-    Returns (wall seconds per call, event seconds per call: mean, min)."""
+    """W untimed calls, then exactly K timed calls back to back, between one pair of HIP
+    events on the launch stream and a synchronisation on each side.  (The GPU's clock ramps
+    up over its first tens of milliseconds of work, which is what the warmup covers; events
+    recorded around every call slowed the calls by about 3%, so there are none in between.)
+    Returns (wall seconds per call, event seconds per call)."""
     import torch
     for _ in range(warmup):
         call()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for e0, e1 in ev:
-        e0.record(stream)
+    e0.record(stream)
+    for _ in range(steps):
         call()
-        e1.record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    durs = np.array([e0.elapsed_time(e1) for e0, e1 in ev]) * 1e-3
-    return wall, float(durs.mean()), float(durs.min())
+    return wall, e0.elapsed_time(e1) * 1e-3 / steps
 
 
 def cpu_baseline_backward(wl, target_s: float = 10.0) -> dict:
@@ -287,7 +288,7 @@ def bench_backward(wl, args, dev) -> int:
     stream = torch.cuda.current_stream(dev)
     print(f"[bench] backward {wl.name}: batch={wl.batch} L={wl.seqlen} dim={wl.dim} N={wl.dstate} "
           f"io={wl.io}", file=sys.stderr, flush=True)
-    wall, ev_avg, ev_min = _time(
+    wall, ev_avg = _time(
         lambda: sscan.backward(x, delta, A, B, C, dy, Dskip=D, dfinal_state=dhT, stream=stream),
         args.steps, args.warmup, stream)
     if args.calib_copy:
@@ -314,8 +315,7 @@ def bench_backward(wl, args, dev) -> int:
                      "traffic": recorded_traffic(f"k_bwd_{wl.name}_hbm_counters.md", BWD_SOURCES),
                      "per_launch": {"updates": updates, "flops_per_update": FLOPS_PER_UPDATE_BWD,
                                     "algorithmic_bytes": nbytes,
-                                    "event_avg_us": round(ev_avg * 1e6, 2),
-                                    "event_min_us": round(ev_min * 1e6, 2)},
+                                    "event_avg_us": round(ev_avg * 1e6, 2)},
                      "hbm": {"achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                              "frac": round(gbs / PEAK_HBM_GBS, 4)}},
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_backward(wl)}), flush=True)
@@ -345,7 +345,7 @@ def bench_fused(wl, args, dev) -> int:
     stream = torch.cuda.current_stream(dev)
     print(f"[bench] fused {wl.name}: batch={wl.batch} L={wl.seqlen} dim={wl.dim} N={wl.dstate} "
           f"io={wl.io} d_conv={D_CONV} silu", file=sys.stderr, flush=True)
-    wall, ev_avg, ev_min = _time(
+    wall, ev_avg = _time(
         lambda: sscan.forward_fused(x, cw, draw, A, B, C, D, conv_bias=cb, delta_bias=db,
                                     activation="silu", conv_state=cs, y=y, final_state=hs,
                                     conv_state_out=cso, stream=stream),
@@ -372,8 +372,7 @@ def bench_fused(wl, args, dev) -> int:
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_VALU_TFLOPS, 4),
                      "traffic": recorded_traffic(f"k_lockstep_fused_{wl.name}_hbm_counters.md", FWD_SOURCES),
                      "per_launch": {"updates": updates, "flops": flops, "algorithmic_bytes": nbytes,
-                                    "event_avg_us": round(ev_avg * 1e6, 2),
-                                    "event_min_us": round(ev_min * 1e6, 2)},
+                                    "event_avg_us": round(ev_avg * 1e6, 2)},
                      "hbm": {"achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                              "frac": round(gbs / PEAK_HBM_GBS, 4)}},
         "cpu_baseline": None}), flush=True)
@@ -398,7 +397,7 @@ def bench_ssd(wl, args, dev) -> int:
     stream = torch.cuda.current_stream(dev)
     print(f"[bench] ssd {wl.name}: batch={wl.batch} L={wl.seqlen} heads={wl.nheads} P={wl.headdim} "
           f"groups={wl.ngroups} N={wl.dstate} io={wl.io}", file=sys.stderr, flush=True)
-    wall, ev_avg, ev_min = _time(
+    wall, ev_avg = _time(
         lambda: sscan.ssd_forward(x, delta, A, B, C, D, y=y, final_state=hs, stream=stream),
         args.steps, args.warmup, stream)
     if args.calib_copy:
@@ -427,8 +426,7 @@ def bench_ssd(wl, args, dev) -> int:
                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": recorded_traffic(f"k_ssd_{wl.name}_hbm_counters.md", SSD_SOURCES),
                      "per_launch": {"algorithmic_bytes": nbytes, "matrix_flops": flops,
-                                    "event_avg_us": round(ev_avg * 1e6, 2),
-                                    "event_min_us": round(ev_min * 1e6, 2)},
+                                    "event_avg_us": round(ev_avg * 1e6, 2)},
                      "mfma": {"achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                               "frac": round(tflops / PEAK_BF16_TFLOPS, 4)}},
         "cpu_baseline": None}), flush=True)
@@ -467,8 +465,8 @@ def bench_step(wl, args, dev) -> int:
         for k in range(S):
             sscan.step(states[k % 4 if rotate else 0], X[k], Dl[k], A, Bs[k], Cs[k], D, y_t=Y[k], stream=stream)
 
-    wall, ev_avg, ev_min = _time(lambda: run(False), args.steps, args.warmup, stream)
-    _, rot_avg, _ = _time(lambda: run(True), max(1, args.steps // 4), 1, stream)
+    wall, ev_avg = _time(lambda: run(False), args.steps, args.warmup, stream)
+    _, rot_avg = _time(lambda: run(True), max(1, args.steps // 4), 1, stream)
     copy_gbs = copy_bandwidth(dev)
     per_call = ev_avg / S
     elems = wl.batch * wl.dim
@@ -492,8 +490,7 @@ def bench_step(wl, args, dev) -> int:
                              "achieved counts algorithmic bytes over fabric; state_rotated is the rate "
                              "with four state buffers (336 MB) used in turn",
                      "traffic": recorded_traffic(f"k_step_{wl.name}_hbm_counters.md", FWD_SOURCES),
-                     "per_launch": {"algorithmic_bytes": nbytes, "event_avg_us": round(per_call * 1e6, 2),
-                                    "event_min_us_per_call": round(ev_min / S * 1e6, 2)},
+                     "per_launch": {"algorithmic_bytes": nbytes, "event_avg_us": round(per_call * 1e6, 2)},
                      "state_rotated": {"achieved": round(rot_gbs, 1), "frac": round(rot_gbs / PEAK_HBM_GBS, 4),
                                        "event_avg_us": round(rot_avg / S * 1e6, 2)}},
         "cpu_baseline": None}), flush=True)
@@ -520,21 +517,14 @@ def bench_ssd_step(wl, args, dev) -> int:
     stream = torch.cuda.current_stream(dev)
     print(f"[bench] ssd decode {wl.name}: batch={wl.batch} heads={wl.nheads} P={wl.headdim} "
           f"groups={wl.ngroups} N={wl.dstate} io={wl.io}", file=sys.stderr, flush=True)
-    for k in range(args.warmup):
-        j = k % nstage
+    count = [0]
+
+    def one():  # the next staged token's inputs
+        j = count[0] % nstage
+        count[0] += 1
         sscan.ssd_step(state, X[j], Dl[j], A, Bs[j], Cs[j], D, y_t=Y[j], stream=stream)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k, (e0, e1) in enumerate(ev):
-        j = k % nstage
-        e0.record(stream)
-        sscan.ssd_step(state, X[j], Dl[j], A, Bs[j], Cs[j], D, y_t=Y[j], stream=stream)
-        e1.record(stream)
-    torch.cuda.synchronize()
-    per_step = (time.perf_counter() - t0) / args.steps
-    ev_avg = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e-3
+
+    per_step, ev_avg = _time(one, args.steps, args.warmup, stream)
     es = 2 if wl.io == "bf16" else 4
     chans = wl.batch * wl.nheads * wl.headdim
     nbytes = (2 * chans * wl.dstate * 4 + 2 * chans * es + wl.batch * wl.nheads * es
@@ -560,7 +550,8 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps first: the GPU's clock ramps up over its first tens of ms of work")
     ap.add_argument("--workload", default="mamba1p4b_bf16")
     ap.add_argument("--pass", dest="which", choices=("forward", "backward", "fused"), default="forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -609,24 +600,8 @@ def main() -> int:
     def step():
         sscan.forward(x, delta, A, B, C, D, y=y, final_state=hs, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # ---- timed region: exactly K steps, HIP events on the launch stream around each call
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for e0, e1 in ev:
-        e0.record(stream)
-        step()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    durs = np.array([e0.elapsed_time(e1) for e0, e1 in ev]) * 1e-3  # seconds
-    per_step = wall / args.steps
-    ev_avg = float(durs.mean())
+    # ---- timed region: W warmup steps, then exactly K steps back to back
+    per_step, ev_avg = _time(step, args.steps, args.warmup, stream)
 
     if args.calib_copy:
         _calib_copy(dev)
@@ -659,7 +634,6 @@ def main() -> int:
         "traffic": recorded_traffic(f"{prof}_hbm_counters.md", FWD_SOURCES),
         "per_launch": {"updates": updates, "flops_per_update": FLOPS_PER_UPDATE,
                        "algorithmic_bytes": nbytes, "event_avg_us": round(ev_avg * 1e6, 2),
-                       "event_min_us": round(float(durs.min()) * 1e6, 2),
                        "cold_median_us": round(cold_med * 1e6, 2), "cold_min_us": round(cold_min * 1e6, 2),
                        "cold_runs": COLD_RUNS, "flush_bytes": FLUSH_BYTES},
         "hbm": {"achieved": round(hbm_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
