@@ -603,7 +603,11 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
                     off[u] = mfma32(off[u], sl, cb);
                 }
             }
+            // the score tiles gate every wave's next phase: their waves take a raised issue
+            // priority while they compute them, so that their matrix and LDS work goes first
+            __builtin_amdgcn_s_setprio(2);
             score_tile(ktile, par);
+            __builtin_amdgcn_s_setprio(0);
             if (v == kScalarWave) scalars(Pn, par ^ 1);
             __syncthreads();  // scores and scalars in LDS; every read of S_in, B, C, w x done
 
@@ -661,7 +665,11 @@ __global__ __launch_bounds__(BTH) void k_ssd_bf(
         auto chunk = [&](int c, int par, Chunk &Pn) {
             // ---- phase A: waves 8 and 9 a score tile, then S = exp(A sum delta) S +
             // B^T diag(w) X
-            if (ktile >= 0) score_tile(ktile, par);
+            if (ktile >= 0) {
+                __builtin_amdgcn_s_setprio(2);  // as on the output waves
+                score_tile(ktile, par);
+                __builtin_amdgcn_s_setprio(0);
+            }
             const float dec = sDec[par];
 #pragma unroll
             for (int i = 0; i < NBW; ++i) S[i] *= dec;
