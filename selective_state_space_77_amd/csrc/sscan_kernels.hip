@@ -168,11 +168,14 @@ __global__ __launch_bounds__(256) void k_conv_tail(const typename IO::T *__restr
 constexpr int kUnroll = 8;  // tokens of x/delta prefetched ahead
 
 // Workgroups are handed to the 8 XCDs in turn (workgroup i to XCD i mod 8), and
-// each XCD has its own L2.  The segment kernels renumber them so that XCD x
-// takes the x-th eighth of the (segment, tile) order, in order: the tiles of one
-// segment run on one XCD at about the same time and read each B/C row from that
-// XCD's L2 instead of each fetching it.  (Launches not a multiple of 8 keep the
-// plain order.)
+// each XCD has its own L2.  The forward kernels renumber them so that XCD x
+// takes the x-th eighth of the logical order, in order: the tiles of one segment
+// (segment kernels) or of one batch row (lockstep kernel) run on one XCD at
+// about the same time and read the B/C rows they share from that XCD's L2
+// instead of each fetching them.  (Launches not a multiple of 8 keep the plain
+// order.)  Measured on the lockstep kernel: 416 -> 408-411 us on the
+// 4 x 8192 x 4096 workload; the same renumbering made the backward and the
+// scalar-A scan 3-4% slower, and they keep the plain order.
 constexpr int kXcds = 8;
 __device__ __forceinline__ int64_t xcd_order(int64_t wid, int64_t n) {
     return n % kXcds == 0 ? (wid % kXcds) * (n / kXcds) + wid / kXcds : wid;
@@ -898,7 +901,7 @@ __global__ __launch_bounds__(W *kWave) void k_lockstep(
     lds_poison(sh);
     const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
     const int lane = int(threadIdx.x) % kWave;
-    const int64_t tile = blockIdx.x;
+    const int64_t tile = xcd_order(blockIdx.x, gridDim.x);
     const int64_t b = tile / tiles_per_batch;
     const int64_t dt = tile - b * tiles_per_batch;
     // the tile's path is uniform over the workgroup
