@@ -19,13 +19,15 @@
 // Space Models", the hardware-aware implementation; "Mamba matches the
 // Transformer...", "Fuse the kernel and recompute") without spelling it out.
 //
-// Mapping.  One workgroup of BW waves owns one 64-channel tile (lane = channel,
+// Mapping.  Each pass takes one 64-channel tile per workgroup (lane = channel,
 // B/C wave-uniform in SGPRs, as in the forward kernels) for the whole
-// sequence, in chunks of BW runs of BT tokens:
-//   pass 1, chunks in order: each run is scanned from zero (run 0 from the
-//     chunk's entering state), the runs are composed through LDS with the
-//     associative combine, and the state entering every chunk is saved;
-//   pass 2, chunks in reverse: each run scans its tokens forward from zero
+// sequence, in chunks of BCH = BW * BT tokens:
+//   pass 1 (k_bwd_ckpt), chunks in order, CW = 16 waves of one chunk each:
+//     each run is scanned from zero (run 0 from the carried state), the runs
+//     are composed through LDS with the associative combine, and the state
+//     entering every chunk is saved;
+//   pass 2 (k_bwd), chunks in reverse, BW waves of BT tokens per chunk: each
+//     run scans its tokens forward from zero
 //     (run 0: from the chunk's entering state), keeping the BT states in
 //     VGPRs, and backward (adjoint from zero at its right end); the forward
 //     aggregates are folded left to right (state entering each run) and the
@@ -284,11 +286,144 @@ struct GenMath {
     }
 };
 
+// Pass 1 of the backward: the state entering every BCH-token chunk, saved for the
+// reverse pass (ckpt, (chunks, batch, NT, dim), in the Math's state form).  One
+// workgroup of CW waves per tile (lane = channel), over the sequence in steps of
+// CW chunks: wave w scans chunk c*CW + w from zero -- wave 0 from the state
+// carried in -- and the CW runs are composed through LDS with the associative
+// combine, which gives the state entering each of them (the same fold as the
+// forward kernels).  Only states: no readout and no correction, so a token costs
+// the update's 3 operations per state, and a workgroup holds CW = 16 waves where
+// the reverse pass, short of registers, holds BW = 8.
+constexpr int CW = 16;   // waves (runs of one chunk each) per workgroup of the checkpoint pass
+constexpr int CU8 = 8;   // tokens per load group
+
+template <class IO, int NT, bool kFast>
+__global__ __launch_bounds__(CW *kWave) void k_bwd_ckpt(
+    const typename IO::T *__restrict__ x, const typename IO::T *__restrict__ delta,
+    const float *__restrict__ A, const float *__restrict__ bc, const float *__restrict__ h0,
+    float *__restrict__ ckpt, const int *__restrict__ tile_fast, int64_t batch, int64_t L, int64_t dim,
+    int N, int64_t tiles_per_batch) {
+    using T = typename IO::T;
+    using Math = std::conditional_t<kFast, FastMath<NT>, GenMath<NT>>;
+    constexpr int NPW = (NT + CW - 1) / CW;  // states each wave folds
+    constexpr int ES = IO::kBytes;
+    static_assert(BCH % CU8 == 0, "a chunk is a whole number of load groups");
+    __shared__ float s_sum[CW][kWave];
+    __shared__ float s_k[CW][NT][kWave];    // run end states (from the run's start state)
+    __shared__ float s_pre[CW][NT][kWave];  // [0]: state carried into the next step; [j]: entering run j
+    lds_poison(s_sum, s_k, s_pre);
+
+    const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
+    const int lane = int(threadIdx.x) % kWave;
+    const int64_t tile = blockIdx.x;
+    const int64_t b = tile / tiles_per_batch;
+    const int64_t dt_ = tile - b * tiles_per_batch;
+    if ((tile_fast[dt_] != 0) != kFast) return;  // whole workgroup
+    const int64_t dbase = dt_ * kWave;
+    const bool active = dbase + lane < dim;
+    const int64_t d = active ? dbase + lane : dim - 1;
+    Math m;
+    m.init(A, d, N);
+    // inactive lanes read channel dim-1 with x = 0 and store nothing
+    const float amask = active ? 1.f : 0.f;
+    const uint32_t voff = uint32_t(d * ES);
+    const uint32_t rowb = uint32_t(dim * ES);
+    const float *bcrow = bc + (b * L) * (2 * NT);
+    const int64_t ncb = (L + BCH - 1) / BCH;  // chunks of the reverse pass
+    const int64_t nst = (ncb + CW - 1) / CW;  // steps of CW chunks
+    auto ck = [&](int64_t cb, int n) -> float & { return ckpt[((cb * batch + b) * NT + n) * dim + d]; };
+    // CU8 tokens from token tg on (a descriptor per group keeps every offset small;
+    // tokens at or past L read 0, which leaves the state unchanged)
+    auto load = [&](int64_t tg, T *xo, T *dq) {
+        const int64_t tc = tg < L ? tg : L;
+        const int64_t bytes = (L - tc) * dim * ES;
+        const rsrc_t rx = make_rsrc(x + (b * L + tc) * dim, bytes), rd = make_rsrc(delta + (b * L + tc) * dim, bytes);
+#pragma unroll
+        for (int u = 0; u < CU8; ++u) {
+            xo[u] = IO::bld(rx, voff, uint32_t(u) * rowb);
+            dq[u] = IO::bld(rd, voff, uint32_t(u) * rowb);
+        }
+    };
+
+    if (w == 0) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+            s_pre[0][n][lane] = (h0 && n < N) ? m.to_state(h0[(b * dim + d) * N + n]) : 0.f;
+    }
+    __syncthreads();
+    float k[NT];
+    T xr[CU8], dr[CU8];
+    load(int64_t(w) * BCH, xr, dr);
+    for (int64_t c = 0; c < nst; ++c) {
+        const int64_t cb = c * CW + w;  // this wave's chunk
+        const int64_t t0 = cb * BCH;
+        if (w == 0) {
+#pragma unroll
+            for (int n = 0; n < NT; ++n) k[n] = s_pre[0][n][lane];
+            if (active && cb < ncb) {
+#pragma unroll
+                for (int n = 0; n < NT; ++n) ck(cb, n) = k[n];
+            }
+        } else {
+#pragma unroll
+            for (int n = 0; n < NT; ++n) k[n] = 0.f;
+        }
+        const float *bc0 = bcrow + (t0 < L ? t0 : L - 1) * (2 * NT);
+        const int last = int(max<int64_t>(0, min<int64_t>(BCH, L - t0) - 1));
+        float dsum = 0.f;
+#pragma unroll
+        for (int g = 0; g < BCH / CU8; ++g) {
+            float xv[CU8], dv[CU8];
+#pragma unroll
+            for (int u = 0; u < CU8; ++u) {
+                xv[u] = amask * IO::cvt(xr[u]);
+                dv[u] = IO::cvt(dr[u]);
+            }
+            // the next group: the rest of this chunk, then this wave's chunk of the next step
+            load(g + 1 < BCH / CU8 ? t0 + (g + 1) * CU8 : t0 + int64_t(CW) * BCH, xr, dr);
+#pragma unroll
+            for (int u = 0; u < CU8; ++u) {
+                m.fwd(dv[u], xv[u], bc0 + min(g * CU8 + u, last) * (2 * NT), k);
+                dsum += dv[u];
+            }
+        }
+        s_sum[w][lane] = dsum;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) s_k[w][n][lane] = k[n];
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < NPW; ++i) {
+            const int n = w * NPW + i;
+            if (n < NT) {
+                float dec[CW], kv[CW];
+#pragma unroll
+                for (int j = 0; j < CW; ++j) {
+                    dec[j] = m.run_decay(n, s_sum[j][lane]);
+                    kv[j] = s_k[j][n][lane];
+                }
+                float P = kv[0];  // run 0 started from the carried state
+#pragma unroll
+                for (int j = 1; j < CW; ++j) {
+                    s_pre[j][n][lane] = P;
+                    P = fmaf(dec[j], P, kv[j]);
+                }
+                s_pre[0][n][lane] = P;
+            }
+        }
+        __syncthreads();
+        if (w != 0 && active && cb < ncb) {
+#pragma unroll
+            for (int n = 0; n < NT; ++n) ck(cb, n) = s_pre[w][n][lane];
+        }
+    }
+}
+
 template <class IO, int NT, bool kFast>
 __global__ __launch_bounds__(BW *kWave) void k_bwd(
     const typename IO::T *__restrict__ x, const typename IO::T *__restrict__ delta,
     const float *__restrict__ A, const float *__restrict__ bc, const float *__restrict__ Dskip,
-    const float *__restrict__ h0, const typename IO::T *__restrict__ dy,
+    const typename IO::T *__restrict__ dy,
     const float *__restrict__ dhT, typename IO::T *__restrict__ dx,
     typename IO::T *__restrict__ ddelta, float *__restrict__ part_bc,
     float *__restrict__ part_ad, float *__restrict__ dh0, float *__restrict__ ckpt,
@@ -343,78 +478,11 @@ __global__ __launch_bounds__(BW *kWave) void k_bwd(
         const int64_t t0 = (c < 0 ? 0 : c) * BCH + int64_t(w) * BT;
         return make_rsrc(base + (b * L + t0) * dim, c < 0 ? 0 : (L - t0) * dim * ES);
     };
-    auto ck = [&](int64_t c, int n) -> float & { return ckpt[((c * batch + b) * NT + n) * dim + d]; };
     const RedRow red{&s_red[w][0][lane]};
 
-    // ---------------- pass 1: states entering every chunk
+    // (pass 1, the state entering every chunk, is k_bwd_ckpt's: read from ckpt)
     float k[NT];
-#pragma unroll
-    for (int n = 0; n < NT; ++n)
-        k[n] = (w == 0 && h0 && n < N) ? m.to_state(h0[(b * dim + d) * N + n]) : 0.f;
     T cx[BT], cd[BT];  // raw x and delta of the chunk, loaded one chunk ahead
-    auto load1 = [&](int64_t c, T *xr, T *dr) {
-        const rsrc_t rx = rsrc_chunk(x, c), rd = rsrc_chunk(delta, c);
-#pragma unroll
-        for (int tau = 0; tau < BT; ++tau) {
-            xr[tau] = IO::bld(rx, voff, uint32_t(tau) * rowb);
-            dr[tau] = IO::bld(rd, voff, uint32_t(tau) * rowb);
-        }
-    };
-    load1(0, cx, cd);
-    for (int64_t c = 0; c < nchunks; ++c) {
-        const int64_t t0 = c * BCH + int64_t(w) * BT;
-        T nx[BT], nd[BT];
-        load1(c + 1, nx, nd);
-        const float *bc0 = bcrow + min(t0, L - 1) * (2 * NT);
-        const int last = int(max<int64_t>(0, min<int64_t>(BT, L - t0) - 1));
-        if (w == 0) {
-            if (c > 0) {
-#pragma unroll
-                for (int n = 0; n < NT; ++n) k[n] = s_pre[0][n][lane];
-            }
-            if (active) {
-#pragma unroll
-                for (int n = 0; n < NT; ++n) ck(c, n) = k[n];
-            }
-        } else {
-#pragma unroll
-            for (int n = 0; n < NT; ++n) k[n] = 0.f;
-        }
-        float dsum = 0.f;
-#pragma unroll
-        for (int tau = 0; tau < BT; ++tau) {
-            const float xv = amask * IO::cvt(cx[tau]);
-            const float dv = IO::cvt(cd[tau]);
-            m.fwd(dv, xv, bc0 + min(tau, last) * (2 * NT), k);
-            dsum += dv;
-        }
-        s_sum[w][lane] = dsum;
-#pragma unroll
-        for (int n = 0; n < NT; ++n) s_k[w][n][lane] = k[n];
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < NPW; ++i) {
-            const int n = w * NPW + i;
-            if (n < NT) {
-                float dec[BW], kv[BW];
-#pragma unroll
-                for (int j = 0; j < BW; ++j) {
-                    dec[j] = m.run_decay(n, s_sum[j][lane]);
-                    kv[j] = s_k[j][n][lane];
-                }
-                float P = kv[0];
-#pragma unroll
-                for (int j = 1; j < BW; ++j) P = fmaf(dec[j], P, kv[j]);
-                s_pre[0][n][lane] = P;
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int tau = 0; tau < BT; ++tau) {
-            cx[tau] = nx[tau];
-            cd[tau] = nd[tau];
-        }
-    }
 
     // ---------------- pass 2: chunks in reverse
     float mu[NPW];  // adjoint entering the current chunk from the right (states this wave folds)
@@ -656,10 +724,17 @@ hipError_t backward_t(const BwdArgs &a, const BwdPlan &p, void *ws, hipStream_t 
     float *part_ad = reinterpret_cast<float *>(base + p.off_pad);
     hipError_t e = launch_prep(a.B, a.C, a.A, bc, flags, a.batch * a.L, a.dim, a.N, NT, a.io, s);
     if (e != hipSuccess) return e;
+#define SSCAN_CKPT(FAST)                                                                               \
+    hipLaunchKernelGGL((k_bwd_ckpt<IO, NT, FAST>), dim3(unsigned(p.tiles)), dim3(CW * kWave), 0, s,     \
+                       static_cast<const T *>(a.x), static_cast<const T *>(a.delta), a.A, bc, a.h0, ckpt, \
+                       flags, a.batch, a.L, a.dim, a.N, p.tiles_per_batch)
+    SSCAN_CKPT(true);
+    SSCAN_CKPT(false);
+#undef SSCAN_CKPT
 #define SSCAN_BWD(FAST)                                                                                \
     hipLaunchKernelGGL((k_bwd<IO, NT, FAST>), dim3(unsigned(p.tiles)), dim3(BW * kWave), 0, s,          \
                        static_cast<const T *>(a.x), static_cast<const T *>(a.delta), a.A, bc, a.Dskip,  \
-                       a.h0, static_cast<const T *>(a.dy), a.dhT, static_cast<T *>(a.dx),               \
+                       static_cast<const T *>(a.dy), a.dhT, static_cast<T *>(a.dx),                     \
                        static_cast<T *>(a.ddelta), part_bc, part_ad, a.dh0, ckpt, flags, a.batch, a.L,   \
                        a.dim, a.N, p.tiles_per_batch)
     SSCAN_BWD(true);
