@@ -309,7 +309,8 @@ def bench_backward(wl, args, dev) -> int:
         "data": "synthetic (seeded; x,B,C,dy~N(0,1), delta=softplus(0.5N+bias))",
         "config": {"workload": wl.name, "pass": "backward", "batch": wl.batch, "seqlen": wl.seqlen,
                    "dim": wl.dim, "dstate": wl.dstate, "io_dtype": wl.io, "a_init": wl.a_init},
-        "roofline": {"kernel": "k_bwd (timed: the whole sscan_backward call on its stream)",
+        "roofline": {"kernel": "k_bwd_ckpt + k_bwd + k_bwd_reduce (timed: the whole sscan_backward "
+                                "call on its stream; k_bwd, the reverse pass, is ~90% of it)",
                      "bound": "alu", "achieved": round(tflops, 3), "peak": PEAK_VALU_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_VALU_TFLOPS, 4),
                      "traffic": recorded_traffic(f"k_bwd_{wl.name}_hbm_counters.md", BWD_SOURCES),
