@@ -36,13 +36,9 @@
  *     formula and propagate (A > 0 grows, as an eigenvalue above 1 would).
  *   - Any tensor with zero elements may be passed as NULL.
  *   - Calls on different streams may run concurrently; each call owns the
- *     stream-ordered scratch memory it allocates (hipMallocFromPoolAsync) and frees
- *     it on the same stream.  The memory comes from a pool the library creates per
- *     GPU on first use, which keeps what is freed for later calls and never hands
- *     it back before the process ends: after a call, up to that call's scratch
- *     (sscan_forward_plan's scratch_bytes for a forward) stays reserved on its GPU.
- *     The exception is sscan_forward_noalloc, which allocates nothing and shares
- *     one static scratch array per GPU among its calls.
+ *     stream-ordered scratch memory it allocates (hipMallocAsync) and frees it on
+ *     the same stream.  The exception is sscan_forward_noalloc, which allocates
+ *     nothing and shares one static scratch array per GPU among its calls.
  */
 #ifndef SSCAN_H
 #define SSCAN_H
@@ -115,8 +111,8 @@ int sscan_forward_from_state(const void *x, const void *delta, const float *A, c
 /*
  * sscan_forward_from_state for callers that cannot allocate device memory: code
  * being captured into a HIP graph, tight serving loops, harnesses that forbid
- * hipMalloc.  It makes no allocation of any kind (no hipMalloc, no stream-ordered
- * or pool allocation, no hipFree); its scratch (staged B/C rows, tile flags, segment aggregates) is a
+ * hipMalloc.  It makes no allocation of any kind (no hipMalloc, hipMallocAsync or
+ * hipFree); its scratch (staged B/C rows, tile flags, segment aggregates) is a
  * static array of 64 MiB that the library holds on each GPU it runs on until the
  * process ends.  Every call on one GPU uses that GPU's array: calls that overlap in
  * time on one GPU (on different streams, or from several threads) race and give

@@ -113,44 +113,6 @@ void *noalloc_scratch(hipStream_t stream, int *rc) {
     return g_scratch_dev[dev];
 }
 
-// Scratch of the allocating entry points: stream-ordered allocations from a memory
-// pool the library keeps per device, which holds freed memory for reuse (release
-// threshold: never) rather than handing it back, so a call's allocation is
-// bookkeeping on the stream.  Calls on different streams still get separate
-// memory, in stream order.
-std::mutex g_pool_mu;
-hipMemPool_t g_pool[kMaxDevices];
-
-hipError_t scratch_alloc(void **p, size_t bytes, hipStream_t s) {
-    int dev = 0;
-    hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-    hipMemPool_t pool = nullptr;
-    {
-        std::lock_guard<std::mutex> lock(g_pool_mu);
-        if (!g_pool[dev]) {
-            hipMemPoolProps props{};
-            props.allocType = hipMemAllocationTypePinned;
-            props.handleTypes = hipMemHandleTypeNone;
-            props.location.type = hipMemLocationTypeDevice;
-            props.location.id = dev;
-            hipMemPool_t np = nullptr;
-            e = hipMemPoolCreate(&np, &props);
-            if (e != hipSuccess) return e;
-            uint64_t keep = UINT64_MAX;
-            e = hipMemPoolSetAttribute(np, hipMemPoolAttrReleaseThreshold, &keep);
-            if (e != hipSuccess) {
-                (void)hipMemPoolDestroy(np);
-                return e;
-            }
-            g_pool[dev] = np;
-        }
-        pool = g_pool[dev];
-    }
-    return hipMallocFromPoolAsync(p, bytes, pool, s);
-}
-
 }  // namespace
 
 extern "C" {
@@ -272,8 +234,8 @@ static int forward_impl(const void *x, const void *delta, const float *A, const 
         return el == hipSuccess ? SSCAN_OK : fail_hip("forward launch", el);
     }
     void *ws = nullptr;
-    hipError_t e = scratch_alloc(&ws, plan.ws_bytes, s);
-    if (e != hipSuccess) return fail_hip("scratch allocation (hipMallocFromPoolAsync)", e);
+    hipError_t e = hipMallocAsync(&ws, plan.ws_bytes, s);
+    if (e != hipSuccess) return fail_hip("hipMallocAsync (scratch)", e);
     e = sscan::launch_forward(a, plan, ws, s);
     const hipError_t ef = hipFreeAsync(ws, s);
     if (e != hipSuccess) return fail_hip("forward launch", e);
@@ -354,8 +316,8 @@ int sscan_backward(const void *x, const void *delta, const float *A, const void 
     const sscan::BwdPlan plan = sscan::plan_backward(batch, seqlen, dim, dstate);
     if (plan.reject) return fail(SSCAN_ERR_UNSUPPORTED, "%s", plan.reject);
     void *ws = nullptr;
-    hipError_t e = scratch_alloc(&ws, plan.ws_bytes, s);
-    if (e != hipSuccess) return fail_hip("scratch allocation (hipMallocFromPoolAsync)", e);
+    hipError_t e = hipMallocAsync(&ws, plan.ws_bytes, s);
+    if (e != hipSuccess) return fail_hip("hipMallocAsync (scratch)", e);
     sscan::BwdArgs a{x,  delta, A,  B,  C,  Dskip,  initial_state,  dy, dfinal_state, dx, ddelta, dA,
                      dB, dC,    dDskip, dinitial_state, batch, seqlen, dim, int(dstate), io_dtype};
     e = sscan::launch_backward(a, plan, ws, s);

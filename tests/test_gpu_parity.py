@@ -305,41 +305,6 @@ def test_runs_on_a_side_stream():
     assert rel_err(to_host(y), yr) <= TOL["f32"]
 
 
-def test_scratch_pool_is_reused_across_calls():
-    """The allocating calls take their scratch from the library's per-GPU pool, which keeps
-    freed scratch for the next call: after a first call of each kind, repeated calls (forward
-    on both kernel paths, backward) leave the device's free memory where it was, and the
-    results do not change."""
-    wl = datagen.custom("pool", 2, 2000, 256, 16, "bf16", "s4d_real", key=15)
-    t = upload_scan(datagen.scan_inputs(wl), "bf16")
-    g = datagen.grad_inputs(wl)
-    dy = to_dev(g["dy"], "bf16")
-    y = torch.empty_like(t["x"])
-
-    def calls():  # 8 tiles: the segment kernels (the lockstep kernel runs on the shape below)
-        sscan.forward(t["x"], t["delta"], t["A"], t["B"], t["C"], t["Dskip"], y=y)
-        sscan.backward(t["x"], t["delta"], t["A"], t["B"], t["C"], dy, Dskip=t["Dskip"])
-
-    wl2 = datagen.custom("pool2", 192, 300, 64, 16, "bf16", "s4d_real", key=16)
-    t2 = upload_scan(datagen.scan_inputs(wl2), "bf16")
-    y2 = torch.empty_like(t2["x"])
-    assert sscan.forward_plan(wl2.batch, wl2.seqlen, wl2.dim, wl2.dstate, "bf16")["kernel"] == "lockstep"
-    assert sscan.forward_plan(wl.batch, wl.seqlen, wl.dim, wl.dstate, "bf16")["kernel"] == "segment"
-
-    calls()
-    sscan.forward(t2["x"], t2["delta"], t2["A"], t2["B"], t2["C"], t2["Dskip"], y=y2)
-    torch.cuda.synchronize()
-    ref, ref2 = y.clone(), y2.clone()
-    free0 = torch.cuda.mem_get_info()[0]
-    for _ in range(5):
-        calls()
-        sscan.forward(t2["x"], t2["delta"], t2["A"], t2["B"], t2["C"], t2["Dskip"], y=y2)
-    torch.cuda.synchronize()
-    assert torch.cuda.mem_get_info()[0] == free0
-    assert torch.equal(y.view(torch.int16), ref.view(torch.int16))
-    assert torch.equal(y2.view(torch.int16), ref2.view(torch.int16))
-
-
 # ---------------------------------------------------------------- starting from a state
 
 STATE_SHAPES = [
